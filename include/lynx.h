@@ -1,0 +1,170 @@
+/*
+ * lynx.h — C ABI of liblynx: the Lynx split-stream KV codec and anchor-only
+ * decode attention, hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [Review] "Lynx: Progressive Speculative KV Cache Transfer for Disaggregated
+ *            LLM Inference" (technical review of arXiv 2607.01831).
+ *   [Digest] "Lynx: Progressive Speculative Quantization for accelerating KV
+ *            Transfer in Long-Context Inference" (paper digest), Method.
+ *
+ * Conventions for every entry point
+ *   - Pointers named *_dev are device pointers (hipMalloc'd or torch CUDA
+ *     tensors), owned by the caller, 16-byte aligned.  The library allocates
+ *     nothing, keeps no global state, and is re-entrant.
+ *   - `hip_stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *     enqueued asynchronously on it; the host is never synchronised.
+ *   - Argument errors are detected on the host and returned BEFORE anything
+ *     is launched; nothing is written in that case.  A failed launch returns
+ *     LYNX_ELAUNCH.  No C++ exception crosses this boundary.
+ *   - KV input must be finite BF16.  NaN/Inf inputs give unspecified codes.
+ *
+ * KV page and channel
+ *   A page is `page_tokens` (P) consecutive tokens of one KV tensor, stored
+ *   token-major as BF16 [P][kv_heads][head_dim] ([Review] Mechanism 1: the
+ *   page block X in R^{H x P}).  A channel is one (kv_head, head_dim) pair,
+ *   H = kv_heads*head_dim channels per page; channel index c = h*head_dim + d.
+ *   Per-channel statistics run over the page's tokens; chunk k covers tokens
+ *   k*C .. k*C+C-1 ([Review] Mechanism 1, Stage 2).  K and V are encoded
+ *   identically.
+ *
+ * Stream layout (per page; pages are contiguous and page-major)
+ *   anchor segment  = [anchor nibbles : P*H/2 bytes]
+ *                     [gamma_min   : float32[H]]
+ *                     [gamma_scale : float32[H]]
+ *                     [mu          : float32[P/C][H]]
+ *                     [sigma       : float32[P/C][H]]
+ *   residual segment = [residual nibbles : P*H/2 bytes]
+ *   Anchor codes and their metadata are contiguous so one copy moves the whole
+ *   high-priority stream ([Review] Mechanism 2, prefill-side workflow).  Codes
+ *   are ordered [kv_head][token][head_dim] inside a page; two 4-bit codes share
+ *   a byte, the even element in the low nibble ([Review] Implementation Notes).
+ *   A 4-bit code q in [-8, 7] is stored as the nibble q & 0xF.
+ *   Metadata count = H*(2 + 2P/C) float32 scalars ([Review] Deep Dive).
+ *
+ * Readings of the pages this ABI implements (where the pages are silent or
+ * inconsistent):
+ *   eps = 1e-6 in both normalisation stages; metadata stored as float32 and the
+ *   stored values used by every later stage; sigma = max |X_n - mu| over the
+ *   chunk; sign S taken from X_final (S(0) = +1); Round = nearest-even;
+ *   Stage 4 with the +7 bias applied at reconstruction:
+ *     V_mag = I >> 4, V_recon = 16*V_mag + 7, V_res = V_recon - I in [-8, 7],
+ *     Q_anc = V_mag*S + min(S, 0) in [-8, 7] (Eq. 9), Q_res = V_res;
+ *   anchor-only decode uses I = 16*V_mag + 7, full decode I = V_recon - V_res.
+ */
+#ifndef LYNX_H
+#define LYNX_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define LYNX_OK            0
+#define LYNX_EINVAL       -1   /* bad size, count, chunk, alpha, selector or dtype */
+#define LYNX_EALIGN       -2   /* a pointer is NULL where data is required, or not 16-byte aligned */
+#define LYNX_EUNSUPPORTED -3   /* a valid shape this build does not implement (e.g. head_dim != 128) */
+#define LYNX_ENOSPACE     -4   /* workspace smaller than lynx_attn_workspace_bytes() */
+#define LYNX_ELAUNCH      -5   /* the HIP runtime rejected a kernel launch */
+
+/* ---- selectors ---------------------------------------------------------- */
+#define LYNX_SEL_ANCHOR   1u   /* encode: write the anchor segments (codes + metadata); required */
+#define LYNX_SEL_RESIDUAL 2u   /* encode: also write the residual segments */
+#define LYNX_OUT_BF16     0    /* decoders / attention: BF16 output, round to nearest even */
+#define LYNX_OUT_F32      1    /* decoders / attention: float32 output */
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* lynx_strerror(int status);
+
+/*
+ * Bytes of one page's anchor segment (P*H/2 + 4*H*(2 + 2P/C)) and residual
+ * segment (P*H/2).  Pure host arithmetic.  Returns LYNX_EINVAL for
+ * non-positive sizes, P % C != 0, or odd P*H.
+ */
+int lynx_stream_sizes(int page_tokens, int kv_heads, int head_dim, int chunk,
+                      size_t* anchor_seg_bytes, size_t* residual_seg_bytes);
+
+/*
+ * Encode ([Review] Mechanism 1, Algorithm 1, Stages 1-4; [Digest] Method 1-4).
+ *   kv_dev      : BF16 [n_pages*P][kv_heads][head_dim], read only.
+ *   n_pages     : >= 0; 0 is a no-op returning LYNX_OK.
+ *   page_tokens : P, a multiple of `chunk`.
+ *   chunk       : C, a multiple of 16, C <= P.
+ *   alpha       : finite, > 0 (alpha-law parameter of Eq. 7).
+ *   sel         : LYNX_SEL_ANCHOR, optionally | LYNX_SEL_RESIDUAL.
+ *   anchor_dev  : n_pages anchor segments (see lynx_stream_sizes), written.
+ *   residual_dev: n_pages residual segments, written when selected (may be
+ *                 NULL otherwise).
+ * Per element: X_n = (X - gamma_min)/(gamma_scale + eps);
+ * X_f = (X_n - mu)/(sigma + eps); Y = 127*ln(1 + alpha|X_f|)/ln(1 + alpha);
+ * I = Round(Y); S = sign(X_f); then the split above.
+ * Supported in this build: head_dim == 128 (else LYNX_EUNSUPPORTED).
+ */
+int lynx_encode(const void* kv_dev, int n_pages, int page_tokens, int kv_heads, int head_dim,
+                int chunk, float alpha, unsigned sel, void* anchor_dev, void* residual_dev,
+                void* hip_stream);
+
+/*
+ * Anchor-only decode: Q_approx = dequant(Q_anc, gamma, mu, sigma)
+ * ([Review] Mechanism 2, decode-side anchor phase; Eq. 8 and the worked
+ * example's anchor-only reconstruction, Eq. 14).
+ *   anchor_dev : n_pages anchor segments, read only.
+ *   out_dtype  : LYNX_OUT_BF16 or LYNX_OUT_F32.
+ *   out_dev    : [n_pages*P][kv_heads][head_dim] of out_dtype, written.
+ * x_hat = ((S*|x|)*(sigma + eps) + mu)*(gamma_scale + eps) + gamma_min with
+ * |x| = ((1 + alpha)^(I/127) - 1)/alpha and I = 16*V_mag + 7.
+ * Other arguments and errors as lynx_encode.
+ */
+int lynx_decode_anchor(const void* anchor_dev, int n_pages, int page_tokens, int kv_heads,
+                       int head_dim, int chunk, float alpha, int out_dtype, void* out_dev,
+                       void* hip_stream);
+
+/*
+ * Full decode from Anchor + Residual: Q_full = dequant(Q_anc + Q_res)
+ * ([Review] Mechanism 2, decode-side residual phase; worked example, Eq. 15):
+ * the exact 7-bit code I = V_recon - V_res, then as lynx_decode_anchor.
+ *   residual_dev : n_pages residual segments, read only.
+ */
+int lynx_decode_full(const void* anchor_dev, const void* residual_dev, int n_pages,
+                     int page_tokens, int kv_heads, int head_dim, int chunk, float alpha,
+                     int out_dtype, void* out_dev, void* hip_stream);
+
+/*
+ * Workspace bytes lynx_attn_anchor needs for the given shape (split-context
+ * partial results); 0 for shapes it would reject.
+ */
+size_t lynx_attn_workspace_bytes(int batch, int ctx_tokens, int q_heads, int kv_heads,
+                                 int head_dim, int page_tokens, int chunk);
+
+/*
+ * Single-token decode attention over anchor-only codes, the speculative draft
+ * path ([Review] Prerequisites §1, Eq. 1 evaluated on Q_approx of Mechanism 2),
+ * fused with the anchor decode: O = softmax(q K^T * sm_scale) V where K and V
+ * are the anchor-only reconstructions of the given segments.
+ *   q_dev        : BF16 [batch][q_heads][head_dim].
+ *   k_anchor_dev, v_anchor_dev : anchor segments; sequence b's context is the
+ *                  ctx_tokens/page_tokens consecutive segments starting at
+ *                  segment b*(ctx_tokens/page_tokens), with kv_heads heads.
+ *   q_heads      : a multiple of kv_heads; query head hq reads kv head
+ *                  hq / (q_heads/kv_heads).  Group size q_heads/kv_heads <= 8.
+ *   ctx_tokens   : a positive multiple of page_tokens.
+ *   chunk        : a multiple of 64 in this build (else LYNX_EUNSUPPORTED).
+ *   sm_scale     : > 0, or <= 0 to use 1/sqrt(head_dim).
+ *   workspace_dev, ws_bytes : at least lynx_attn_workspace_bytes(...) bytes.
+ *   out_dtype    : LYNX_OUT_BF16 or LYNX_OUT_F32.
+ *   out_dev      : [batch][q_heads][head_dim] of out_dtype, written.
+ * Supported in this build: head_dim == 128.
+ */
+int lynx_attn_anchor(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev,
+                     int batch, int ctx_tokens, int q_heads, int kv_heads, int head_dim,
+                     int page_tokens, int chunk, float alpha, float sm_scale,
+                     void* workspace_dev, size_t ws_bytes, int out_dtype, void* out_dev,
+                     void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LYNX_H */
