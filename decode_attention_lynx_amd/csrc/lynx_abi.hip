@@ -1,0 +1,191 @@
+// C ABI of liblynx: argument validation, parameter blocks and kernel launches.
+// Every argument error is detected here, on the host, before any launch.  The
+// library allocates nothing and keeps no state between calls.
+//
+// Sources, cited by page title and section:
+//   [Review] "Lynx: Progressive Speculative KV Cache Transfer for Disaggregated
+//            LLM Inference" (technical review of arXiv 2607.01831).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/lynx.h"
+#include "lynx_common.hpp"
+#include "lynx_kernels.hpp"
+
+using namespace lynx;
+
+namespace {
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool pow2_chunk(int c) { return c == 8 || c == 16 || c == 32 || c == 64 || c == 128 || c == 256; }
+
+// Shared validation of the page geometry; fills `g` on success.
+int check_geometry(int n_pages, int P, int Hkv, int D, int C, float alpha, Geometry* g) {
+  if (n_pages < 0 || P <= 0 || Hkv <= 0 || D <= 0 || C <= 0) return LYNX_EINVAL;
+  if (P % C != 0) return LYNX_EINVAL;
+  if (!std::isfinite(alpha) || !(alpha > 0.0f)) return LYNX_EINVAL;
+  if (D != kHeadDim) return LYNX_EUNSUPPORTED;
+  if (!pow2_chunk(C)) return LYNX_EUNSUPPORTED;
+  if ((long long)n_pages * Hkv * (kHeadDim / kSlab) * ((P + kTileTokens - 1) / kTileTokens) > 0x7fffffffll)
+    return LYNX_EUNSUPPORTED;
+  g->n_pages = n_pages;
+  g->P = P;
+  g->Hkv = Hkv;
+  g->C = C;
+  g->nck = P / C;
+  g->H = Hkv * D;
+  g->codes = (long long)P * g->H / 2;
+  g->res_seg = g->codes;
+  g->anc_seg = g->codes + 4ll * g->H * (2 + 2ll * (P / C));
+  return LYNX_OK;
+}
+
+// |x_hat| = ((1+alpha)^(I/127) - 1)/alpha  ([Review] Mechanism 1, Stage 3, Eq. 8 as
+// normalised in the Worked Example, Eq. 14-15).
+double alaw_mag(int I, double alpha) { return std::expm1((double)I / kCodeMax * std::log1p(alpha)) / alpha; }
+
+// Signed anchor value of a nibble: Q_anc = nibble as 4-bit two's complement;
+// S = -1 iff Q_anc < 0; V_mag = Q_anc or -Q_anc - 1 (Eq. 9 inverted).
+void anchor_fields(int nib, int* S, int* vmag) {
+  const int q = nib >= 8 ? nib - 16 : nib;
+  *S = q < 0 ? -1 : 1;
+  *vmag = q < 0 ? -q - 1 : q;
+}
+
+int launch(const void* fn, dim3 grid, void* args_struct, hipStream_t stream) {
+  void* kargs[] = {args_struct};
+  const hipError_t e = hipLaunchKernel(fn, grid, dim3(kThreads), kargs, 0, stream);
+  return e == hipSuccess ? LYNX_OK : LYNX_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lynx_strerror(int status) {
+  switch (status) {
+    case LYNX_OK: return "ok";
+    case LYNX_EINVAL: return "invalid argument (size, count, chunk, alpha, selector or dtype)";
+    case LYNX_EALIGN: return "null or misaligned pointer (16-byte alignment required)";
+    case LYNX_EUNSUPPORTED: return "shape not supported by this build";
+    case LYNX_ENOSPACE: return "workspace too small";
+    case LYNX_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int lynx_stream_sizes(int page_tokens, int kv_heads, int head_dim, int chunk, size_t* anchor_seg_bytes,
+                      size_t* residual_seg_bytes) {
+  if (page_tokens <= 0 || kv_heads <= 0 || head_dim <= 0 || chunk <= 0) return LYNX_EINVAL;
+  if (page_tokens % chunk != 0) return LYNX_EINVAL;
+  const long long H = (long long)kv_heads * head_dim;
+  if ((page_tokens * H) % 2 != 0) return LYNX_EINVAL;
+  const long long codes = page_tokens * H / 2;
+  if (anchor_seg_bytes) *anchor_seg_bytes = (size_t)(codes + 4ll * H * (2 + 2ll * (page_tokens / chunk)));
+  if (residual_seg_bytes) *residual_seg_bytes = (size_t)codes;
+  return LYNX_OK;
+}
+
+int lynx_encode(const void* kv_dev, int n_pages, int page_tokens, int kv_heads, int head_dim, int chunk,
+                float alpha, unsigned sel, void* anchor_dev, void* residual_dev, void* hip_stream) {
+  EncodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int st = check_geometry(n_pages, page_tokens, kv_heads, head_dim, chunk, alpha, &a.g);
+  if (st != LYNX_OK) return st;
+  if ((sel & ~(LYNX_SEL_ANCHOR | LYNX_SEL_RESIDUAL)) != 0 || !(sel & LYNX_SEL_ANCHOR)) return LYNX_EINVAL;
+  if (n_pages == 0) return LYNX_OK;
+  if (!aligned16(kv_dev) || !aligned16(anchor_dev)) return LYNX_EALIGN;
+  if ((sel & LYNX_SEL_RESIDUAL) && !aligned16(residual_dev)) return LYNX_EALIGN;
+  a.kv = static_cast<const uint16_t*>(kv_dev);
+  a.anchor = static_cast<uint8_t*>(anchor_dev);
+  a.residual = (sel & LYNX_SEL_RESIDUAL) ? static_cast<uint8_t*>(residual_dev) : nullptr;
+  a.alpha = alpha;
+  const double al = (double)alpha, L = std::log1p(al);
+  a.ylog2k = (float)((double)kCodeMax / std::log2(1.0 + al));
+  // Band half-width around a rounding boundary of Y inside which the float32
+  // estimate is not trusted and the element is decided in float64.  The float32
+  // evaluation's error stays below 4e-5 (bound derived in the design notes and
+  // measured on the device); 1e-4 leaves a margin of 2.5x.
+  a.ziv = 1e-4f;
+  a.bnd[0] = 0.0;
+  for (int j = 1; j <= kCodeMax; ++j) a.bnd[j] = std::expm1(((double)j - 0.5) * L / kCodeMax) / al;
+  a.bnd[128] = INFINITY;
+  const dim3 grid((unsigned)(n_pages * kv_heads * (kHeadDim / kSlab)));   // (page, head, slab)
+  return launch(reinterpret_cast<const void*>(&k_encode), grid, &a, static_cast<hipStream_t>(hip_stream));
+}
+
+static int decode_common(bool full, const void* anchor_dev, const void* residual_dev, int n_pages,
+                         int page_tokens, int kv_heads, int head_dim, int chunk, float alpha, int out_dtype,
+                         void* out_dev, void* hip_stream) {
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int st = check_geometry(n_pages, page_tokens, kv_heads, head_dim, chunk, alpha, &a.g);
+  if (st != LYNX_OK) return st;
+  if (out_dtype != LYNX_OUT_BF16 && out_dtype != LYNX_OUT_F32) return LYNX_EINVAL;
+  if (n_pages == 0) return LYNX_OK;
+  if (!aligned16(anchor_dev) || !aligned16(out_dev)) return LYNX_EALIGN;
+  if (full && !aligned16(residual_dev)) return LYNX_EALIGN;
+  a.anchor = static_cast<const uint8_t*>(anchor_dev);
+  a.residual = full ? static_cast<const uint8_t*>(residual_dev) : nullptr;
+  a.out = out_dev;
+  const double al = (double)alpha;
+  if (full) {
+    // index = anchor nibble | residual nibble << 4; I = V_recon - V_res ([Review] Eq. 15)
+    for (int idx = 0; idx < 256; ++idx) {
+      int S, vmag;
+      anchor_fields(idx & 15, &S, &vmag);
+      const int rn = idx >> 4;
+      const int vres = rn >= 8 ? rn - 16 : rn;
+      int I = 16 * vmag + 7 - vres;
+      a.lut[idx] = (float)(S * alaw_mag(I, al));
+    }
+  } else {
+    // anchor only: I = 16*V_mag + 7 (the residual taken as 0)
+    for (int nib = 0; nib < 16; ++nib) {
+      int S, vmag;
+      anchor_fields(nib, &S, &vmag);
+      a.lut[nib] = (float)(S * alaw_mag(16 * vmag + 7, al));
+    }
+  }
+  const int ntiles = (page_tokens + kTileTokens - 1) / kTileTokens;
+  const dim3 grid((unsigned)(n_pages * kv_heads * (kHeadDim / kSlab) * ntiles));   // (page, head, slab, tile)
+  const void* fn;
+  if (full) fn = out_dtype == LYNX_OUT_F32 ? reinterpret_cast<const void*>(&k_decode<true, true>)
+                                           : reinterpret_cast<const void*>(&k_decode<true, false>);
+  else fn = out_dtype == LYNX_OUT_F32 ? reinterpret_cast<const void*>(&k_decode<false, true>)
+                                      : reinterpret_cast<const void*>(&k_decode<false, false>);
+  return launch(fn, grid, &a, static_cast<hipStream_t>(hip_stream));
+}
+
+int lynx_decode_anchor(const void* anchor_dev, int n_pages, int page_tokens, int kv_heads, int head_dim,
+                       int chunk, float alpha, int out_dtype, void* out_dev, void* hip_stream) {
+  return decode_common(false, anchor_dev, nullptr, n_pages, page_tokens, kv_heads, head_dim, chunk, alpha,
+                       out_dtype, out_dev, hip_stream);
+}
+
+int lynx_decode_full(const void* anchor_dev, const void* residual_dev, int n_pages, int page_tokens,
+                     int kv_heads, int head_dim, int chunk, float alpha, int out_dtype, void* out_dev,
+                     void* hip_stream) {
+  return decode_common(true, anchor_dev, residual_dev, n_pages, page_tokens, kv_heads, head_dim, chunk, alpha,
+                       out_dtype, out_dev, hip_stream);
+}
+
+size_t lynx_attn_workspace_bytes(int batch, int ctx_tokens, int q_heads, int kv_heads, int head_dim,
+                                 int page_tokens, int chunk) {
+  return attn_workspace_bytes(batch, ctx_tokens, q_heads, kv_heads, head_dim, page_tokens, chunk);
+}
+
+int lynx_attn_anchor(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev, int batch,
+                     int ctx_tokens, int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk,
+                     float alpha, float sm_scale, void* workspace_dev, size_t ws_bytes, int out_dtype,
+                     void* out_dev, void* hip_stream) {
+  return attn_anchor_launch(q_dev, k_anchor_dev, v_anchor_dev, batch, ctx_tokens, q_heads, kv_heads, head_dim,
+                            page_tokens, chunk, alpha, sm_scale, workspace_dev, ws_bytes, out_dtype, out_dev,
+                            static_cast<hipStream_t>(hip_stream));
+}
+
+}  // extern "C"

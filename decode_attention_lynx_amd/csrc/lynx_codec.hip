@@ -1,0 +1,431 @@
+// Lynx split-stream KV codec kernels for gfx950: encode, anchor-only decode, full decode.
+//
+// Sources, cited by page title and section:
+//   [Review] "Lynx: Progressive Speculative KV Cache Transfer for Disaggregated
+//            LLM Inference" (technical review of arXiv 2607.01831),
+//            Mechanism 1 (Algorithm 1, Stages 1-4, Eq. 7-9), Mechanism 2
+//            (decode-side anchor / residual phases), Worked Example (Eq. 14-15),
+//            Implementation Notes (two 4-bit codes per byte, 256-token pages).
+//
+// Work decomposition.  A workgroup of 256 threads owns a 64-channel slab of one
+// kv head of one page (encode) or of one 256-token tile of a page (decode).
+// Thread t owns channels 8*(t % 8) .. +7 of the slab and the 8 consecutive
+// tokens 8*(t / 8) .. +7 of the tile.  A token row of the slab is 128 B of BF16
+// (8 threads x 16 B loads) and 32 B of nibbles per stream (8 threads x 4 B).
+// Chunk sizes are powers of two in [8, 256], so a thread's tokens always lie in
+// one chunk, a chunk is a power-of-two run of threads, and chunks never straddle
+// 256-token tiles.
+#include "lynx_common.hpp"
+
+namespace lynx {
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int m) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __shfl_xor((int)(b & 0xffffffffll), m);
+  const int hi = __shfl_xor((int)(b >> 32), m);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// ---------------------------------------------------------------------------
+// Encode ([Review] Mechanism 1, Algorithm 1)
+// ---------------------------------------------------------------------------
+
+// One element's float64 decision, taken where the float32 estimate lies within
+// `ziv` of a rounding boundary of Y.  X_f is formed with the same float64
+// operations, in the same order, as the plain definition (Stage 1 division, then
+// the Stage 2 subtraction and division), and Round(Y) is decided by comparing
+// |X_f| with the exact boundaries bnd[j] (the |X_f| at which Y = j - 1/2), which is
+// Round(Eq. 7) without evaluating a logarithm.
+// Returns the byte I ^ (S < 0 ? 0xF7 : 0x07): high nibble = anchor, low = residual.
+__device__ __noinline__ uint32_t encode_exact(float x, float gmin, double D1, float mu, double D2,
+                                              const double* __restrict__ bnd) {
+  const double xn = ((double)x - (double)gmin) / D1;
+  const double xfe = (xn - (double)mu) / D2;
+  const double ax = fabs(xfe);
+  int lo = 0, hi = kCodeMax;                  // largest I with bnd[I] <= ax (bnd[0] = 0)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ax >= bnd[mid]) lo = mid; else hi = mid - 1;
+  }
+  return (uint32_t)lo ^ ((xfe < 0.0) ? 0xF7u : 0x07u);
+}
+
+// Pack 8 codes (one token, 8 consecutive channels) into one anchor word and one
+// residual word ([Review] Mechanism 1, Stage 4 and Eq. 9, with the +7 bias at
+// reconstruction; Implementation Notes: even element in the low nibble).
+//   anchor nibble   = V_mag ^ (S < 0 ? 0xF : 0)  == (V_mag*S + min(S,0)) & 0xF
+//   residual nibble = (I & 15) ^ 7               == (16*V_mag + 7 - I) & 0xF
+// Bytes are formed as I ^ (S < 0 ? 0xF7 : 0x07): high nibble = anchor, low = residual.
+__device__ __forceinline__ void pack8(const float* r, const float* xf, uint32_t* anc_w, uint32_t* res_w) {
+  uint32_t be = 0, bo = 0;
+  be = __builtin_amdgcn_cvt_pk_u8_f32(r[0], 0, be);
+  be = __builtin_amdgcn_cvt_pk_u8_f32(r[2], 1, be);
+  be = __builtin_amdgcn_cvt_pk_u8_f32(r[4], 2, be);
+  be = __builtin_amdgcn_cvt_pk_u8_f32(r[6], 3, be);
+  bo = __builtin_amdgcn_cvt_pk_u8_f32(r[1], 0, bo);
+  bo = __builtin_amdgcn_cvt_pk_u8_f32(r[3], 1, bo);
+  bo = __builtin_amdgcn_cvt_pk_u8_f32(r[5], 2, bo);
+  bo = __builtin_amdgcn_cvt_pk_u8_f32(r[7], 3, bo);
+  // 0xFF bytes where the value is negative: v_perm selectors 9 / 11 replicate the
+  // sign bit of its second / first operand (X_f is never -0 here).
+  const uint32_t ne = __builtin_amdgcn_perm(__float_as_uint(xf[2]), __float_as_uint(xf[0]), 0x0c0c0b09u) |
+                      __builtin_amdgcn_perm(__float_as_uint(xf[6]), __float_as_uint(xf[4]), 0x0b090c0cu);
+  const uint32_t no = __builtin_amdgcn_perm(__float_as_uint(xf[3]), __float_as_uint(xf[1]), 0x0c0c0b09u) |
+                      __builtin_amdgcn_perm(__float_as_uint(xf[7]), __float_as_uint(xf[5]), 0x0b090c0cu);
+  const uint32_t ee = be ^ ((ne & 0xF0F0F0F0u) | 0x07070707u);
+  const uint32_t eo = bo ^ ((no & 0xF0F0F0F0u) | 0x07070707u);
+  *anc_w = ((ee >> 4) & 0x0F0F0F0Fu) | (eo & 0xF0F0F0F0u);
+  *res_w = (ee & 0x0F0F0F0Fu) | ((eo << 4) & 0xF0F0F0F0u);
+}
+
+__global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
+  const Geometry& g = a.g;
+  const int slab = blockIdx.x & 1;
+  const int ph = blockIdx.x >> 1;                  // page * Hkv + head
+  const int page = ph / g.Hkv;
+  const int h = ph - page * g.Hkv;
+  const int tid = threadIdx.x, dg = tid & (kDG - 1), tg = tid / kDG, lane = tid & 63, wave = tid >> 6;
+  const int H = g.H;
+  const int ntiles = (g.P + kTileTokens - 1) / kTileTokens;
+  const int G = g.C / kTokPerThread;               // threads (token groups) per chunk
+  const int cbase = h * kHeadDim + slab * kSlab;   // first channel of the slab
+
+  const uint16_t* X = a.kv + (size_t)page * g.P * H + cbase + dg * 8;
+  uint8_t* anc = a.anchor + (size_t)page * g.anc_seg;
+  float* meta = reinterpret_cast<float*>(anc + g.codes);
+  const size_t code_off = (size_t)h * g.P * (kHeadDim / 2) + slab * (kSlab / 2) + dg * 4;
+  uint8_t* anc_codes = anc + code_off;
+  uint8_t* res_codes = a.residual ? a.residual + (size_t)page * g.res_seg + code_off : nullptr;
+
+  __shared__ double s_bnd[130];
+  __shared__ float s_rmin[4][kSlab], s_rmax[4][kSlab];
+  __shared__ double s_rsum[4][kSlab];
+  __shared__ float s_gmin[kSlab];
+  __shared__ double s_D1[kSlab], s_r1[kSlab];
+  __shared__ float s_mu[kTileTokens / 8][kSlab];
+  __shared__ double s_D2[kTileTokens / 8][kSlab];
+
+  for (int i = tid; i < 129; i += kThreads) s_bnd[i] = a.bnd[i];
+
+  uint4 v[kTokPerThread];
+  auto load_tile = [&](int t0) {
+    const int tok0 = t0 + tg * kTokPerThread;
+    if (tok0 < g.P) {
+#pragma unroll
+      for (int i = 0; i < kTokPerThread; ++i)
+        v[i] = ld_stream(X + (size_t)(tok0 + i) * H);
+    }
+  };
+
+  // ---- Stage 1: per-channel page min / max over all tokens ([Review] Stage 1)
+  {
+    float mn[8], mx[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { mn[j] = INFINITY; mx[j] = -INFINITY; }
+    for (int t = 0; t < ntiles; ++t) {
+      load_tile(t * kTileTokens);
+      if (t * kTileTokens + tg * kTokPerThread < g.P) {
+#pragma unroll
+        for (int i = 0; i < kTokPerThread; ++i) {
+          const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float lo = bf16_lo(q[k]), hi = bf16_hi(q[k]);
+            mn[2 * k] = fminf(mn[2 * k], lo);
+            mx[2 * k] = fmaxf(mx[2 * k], lo);
+            mn[2 * k + 1] = fminf(mn[2 * k + 1], hi);
+            mx[2 * k + 1] = fmaxf(mx[2 * k + 1], hi);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int m = 8; m < 64; m <<= 1) {
+        mn[j] = fminf(mn[j], __shfl_xor(mn[j], m));
+        mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], m));
+      }
+    }
+    if (lane < kDG) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { s_rmin[wave][dg * 8 + j] = mn[j]; s_rmax[wave][dg * 8 + j] = mx[j]; }
+    }
+  }
+  __syncthreads();
+  if (tid < kSlab) {
+    const int c = tid;
+    // + 0: a zero minimum / range is stored as +0 whatever the signs of the zeros
+    const float gmin = fminf(fminf(s_rmin[0][c], s_rmin[1][c]), fminf(s_rmin[2][c], s_rmin[3][c])) + 0.0f;
+    const float gmax = fmaxf(fmaxf(s_rmax[0][c], s_rmax[1][c]), fmaxf(s_rmax[2][c], s_rmax[3][c]));
+    const float gscale = (float)(((double)gmax - (double)gmin) + 0.0);   // exact difference, one rounding
+    const double D1 = (double)gscale + kEps;
+    s_gmin[c] = gmin;
+    s_D1[c] = D1;
+    s_r1[c] = 1.0 / D1;
+    meta[cbase + c] = gmin;
+    meta[H + cbase + c] = gscale;
+  }
+  __syncthreads();
+
+  const float alpha = a.alpha, ylog2k = a.ylog2k, zlim = 0.5f - a.ziv;
+  const double cC = (double)g.C, inv_c = 1.0 / (double)g.C;     // 1/C exact (C a power of two)
+  float* meta_mu = meta + 2 * H + cbase;
+  float* meta_sig = meta + 2 * H + (size_t)g.nck * H + cbase;
+
+  // ---- per tile: Stage 2 chunk statistics, then Stages 3-4 per element
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = t * kTileTokens;
+    if (ntiles > 1) load_tile(t0);
+    const int tok0 = t0 + tg * kTokPerThread;
+    const bool act = tok0 < g.P;
+    const int kc = (tg * kTokPerThread) / g.C;         // chunk within tile
+    const int kglob = tok0 / g.C;                      // chunk within page
+
+    double sm[8];
+    float cmn[8], cmx[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { sm[j] = 0.0; cmn[j] = INFINITY; cmx[j] = -INFINITY; }
+    if (act) {
+#pragma unroll
+      for (int i = 0; i < kTokPerThread; ++i) {
+        const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float lo = bf16_lo(q[k]), hi = bf16_hi(q[k]);
+          sm[2 * k] += (double)lo;
+          sm[2 * k + 1] += (double)hi;
+          cmn[2 * k] = fminf(cmn[2 * k], lo);
+          cmx[2 * k] = fmaxf(cmx[2 * k], lo);
+          cmn[2 * k + 1] = fminf(cmn[2 * k + 1], hi);
+          cmx[2 * k + 1] = fmaxf(cmx[2 * k + 1], hi);
+        }
+      }
+    }
+    // reduce over the G token groups of the chunk: lanes ^8, ^16, ^32, then across waves
+#pragma unroll
+    for (int m = 8; m < 64; m <<= 1) {
+      if (G >= 2 * (m / 8)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          sm[j] += shfl_xor_f64(sm[j], m);
+          cmn[j] = fminf(cmn[j], __shfl_xor(cmn[j], m));
+          cmx[j] = fmaxf(cmx[j], __shfl_xor(cmx[j], m));
+        }
+      }
+    }
+    if (G >= 16) {
+      if (lane < kDG) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          s_rsum[wave][dg * 8 + j] = sm[j];
+          s_rmin[wave][dg * 8 + j] = cmn[j];
+          s_rmax[wave][dg * 8 + j] = cmx[j];
+        }
+      }
+      __syncthreads();
+      const int wpc = G / 8;                       // waves per chunk (2 or 4)
+      const int w0 = (wave / wpc) * wpc;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        double s = 0.0;
+        float lo = INFINITY, hi = -INFINITY;
+        for (int w = w0; w < w0 + wpc; ++w) {
+          s += s_rsum[w][dg * 8 + j];
+          lo = fminf(lo, s_rmin[w][dg * 8 + j]);
+          hi = fmaxf(hi, s_rmax[w][dg * 8 + j]);
+        }
+        sm[j] = s; cmn[j] = lo; cmx[j] = hi;
+      }
+    }
+
+    // chunk metadata ([Review] Stage 2): mu = mean(X_n), sigma = max |X_n - mu|,
+    // both stored as float32 and used in their stored form from here on.  The
+    // mean comes from the float64 sum of the chunk's BF16 values; sigma from the
+    // chunk's extreme values (X_n is monotone in X).
+    float ch[8], ckn[8], kk[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = dg * 8 + j;
+      const double gmin = (double)s_gmin[c], D1 = s_D1[c], r1 = s_r1[c];
+      const double mean = (sm[j] - cC * gmin) * r1 * inv_c;
+      const float mu32 = (float)mean;
+      const double mu = (double)mu32;
+      const double xnmax = ((double)cmx[j] - gmin) * r1;
+      const double xnmin = ((double)cmn[j] - gmin) * r1;
+      const float sig32 = (float)fmax(fabs(xnmax - mu), fabs(mu - xnmin));
+      const double D2 = (double)sig32 + kEps;
+      // float32 fast path: X_f = (x - c) * k with the chunk centre c = gmin + mu*D1
+      // held as c_hi + c_lo, and k = 1/(D1*D2)
+      const double cen = gmin + mu * D1;
+      const float c_hi = (float)cen;
+      const float c_lo = (float)(cen - (double)c_hi);
+      const float k = __builtin_amdgcn_rcpf((float)(D1 * D2));
+      ch[j] = c_hi;
+      kk[j] = k;
+      ckn[j] = 0.0f - c_lo * k;     // +0 when c_lo == 0, so X_f never comes out as -0
+      if (act && (tg % G) == 0) {
+        s_mu[kc][c] = mu32;
+        s_D2[kc][c] = D2;
+        meta_mu[(size_t)kglob * H + c] = mu32;
+        meta_sig[(size_t)kglob * H + c] = sig32;
+      }
+    }
+    __syncthreads();
+
+    // ---- Stages 3-4 per element: float32 fast path for every element; the rare
+    // elements near a rounding boundary are re-decided in float64 afterwards and
+    // their nibbles patched in place (each thread only touches its own words).
+    if (act) {
+      uint32_t tokflags = 0;
+#pragma unroll
+      for (int i = 0; i < kTokPerThread; ++i) {
+        const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        float r[8], xf[8];
+        float dmax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
+          const float f = fmaf(x - ch[j], kk[j], ckn[j]);
+          const float tt = fmaf(alpha, fabsf(f), 1.0f);
+          const float Y = __builtin_amdgcn_logf(tt) * ylog2k;      // Eq. 7 in float32
+          const float rr = fminf(__builtin_rintf(Y), (float)kCodeMax);
+          dmax = fmaxf(dmax, fabsf(Y - rr));
+          r[j] = rr;
+          xf[j] = f;
+        }
+        tokflags |= (dmax > zlim) ? (1u << i) : 0u;
+        uint32_t aw, rw;
+        pack8(r, xf, &aw, &rw);
+        const int tok = tok0 + i;
+        *reinterpret_cast<uint32_t*>(anc_codes + (size_t)tok * (kHeadDim / 2)) = aw;
+        if (res_codes) *reinterpret_cast<uint32_t*>(res_codes + (size_t)tok * (kHeadDim / 2)) = rw;
+        // keep each token's flag test here: left alone the compiler defers every
+        // test to the end of the loop and holds all Y values live
+        asm volatile("" : "+v"(tokflags)::"memory");
+      }
+      while (tokflags) {
+        const int i = __builtin_ctz(tokflags);
+        tokflags &= tokflags - 1;
+        const int tok = tok0 + i;
+        const uint4 w = *reinterpret_cast<const uint4*>(X + (size_t)tok * H);
+        const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+        uint32_t* pa = reinterpret_cast<uint32_t*>(anc_codes + (size_t)tok * (kHeadDim / 2));
+        uint32_t* pr = res_codes ? reinterpret_cast<uint32_t*>(res_codes + (size_t)tok * (kHeadDim / 2)) : nullptr;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
+          const float f = fmaf(x - ch[j], kk[j], ckn[j]);
+          const float tt = fmaf(alpha, fabsf(f), 1.0f);
+          const float Y = __builtin_amdgcn_logf(tt) * ylog2k;
+          const float rr = fminf(__builtin_rintf(Y), (float)kCodeMax);
+          if (fabsf(Y - rr) > zlim) {
+            const int c = dg * 8 + j;
+            const uint32_t e = encode_exact(x, s_gmin[c], s_D1[c], s_mu[kc][c], s_D2[kc][c], s_bnd);
+            *pa = (*pa & ~(0xFu << (4 * j))) | ((e >> 4) << (4 * j));
+            if (pr) *pr = (*pr & ~(0xFu << (4 * j))) | ((e & 0xFu) << (4 * j));
+          }
+        }
+      }
+    }
+    if (ntiles > 1) __syncthreads();   // the LDS partials and chunk tables are reused by the next tile
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode ([Review] Mechanism 2: Q_approx = dequant(Q_anc, gamma, mu, sigma) and
+// Q_full = dequant(Q_anc + Q_res); Eq. 8; Worked Example Eq. 14-15)
+//   x_hat = ((S|x|)(sigma+eps) + mu)(gamma_scale+eps) + gamma_min = A*L + B
+//   with A = (gamma_scale+eps)(sigma+eps), B = gamma_min + mu(gamma_scale+eps)
+//   per (chunk, channel) and L = S|x| from a table indexed by the nibble(s).
+// ---------------------------------------------------------------------------
+template <bool FULL, bool F32OUT>
+__global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
+  const Geometry& g = a.g;
+  const int ntiles = (g.P + kTileTokens - 1) / kTileTokens;
+  int bid = blockIdx.x;
+  const int tile = bid % ntiles;
+  bid /= ntiles;
+  const int slab = bid & 1;
+  const int ph = bid >> 1;
+  const int page = ph / g.Hkv;
+  const int h = ph - page * g.Hkv;
+  const int tid = threadIdx.x, dg = tid & (kDG - 1), tg = tid / kDG;
+  const int H = g.H;
+  const int cbase = h * kHeadDim + slab * kSlab;
+
+  __shared__ float s_lut[256];
+  if (FULL) s_lut[tid] = a.lut[tid];
+  else if (tid < 16) s_lut[tid] = a.lut[tid];
+
+  const int tok0 = tile * kTileTokens + tg * kTokPerThread;
+  const bool act = tok0 < g.P;
+  const uint8_t* anc = a.anchor + (size_t)page * g.anc_seg;
+  const float* meta = reinterpret_cast<const float*>(anc + g.codes);
+  const size_t code_off = (size_t)h * g.P * (kHeadDim / 2) + slab * (kSlab / 2) + dg * 4;
+  const uint8_t* anc_codes = anc + code_off;
+  const uint8_t* res_codes = FULL ? a.residual + (size_t)page * g.res_seg + code_off : nullptr;
+
+  float A[8], B[8];
+  if (act) {
+    const int k = tok0 / g.C;
+    const int c0 = cbase + dg * 8;
+    const float4* pg = reinterpret_cast<const float4*>(meta + c0);
+    const float4* ps = reinterpret_cast<const float4*>(meta + H + c0);
+    const float4* pm = reinterpret_cast<const float4*>(meta + 2 * H + (size_t)k * H + c0);
+    const float4* pz = reinterpret_cast<const float4*>(meta + 2 * H + (size_t)(g.nck + k) * H + c0);
+    const float4 g0 = pg[0], g1 = pg[1], s0 = ps[0], s1 = ps[1], m0 = pm[0], m1 = pm[1], z0 = pz[0], z1 = pz[1];
+    const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float gs[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    const float mu[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    const float sg[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const double D1 = (double)gs[j] + kEps, D2 = (double)sg[j] + kEps;
+      A[j] = (float)(D1 * D2);
+      B[j] = (float)((double)gm[j] + (double)mu[j] * D1);
+    }
+  }
+  __syncthreads();
+  if (!act) return;
+
+#pragma unroll
+  for (int i = 0; i < kTokPerThread; ++i) {
+    const int tok = tok0 + i;
+    const uint32_t wa = *reinterpret_cast<const uint32_t*>(anc_codes + (size_t)tok * (kHeadDim / 2));
+    float o[8];
+    if (FULL) {
+      const uint32_t wr = *reinterpret_cast<const uint32_t*>(res_codes + (size_t)tok * (kHeadDim / 2));
+      const uint32_t ie = (wa & 0x0F0F0F0Fu) | ((wr & 0x0F0F0F0Fu) << 4);   // even elements: anc | res << 4
+      const uint32_t io = ((wa >> 4) & 0x0F0F0F0Fu) | (wr & 0xF0F0F0F0u);   // odd elements
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        o[2 * k] = fmaf(A[2 * k], s_lut[(ie >> (8 * k)) & 0xFF], B[2 * k]);
+        o[2 * k + 1] = fmaf(A[2 * k + 1], s_lut[(io >> (8 * k)) & 0xFF], B[2 * k + 1]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = fmaf(A[j], s_lut[(wa >> (4 * j)) & 0xF], B[j]);
+    }
+    const size_t off = (size_t)(page * g.P + tok) * H + cbase + dg * 8;
+    if (F32OUT) {
+      float* dst = static_cast<float*>(a.out) + off;
+      st_stream(dst, make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])));
+      st_stream(dst + 4, make_uint4(__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])));
+    } else {
+      uint4 pk;
+      pk.x = pack_bf16x2(o[0], o[1]);
+      pk.y = pack_bf16x2(o[2], o[3]);
+      pk.z = pack_bf16x2(o[4], o[5]);
+      pk.w = pack_bf16x2(o[6], o[7]);
+      st_stream(static_cast<uint16_t*>(a.out) + off, pk);
+    }
+  }
+}
+
+template __global__ void k_decode<false, false>(DecodeArgs);
+template __global__ void k_decode<false, true>(DecodeArgs);
+template __global__ void k_decode<true, false>(DecodeArgs);
+template __global__ void k_decode<true, true>(DecodeArgs);
+
+}  // namespace lynx

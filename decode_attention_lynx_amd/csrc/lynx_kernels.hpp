@@ -1,0 +1,23 @@
+// Kernel and launcher declarations shared between the C ABI shim and the kernel sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "lynx_common.hpp"
+
+namespace lynx {
+
+__global__ void k_encode(EncodeArgs a);
+template <bool FULL, bool F32OUT>
+__global__ void k_decode(DecodeArgs a);
+
+// Anchor-only decode attention (lynx_attn.hip).
+size_t attn_workspace_bytes(int batch, int ctx_tokens, int q_heads, int kv_heads, int head_dim, int page_tokens,
+                            int chunk);
+int attn_anchor_launch(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev, int batch,
+                       int ctx_tokens, int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk,
+                       float alpha, float sm_scale, void* workspace_dev, size_t ws_bytes, int out_dtype,
+                       void* out_dev, hipStream_t stream);
+
+}  // namespace lynx

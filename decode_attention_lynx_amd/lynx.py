@@ -1,0 +1,155 @@
+"""Thin ctypes binding of liblynx.so (C ABI declared in include/lynx.h).
+
+Argument marshalling only: tensors are passed as device pointers with the
+current HIP stream; every step of the codec and the attention runs in the
+library's HIP kernels.  Loading fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LYNX_OK = 0
+LYNX_EINVAL = -1
+LYNX_EALIGN = -2
+LYNX_EUNSUPPORTED = -3
+LYNX_ENOSPACE = -4
+LYNX_ELAUNCH = -5
+SEL_ANCHOR = 1
+SEL_RESIDUAL = 2
+OUT_BF16 = 0
+OUT_F32 = 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblynx.so")
+EXPORTS = ("lynx_strerror", "lynx_stream_sizes", "lynx_encode", "lynx_decode_anchor", "lynx_decode_full",
+           "lynx_attn_workspace_bytes", "lynx_attn_anchor")
+
+_lib = None
+
+
+class LynxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblynx.so once; raise if it was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"liblynx.so not found at {LIB_PATH}; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        c_int, c_float, c_uint, c_size, c_void = (ctypes.c_int, ctypes.c_float, ctypes.c_uint, ctypes.c_size_t,
+                                                   ctypes.c_void_p)
+        L.lynx_strerror.restype = ctypes.c_char_p
+        L.lynx_strerror.argtypes = [c_int]
+        L.lynx_stream_sizes.restype = c_int
+        L.lynx_stream_sizes.argtypes = [c_int, c_int, c_int, c_int, ctypes.POINTER(c_size), ctypes.POINTER(c_size)]
+        L.lynx_encode.restype = c_int
+        L.lynx_encode.argtypes = [c_void, c_int, c_int, c_int, c_int, c_int, c_float, c_uint, c_void, c_void, c_void]
+        L.lynx_decode_anchor.restype = c_int
+        L.lynx_decode_anchor.argtypes = [c_void, c_int, c_int, c_int, c_int, c_int, c_float, c_int, c_void, c_void]
+        L.lynx_decode_full.restype = c_int
+        L.lynx_decode_full.argtypes = [c_void, c_void, c_int, c_int, c_int, c_int, c_int, c_float, c_int, c_void,
+                                       c_void]
+        L.lynx_attn_workspace_bytes.restype = c_size
+        L.lynx_attn_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int]
+        L.lynx_attn_anchor.restype = c_int
+        L.lynx_attn_anchor.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                       c_float, c_float, c_void, c_size, c_int, c_void, c_void]
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().lynx_strerror(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != LYNX_OK:
+        raise LynxError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def stream_sizes(page_tokens: int, kv_heads: int, head_dim: int, chunk: int):
+    """(anchor segment bytes, residual segment bytes) of one page."""
+    a, r = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().lynx_stream_sizes(page_tokens, kv_heads, head_dim, chunk, ctypes.byref(a), ctypes.byref(r)),
+           "lynx_stream_sizes")
+    return a.value, r.value
+
+
+def encode(kv, page_tokens: int, chunk: int, alpha: float, residual: bool = True, anchor_out=None,
+           residual_out=None, stream=None):
+    """kv: CUDA bfloat16 [n_pages*P, Hkv, D].  Returns (anchor uint8 [n_pages, a_seg], residual or None)."""
+    import torch
+    T, Hkv, D = kv.shape
+    n_pages = T // page_tokens
+    a_sz, r_sz = stream_sizes(page_tokens, Hkv, D, chunk)
+    if anchor_out is None:
+        anchor_out = torch.empty((n_pages, a_sz), dtype=torch.uint8, device=kv.device)
+    if residual and residual_out is None:
+        residual_out = torch.empty((n_pages, r_sz), dtype=torch.uint8, device=kv.device)
+    sel = SEL_ANCHOR | (SEL_RESIDUAL if residual else 0)
+    _check(lib().lynx_encode(_ptr(kv), n_pages, page_tokens, Hkv, D, chunk, alpha, sel, _ptr(anchor_out),
+                             _ptr(residual_out) if residual else None, _stream(stream)), "lynx_encode")
+    return anchor_out, (residual_out if residual else None)
+
+
+def decode_anchor(anchor, n_pages: int, page_tokens: int, kv_heads: int, head_dim: int, chunk: int, alpha: float,
+                  out_dtype=None, out=None, stream=None):
+    """Anchor segments -> [n_pages*P, Hkv, D] tensor (bfloat16 by default, or float32)."""
+    import torch
+    dt = torch.bfloat16 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((n_pages * page_tokens, kv_heads, head_dim), dtype=dt, device=anchor.device)
+    code = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    _check(lib().lynx_decode_anchor(_ptr(anchor), n_pages, page_tokens, kv_heads, head_dim, chunk, alpha, code,
+                                    _ptr(out), _stream(stream)), "lynx_decode_anchor")
+    return out
+
+
+def decode_full(anchor, residual, n_pages: int, page_tokens: int, kv_heads: int, head_dim: int, chunk: int,
+                alpha: float, out_dtype=None, out=None, stream=None):
+    """Anchor + residual segments -> [n_pages*P, Hkv, D] tensor (bfloat16 by default, or float32)."""
+    import torch
+    dt = torch.bfloat16 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((n_pages * page_tokens, kv_heads, head_dim), dtype=dt, device=anchor.device)
+    code = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    _check(lib().lynx_decode_full(_ptr(anchor), _ptr(residual), n_pages, page_tokens, kv_heads, head_dim, chunk,
+                                  alpha, code, _ptr(out), _stream(stream)), "lynx_decode_full")
+    return out
+
+
+def attn_workspace_bytes(batch: int, ctx_tokens: int, q_heads: int, kv_heads: int, head_dim: int,
+                         page_tokens: int, chunk: int) -> int:
+    return int(lib().lynx_attn_workspace_bytes(batch, ctx_tokens, q_heads, kv_heads, head_dim, page_tokens, chunk))
+
+
+def attn_anchor(q, k_anchor, v_anchor, ctx_tokens: int, kv_heads: int, page_tokens: int, chunk: int, alpha: float,
+                sm_scale: float = 0.0, out_dtype=None, workspace=None, out=None, stream=None):
+    """q: CUDA bfloat16 [B, Hq, D]; k_anchor/v_anchor: B*ctx/P anchor segments.  Returns O [B, Hq, D]."""
+    import torch
+    B, Hq, D = q.shape
+    ws = attn_workspace_bytes(B, ctx_tokens, Hq, kv_heads, D, page_tokens, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
+    dt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=dt, device=q.device)
+    code = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    _check(lib().lynx_attn_anchor(_ptr(q), _ptr(k_anchor), _ptr(v_anchor), B, ctx_tokens, Hq, kv_heads, D,
+                                  page_tokens, chunk, alpha, sm_scale, _ptr(workspace), workspace.numel(), code,
+                                  _ptr(out), _stream(stream)), "lynx_attn_anchor")
+    return out

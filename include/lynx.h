@@ -91,7 +91,7 @@ int lynx_stream_sizes(int page_tokens, int kv_heads, int head_dim, int chunk,
  *   kv_dev      : BF16 [n_pages*P][kv_heads][head_dim], read only.
  *   n_pages     : >= 0; 0 is a no-op returning LYNX_OK.
  *   page_tokens : P, a multiple of `chunk`.
- *   chunk       : C, a multiple of 16, C <= P.
+ *   chunk       : C, a power of two in [8, 256] dividing P.
  *   alpha       : finite, > 0 (alpha-law parameter of Eq. 7).
  *   sel         : LYNX_SEL_ANCHOR, optionally | LYNX_SEL_RESIDUAL.
  *   anchor_dev  : n_pages anchor segments (see lynx_stream_sizes), written.

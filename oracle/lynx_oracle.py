@@ -43,6 +43,8 @@ Readings (where the pages are silent, ambiguous or inconsistent):
             gamma_min f32[H], gamma_scale f32[H], mu f32[P/C][H],
             sigma f32[P/C][H] (H = kv_heads*head_dim, channel = h*D + d);
             the residual segment is the residual nibbles alone.
+  R-zero    the sign of a zero is not data: a zero gamma_min or gamma_scale is
+            stored as +0 whatever the signs of the zeros in the channel.
   R-attn    decode attention is Eq. 1 over the anchor-only reconstruction;
             query head hq uses kv head hq // (Hq/Hkv) (contiguous groups).
 """
@@ -95,9 +97,9 @@ def page_stats(X: np.ndarray):
     gamma_min is a BF16 value, so its float32 copy is exact; gamma_scale is the
     float64 range (max - min) rounded once to float32 (R-meta).
     """
-    gmin = X.min(axis=0)
+    gmin = X.min(axis=0) + 0.0                  # + 0.0: a zero minimum is stored as +0 (R-zero)
     gmax = X.max(axis=0)
-    return gmin.astype(np.float32), (gmax - gmin).astype(np.float32)
+    return gmin.astype(np.float32), ((gmax - gmin) + 0.0).astype(np.float32)
 
 
 def normalize_page(X: np.ndarray, gmin32: np.ndarray, gscale32: np.ndarray) -> np.ndarray:

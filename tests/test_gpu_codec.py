@@ -1,0 +1,126 @@
+"""GPU parity of the codec (encode, anchor-only decode, full decode) against the oracle.
+
+Every page the oracle checks is compared element by element under the contract
+written in tests/parity.py.  Cases span several 256-token tiles, ragged tails,
+every supported chunk size, the three alpha values of the sweep, and the
+degenerate inputs the method has (constant channels and chunks, signed zeros,
+extreme magnitudes).
+"""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_lynx_amd import lynx, synth
+from oracle import lynx_oracle as o
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def to_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def run_codec(bits: np.ndarray, P: int, C: int, alpha: float, pages=None, label="", bf16_share=parity.CODE_FLIP_FRAC):
+    """Encode + both decoders on the GPU; oracle comparison on `pages` (default: all)."""
+    T, Hkv, D = bits.shape
+    n_pages = T // P
+    print(f"[codec] {label} T={T} Hkv={Hkv} P={P} C={C} alpha={alpha}", flush=True)
+    kv = to_dev(bits)
+    anc, res = lynx.encode(kv, P, C, alpha)
+    outs = {
+        "anc32": lynx.decode_anchor(anc, n_pages, P, Hkv, D, C, alpha, out_dtype=torch.float32),
+        "full32": lynx.decode_full(anc, res, n_pages, P, Hkv, D, C, alpha, out_dtype=torch.float32),
+        "anc16": lynx.decode_anchor(anc, n_pages, P, Hkv, D, C, alpha),
+        "full16": lynx.decode_full(anc, res, n_pages, P, Hkv, D, C, alpha),
+    }
+    torch.cuda.synchronize()
+    A, R = anc.cpu().numpy(), res.cpu().numpy()
+    host = {k: v.cpu() for k, v in outs.items()}
+    H = Hkv * D
+    rep = {}
+    for p in (range(n_pages) if pages is None else pages):
+        X = o.bf16_bits_to_f64(bits[p * P:(p + 1) * P]).reshape(P, H)
+        enc = o.encode_page(X, C, alpha)
+        got = o.parse_anchor_segment(A[p], P, Hkv, D, C)
+        q_res = o.unpack_nibbles(R[p], P, Hkv, D)
+        parity.check_metadata(got, enc, X, C, rep)
+        parity.check_codes(got, q_res, X, C, alpha, rep)
+        args = (got["mu"], got["sigma"], got["gmin"], got["gscale"], C, alpha)
+        ref_full = o.decode_page_full(got["Q_anc"], q_res, *args)
+        ref_anc = o.decode_page_anchor(got["Q_anc"], *args)
+        sl = slice(p * P, (p + 1) * P)
+        parity.check_decode_f32(host["full32"][sl].numpy().reshape(P, H), ref_full, got["gscale"], rep)
+        parity.check_decode_f32(host["anc32"][sl].numpy().reshape(P, H), ref_anc, got["gscale"], rep)
+        parity.check_decode_bf16(host["full16"][sl].view(torch.int16).numpy().view(np.uint16).reshape(P, H),
+                                 ref_full, parity.decode_slack(got, ref_full, C), rep)
+        parity.check_decode_bf16(host["anc16"][sl].view(torch.int16).numpy().view(np.uint16).reshape(P, H),
+                                 ref_anc, parity.decode_slack(got, ref_anc, C), rep)
+    parity.finish_codes(rep)
+    parity.finish_bf16(rep, bf16_share)
+    print(f"[codec] {label} report {rep}", flush=True)
+    return anc, res, rep
+
+
+def test_single_page_4096_tokens_k_and_v(gpu):
+    """One 4096-token page of K and of V, 8 kv heads x 128, C = 64, alpha = 255, seed 0."""
+    for kv_idx in (0, 1):
+        bits = synth.make_kv_np(4096, 8, 128, seed=0, layer=0, kv_idx=kv_idx)
+        run_codec(bits, 4096, 64, 255.0, label=f"page4096 kv{kv_idx}")
+
+
+@pytest.mark.parametrize("P,C,alpha,Hkv,n_pages", [
+    (256, 64, 255.0, 2, 3),
+    (256, 8, 15.0, 1, 2),
+    (256, 16, 63.0, 1, 2),
+    (256, 32, 255.0, 2, 1),
+    (256, 128, 63.0, 1, 2),
+    (256, 256, 15.0, 1, 2),
+    (320, 64, 255.0, 1, 2),     # 256-token tile plus a 64-token ragged tile
+    (24, 8, 255.0, 1, 3),       # a page shorter than one tile
+    (512, 256, 255.0, 1, 1),    # chunk spanning all four waves, two tiles
+    (768, 128, 63.0, 1, 1),
+    (64, 64, 100.0, 4, 2),
+])
+def test_codec_shapes(gpu, P, C, alpha, Hkv, n_pages):
+    bits = synth.make_kv_np(P * n_pages, Hkv, 128, seed=P + C, layer=Hkv)
+    run_codec(bits, P, C, alpha, label=f"shape P{P} C{C}")
+
+
+def test_degenerate_pages(gpu):
+    """Constant channels (at zero, negative, with -0.0), a constant chunk inside a live
+    channel, huge and tiny magnitudes, and an all-constant page."""
+    P, C, Hkv, D = 256, 32, 1, 128
+    rng = np.random.default_rng(7)
+    X = rng.laplace(0, 0.5, size=(2 * P, Hkv, D)).astype(np.float32)
+    X[:, 0, 0] = 0.0
+    X[:, 0, 1] = -3.5
+    X[::2, 0, 2] = -0.0
+    X[1::2, 0, 2] = 0.0
+    X[64:96, 0, 3] = 1.25                          # one constant chunk in a live channel
+    X[:, 0, 4] *= 1e30                             # huge values
+    X[:, 0, 5] *= 1e-30                            # tiny values (normal BF16)
+    X[:, 0, 6] = np.where(np.arange(2 * P) % 2 == 0, 1e-38, -1e-38)   # near the subnormal range
+    X[P:, 0, 7:] = 2.0                             # second page: constant except channels 0..6
+    X[:, 0, 8] = rng.choice([-1.0, 1.0], size=2 * P) * 2.0 ** rng.integers(-20, 20, size=2 * P)
+    bits = o.f64_to_bf16_bits(X.astype(np.float64))
+    run_codec(bits, P, C, 255.0, label="degenerate", bf16_share=None)
+
+
+def test_zero_pages_is_a_noop(gpu):
+    kv = torch.empty((0, 8, 128), dtype=torch.bfloat16, device="cuda")
+    sentinel = torch.full((1, 16), 0xAB, dtype=torch.uint8, device="cuda")
+    st = lynx.lib().lynx_encode(lynx._ptr(kv), 0, 256, 8, 128, 64, 255.0, 3, lynx._ptr(sentinel),
+                                lynx._ptr(sentinel), None)
+    torch.cuda.synchronize()
+    assert st == lynx.LYNX_OK and bool((sentinel == 0xAB).all())
+
+
+def test_anchor_only_encode_matches_full_encode(gpu):
+    """sel = ANCHOR writes the same anchor segment as sel = ANCHOR | RESIDUAL."""
+    bits = synth.make_kv_np(512, 2, 128, seed=3)
+    kv = to_dev(bits)
+    a1, r1 = lynx.encode(kv, 256, 64, 255.0)
+    a2, r2 = lynx.encode(kv, 256, 64, 255.0, residual=False)
+    torch.cuda.synchronize()
+    assert r2 is None and torch.equal(a1, a2)

@@ -371,3 +371,14 @@ def test_attention_anchor_uses_anchor_decode():
     Kh = o.decode_anchor(ka, B * T // P, P, Hkv, D, C, 63.0).reshape(B, T, Hkv, D)
     Vh = o.decode_anchor(va, B * T // P, P, Hkv, D, C, 63.0).reshape(B, T, Hkv, D)
     assert np.max(np.abs(O - o.attention(o.bf16_bits_to_f64(qb), Kh, Vh))) < 1e-12
+
+
+def test_signed_zero_metadata_is_plus_zero():
+    """Reading R-zero: a channel of +-0 values stores gamma_min = gamma_scale = +0 and encodes to
+    (I, S) = (0, +1) everywhere, as the constant-channel closed form."""
+    X = np.zeros((32, 2))
+    X[::2, 0] = -0.0
+    X[:, 1] = -0.0
+    enc = o.encode_page(X, 16, 255.0)
+    assert np.all(enc["gmin"].view(np.uint32) == 0) and np.all(enc["gscale"].view(np.uint32) == 0)
+    assert np.all(enc["I"] == 0) and np.all(enc["S"] == 1)
