@@ -1,14 +1,408 @@
-// Anchor-only decode attention (placeholder until the fused kernel lands).
+// Single-token decode attention over anchor-only codes (the speculative draft
+// path), fused with the anchor decode, for gfx950.
+//
+// Sources, cited by page title and section:
+//   [Review] "Lynx: Progressive Speculative KV Cache Transfer for Disaggregated
+//            LLM Inference" (technical review of arXiv 2607.01831):
+//            Prerequisites §1, Eq. 1 (O = softmax(Q K^T / sqrt(d_k)) V);
+//            Mechanism 2, decode-side anchor phase (drafting runs on
+//            Q_approx = dequant(Q_anc, gamma, mu, sigma)); Mechanism 1, Eq. 8-9.
+//
+// The anchor decode of a key is k_hat[t,d] = A[c,d] L[n_td] + B[c,d] with
+// A = (gamma_scale+eps)(sigma+eps), B = gamma_min + mu(gamma_scale+eps) for the
+// chunk c of token t, and L[n] = S|x| of the anchor nibble n.  Folding the
+// per-chunk affine map into the query turns the score into
+//     q . k_hat_t = sum_d (q_d A[c,d]) L[n_td] + sum_d q_d B[c,d],
+// a dense contraction over the raw nibble table values, which runs on MFMA.
+// Likewise sum_t p_t v_hat[t,d] = A_V[c,d] sum_t p_t L[n_td] + B_V[c,d] sum_t p_t.
+//
+// Decomposition: one workgroup (4 waves) per (sequence, kv head, context split);
+// each wave walks 64-token tiles (one tile lies inside one chunk because the
+// chunk is a multiple of 64) with an online softmax, the 4 waves merge in LDS
+// and write one partial (m, l, o[128]) per query head; k_attn_combine merges the
+// splits with the log-sum-exp rule.
+//
+// MFMA v_mfma_f32_16x16x32_f16 (A 16x32, B 32x16, C 16x16; lane l supplies row /
+// column l % 16 and the k-block l / 16; C rows 4*(l/16)..+3, column l % 16):
+//   scores  S^T[token, col] = sum_d L[token, d] * qt[d, col]: A = nibble-table
+//           values of 16 tokens, B = the folded query, columns 0..7 = the float16
+//           high part of q*A per head, columns 8..15 = the float16 remainder, so
+//           one MFMA carries a ~22-bit query; the two halves are added after.
+//   values  O^T[d, col] += sum_t L_V[t, d] * p[t, col]: A = table values of 16
+//           channels over 32 tokens, B = float16 probabilities.
 #include "../../include/lynx.h"
 #include "lynx_kernels.hpp"
 
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
 namespace lynx {
 
-size_t attn_workspace_bytes(int, int, int, int, int, int, int) { return 0; }
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
 
-int attn_anchor_launch(const void*, const void*, const void*, int, int, int, int, int, int, int, float, float,
-                       void*, size_t, int, void*, hipStream_t) {
-  return LYNX_EUNSUPPORTED;
+constexpr int kAttnWaves = 4;
+constexpr int kAttnTile = 64;        // tokens per wave iteration
+constexpr int kMaxGroup = 8;         // query heads per kv head handled by one workgroup
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint8_t* kanc;
+  const uint8_t* vanc;
+  float* ws;
+  void* out;
+  int B, T, Hq, Hkv, G, P, C, npages, nck, H;
+  long long anc_seg, codes;
+  int splits, tiles_per_split, ntiles;
+  float qscale;        // sm_scale * log2(e): scores are kept in base 2
+  int out_f32;
+  uint16_t lut[16];    // float16 bits of S|x| for each anchor nibble (I = 16*V_mag + 7)
+};
+
+__device__ __forceinline__ float dpp_row_ror8(float v) {
+  // rotate right by 8 lanes inside each row of 16: column n reads column n ^ 8
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ _Float16 lut_at(const uint16_t* s_lut, uint32_t nib) {
+  return __builtin_bit_cast(_Float16, s_lut[nib]);
+}
+
+// 8 consecutive channels of one token (one dword of nibbles) -> MFMA A operand
+__device__ __forceinline__ h8 lookup_row(uint32_t w, const uint16_t* s_lut) {
+  h8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = lut_at(s_lut, (w >> (4 * e)) & 15u);
+  return r;
+}
+
+// nibble j of 8 dwords (8 tokens, same channel) -> MFMA A operand
+__device__ __forceinline__ h8 lookup_col(const uint32_t* w, int j, const uint16_t* s_lut) {
+  h8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = lut_at(s_lut, (w[e] >> (4 * j)) & 15u);
+  return r;
+}
+
+__device__ __forceinline__ float wave_max_g(float v) {   // over the 4 lane groups (l / 16)
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float wave_sum_g(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+__global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int hh = n & 7;                 // query head (within the group) of this column
+  const bool lo_col = n >= 8;
+
+  __shared__ uint16_t s_lut[16];
+  __shared__ float s_m[kAttnWaves][kMaxGroup], s_l[kAttnWaves][kMaxGroup];
+  __shared__ float s_o[kAttnWaves][kMaxGroup][kHeadDim];
+
+  if (tid < 16) s_lut[tid] = a.lut[tid];
+
+  // this lane's query slice: head hh, channels d = 32g .. 32g+31, pre-scaled into base 2
+  float qs[32];
+  {
+    const bool live = hh < a.G;
+    const uint16_t* qp = a.q + ((size_t)(b * a.Hq + kvh * a.G + (live ? hh : 0))) * kHeadDim + 32 * g;
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qp + 8 * v4);
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        qs[8 * v4 + 2 * k] = live ? bf16_lo(u[k]) * a.qscale : 0.0f;
+        qs[8 * v4 + 2 * k + 1] = live ? bf16_hi(u[k]) * a.qscale : 0.0f;
+      }
+    }
+  }
+  __syncthreads();
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f4 o_acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o_acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const int t_begin = split * a.tiles_per_split;
+  const int t_end = min(a.ntiles, t_begin + a.tiles_per_split);
+  const int cbase = kvh * kHeadDim + 32 * g;
+
+  for (int tile = t_begin + wave; tile < t_end; tile += kAttnWaves) {
+    const int tok = tile * kAttnTile;
+    const int page = tok / a.P;
+    const int tin = tok - page * a.P;
+    const int kc = tin / a.C;
+    const size_t seg = ((size_t)b * a.npages + page) * (size_t)a.anc_seg;
+    const uint8_t* kseg = a.kanc + seg;
+    const uint8_t* vseg = a.vanc + seg;
+    const float* kmeta = reinterpret_cast<const float*>(kseg + a.codes);
+    const float* vmeta = reinterpret_cast<const float*>(vseg + a.codes);
+
+    // ---- codes: K rows (token tin + 16mb + n, 16 B at 16g), V dwords (column n of 8 rows per k-step)
+    const uint8_t* kc_ptr = kseg + (size_t)kvh * a.P * (kHeadDim / 2) + (size_t)tin * (kHeadDim / 2) + 16 * g;
+    uint4 kw[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) kw[mb] = *reinterpret_cast<const uint4*>(kc_ptr + (16 * mb + n) * (kHeadDim / 2));
+    const uint8_t* vc_ptr = vseg + (size_t)kvh * a.P * (kHeadDim / 2) + (size_t)tin * (kHeadDim / 2) + 4 * n;
+    uint32_t vw[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int row = 32 * ks + (r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4));
+        vw[ks][r] = *reinterpret_cast<const uint32_t*>(vc_ptr + row * (kHeadDim / 2));
+      }
+
+    // ---- fold the key chunk's affine map into the query: qt = q*A_K (float16 hi / lo by column), beta = q.B_K
+    h8 bq[4];
+    float beta = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c0 = cbase + 8 * kk;
+      const float4* pgm = reinterpret_cast<const float4*>(kmeta + c0);
+      const float4* pgs = reinterpret_cast<const float4*>(kmeta + a.H + c0);
+      const float4* pmu = reinterpret_cast<const float4*>(kmeta + 2 * a.H + (size_t)kc * a.H + c0);
+      const float4* psg = reinterpret_cast<const float4*>(kmeta + 2 * a.H + (size_t)(a.nck + kc) * a.H + c0);
+      const float4 gm0 = pgm[0], gm1 = pgm[1], gs0 = pgs[0], gs1 = pgs[1];
+      const float4 mu0 = pmu[0], mu1 = pmu[1], sg0 = psg[0], sg1 = psg[1];
+      const float gm[8] = {gm0.x, gm0.y, gm0.z, gm0.w, gm1.x, gm1.y, gm1.z, gm1.w};
+      const float gs[8] = {gs0.x, gs0.y, gs0.z, gs0.w, gs1.x, gs1.y, gs1.z, gs1.w};
+      const float mu[8] = {mu0.x, mu0.y, mu0.z, mu0.w, mu1.x, mu1.y, mu1.z, mu1.w};
+      const float sg[8] = {sg0.x, sg0.y, sg0.z, sg0.w, sg1.x, sg1.y, sg1.z, sg1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float D1 = gs[e] + (float)kEps, D2 = sg[e] + (float)kEps;
+        const float x = qs[8 * kk + e];
+        const float qt = x * (D1 * D2);
+        beta = fmaf(x, fmaf(mu[e], D1, gm[e]), beta);
+        const _Float16 hi = (_Float16)qt;
+        bq[kk][e] = lo_col ? (_Float16)(qt - (float)hi) : hi;
+      }
+    }
+    beta = wave_sum_g(beta);
+
+    // ---- scores: S^T = L_K (64 tokens x 128) * qt (128 x 16 columns)
+    float s[16];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+      const uint32_t w4[4] = {kw[mb].x, kw[mb].y, kw[mb].z, kw[mb].w};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lookup_row(w4[kk], s_lut), bq[kk], acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[4 * mb + i] = acc[i] + dpp_row_ror8(acc[i]) + beta;
+    }
+
+    // ---- online softmax (base 2) for head hh over this tile's 64 tokens
+    float mt = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
+    mt = wave_max_g(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float corr = exp2f(m_run - m_new);
+    float lsum = 0.0f;
+    h8 pt[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = exp2f(s[i] - m_new);
+      lsum += p;
+      pt[i >> 3][i & 7] = (_Float16)p;
+    }
+    l_run = fmaf(l_run, corr, lsum);
+    if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0) {   // the running max moved for some head
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o_acc[j] *= corr;
+    }
+    m_run = m_new;
+    const float lt = wave_sum_g(lsum);
+
+    // ---- values: T^T = L_V (128 x 64 tokens) * p (64 tokens x 16 columns), block j holds d = 8*row + j
+    f4 tacc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      tacc[j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        tacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lookup_col(vw[ks], j, s_lut), pt[ks], tacc[j], 0, 0, 0);
+    }
+
+    // ---- undo the value chunk's affine map: o += A_V * T + B_V * sum(p)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c0 = cbase + 8 * i;      // d = 32g + 8i + j
+      const float4* pgm = reinterpret_cast<const float4*>(vmeta + c0);
+      const float4* pgs = reinterpret_cast<const float4*>(vmeta + a.H + c0);
+      const float4* pmu = reinterpret_cast<const float4*>(vmeta + 2 * a.H + (size_t)kc * a.H + c0);
+      const float4* psg = reinterpret_cast<const float4*>(vmeta + 2 * a.H + (size_t)(a.nck + kc) * a.H + c0);
+      const float4 gm0 = pgm[0], gm1 = pgm[1], gs0 = pgs[0], gs1 = pgs[1];
+      const float4 mu0 = pmu[0], mu1 = pmu[1], sg0 = psg[0], sg1 = psg[1];
+      const float gm[8] = {gm0.x, gm0.y, gm0.z, gm0.w, gm1.x, gm1.y, gm1.z, gm1.w};
+      const float gs[8] = {gs0.x, gs0.y, gs0.z, gs0.w, gs1.x, gs1.y, gs1.z, gs1.w};
+      const float mu[8] = {mu0.x, mu0.y, mu0.z, mu0.w, mu1.x, mu1.y, mu1.z, mu1.w};
+      const float sg[8] = {sg0.x, sg0.y, sg0.z, sg0.w, sg1.x, sg1.y, sg1.z, sg1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float D1 = gs[j] + (float)kEps, D2 = sg[j] + (float)kEps;
+        o_acc[j][i] = fmaf(D1 * D2, tacc[j][i], fmaf(fmaf(mu[j], D1, gm[j]), lt, o_acc[j][i]));
+      }
+    }
+  }
+
+  // ---- merge the 4 waves (columns 0..G-1 hold the result; 8..15 duplicate them)
+  l_run = wave_sum_g(l_run);
+  if (g == 0 && n < kMaxGroup) { s_m[wave][n] = m_run; s_l[wave][n] = l_run; }
+  if (n < kMaxGroup) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_o[wave][n][8 * (4 * g + i) + j] = o_acc[j][i];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < a.G * kHeadDim; idx += kAttnWaves * 64) {
+    const int h = idx / kHeadDim, d = idx - h * kHeadDim;
+    float M = s_m[0][h];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float f = (s_m[w][h] == -INFINITY) ? 0.0f : exp2f(s_m[w][h] - M);
+      o = fmaf(s_o[w][h][d], f, o);
+      l = fmaf(s_l[w][h], f, l);
+    }
+    float* rec = a.ws + ((size_t)((b * a.Hq + kvh * a.G + h) * a.splits + split)) * (kHeadDim + 2);
+    rec[2 + d] = o;
+    if (d == 0) { rec[0] = M; rec[1] = l; }
+  }
+}
+
+// log-sum-exp merge of the context splits: one workgroup per (sequence, query head)
+__global__ __launch_bounds__(kHeadDim) void k_attn_combine(AttnArgs a) {
+  const int bh = blockIdx.x;       // b * Hq + hq
+  const int d = threadIdx.x;
+  const float* rec = a.ws + (size_t)bh * a.splits * (kHeadDim + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, rec[(size_t)s * (kHeadDim + 2)]);
+  float o = 0.0f, l = 0.0f;
+  for (int s = 0; s < a.splits; ++s) {
+    const float* r = rec + (size_t)s * (kHeadDim + 2);
+    const float f = (r[0] == -INFINITY) ? 0.0f : exp2f(r[0] - M);
+    o = fmaf(r[2 + d], f, o);
+    l = fmaf(r[1], f, l);
+  }
+  const float res = o / l;
+  if (a.out_f32) static_cast<float*>(a.out)[(size_t)bh * kHeadDim + d] = res;
+  else {
+    const uint32_t u = __float_as_uint(res);
+    static_cast<uint16_t*>(a.out)[(size_t)bh * kHeadDim + d] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+namespace {
+
+struct AttnPlan {
+  int splits, tiles_per_split, ntiles;
+};
+
+bool attn_plan(int batch, int ctx, int Hq, int Hkv, int D, int P, int C, AttnPlan* pl) {
+  if (batch <= 0 || ctx <= 0 || Hq <= 0 || Hkv <= 0 || P <= 0 || C <= 0) return false;
+  if (ctx % P != 0 || P % C != 0 || Hq % Hkv != 0) return false;
+  if (D != kHeadDim || C % kAttnTile != 0 || Hq / Hkv > kMaxGroup) return false;
+  pl->ntiles = ctx / kAttnTile;
+  const long long units = (long long)batch * Hkv;
+  int want = (int)((2048 + units - 1) / units);               // aim for ~2048 workgroups
+  want = std::max(1, std::min(want, pl->ntiles));
+  pl->tiles_per_split = (pl->ntiles + want - 1) / want;
+  pl->splits = (pl->ntiles + pl->tiles_per_split - 1) / pl->tiles_per_split;   // no empty split
+  return true;
+}
+
+uint16_t f64_to_f16_bits(double x) {
+  const _Float16 h = (_Float16)x;     // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+}  // namespace
+
+size_t attn_workspace_bytes(int batch, int ctx, int Hq, int Hkv, int D, int P, int C) {
+  AttnPlan pl;
+  if (!attn_plan(batch, ctx, Hq, Hkv, D, P, C, &pl)) return 0;
+  return (size_t)batch * Hq * pl.splits * (kHeadDim + 2) * sizeof(float);
+}
+
+int attn_anchor_launch(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev, int batch,
+                       int ctx_tokens, int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk,
+                       float alpha, float sm_scale, void* workspace_dev, size_t ws_bytes, int out_dtype,
+                       void* out_dev, hipStream_t stream) {
+  if (batch < 0 || ctx_tokens <= 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 || page_tokens <= 0 ||
+      chunk <= 0)
+    return LYNX_EINVAL;
+  if (ctx_tokens % page_tokens != 0 || page_tokens % chunk != 0 || q_heads % kv_heads != 0) return LYNX_EINVAL;
+  if (!std::isfinite(alpha) || !(alpha > 0.0f) || !std::isfinite(sm_scale)) return LYNX_EINVAL;
+  if (out_dtype != LYNX_OUT_BF16 && out_dtype != LYNX_OUT_F32) return LYNX_EINVAL;
+  if (head_dim != kHeadDim || chunk % kAttnTile != 0 || q_heads / kv_heads > kMaxGroup || batch > 65535 ||
+      kv_heads > 65535)
+    return LYNX_EUNSUPPORTED;
+  if (batch == 0) return LYNX_OK;
+  AttnPlan pl;
+  if (!attn_plan(batch, ctx_tokens, q_heads, kv_heads, head_dim, page_tokens, chunk, &pl)) return LYNX_EINVAL;
+  const size_t need = (size_t)batch * q_heads * pl.splits * (kHeadDim + 2) * sizeof(float);
+  auto al16 = [](const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (!al16(q_dev) || !al16(k_anchor_dev) || !al16(v_anchor_dev) || !al16(out_dev) || !al16(workspace_dev))
+    return LYNX_EALIGN;
+  if (ws_bytes < need) return LYNX_ENOSPACE;
+
+  AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(q_dev);
+  a.kanc = static_cast<const uint8_t*>(k_anchor_dev);
+  a.vanc = static_cast<const uint8_t*>(v_anchor_dev);
+  a.ws = static_cast<float*>(workspace_dev);
+  a.out = out_dev;
+  a.B = batch;
+  a.T = ctx_tokens;
+  a.Hq = q_heads;
+  a.Hkv = kv_heads;
+  a.G = q_heads / kv_heads;
+  a.P = page_tokens;
+  a.C = chunk;
+  a.npages = ctx_tokens / page_tokens;
+  a.nck = page_tokens / chunk;
+  a.H = kv_heads * head_dim;
+  a.codes = (long long)page_tokens * a.H / 2;
+  a.anc_seg = a.codes + 4ll * a.H * (2 + 2ll * a.nck);
+  a.splits = pl.splits;
+  a.tiles_per_split = pl.tiles_per_split;
+  a.ntiles = pl.ntiles;
+  const double scale = sm_scale > 0.0f ? (double)sm_scale : 1.0 / std::sqrt((double)head_dim);
+  a.qscale = (float)(scale * 1.4426950408889634);   // log2(e)
+  a.out_f32 = out_dtype == LYNX_OUT_F32;
+  const double al = (double)alpha, L = std::log1p(al);
+  for (int nib = 0; nib < 16; ++nib) {
+    const int qv = nib >= 8 ? nib - 16 : nib;                 // Q_anc
+    const int S = qv < 0 ? -1 : 1, vmag = qv < 0 ? -qv - 1 : qv;
+    const double mag = std::expm1((double)(16 * vmag + 7) / kCodeMax * L) / al;
+    a.lut[nib] = f64_to_f16_bits(S * mag);
+  }
+  void* kargs[] = {&a};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&k_attn_anchor),
+                                 dim3((unsigned)pl.splits, (unsigned)kv_heads, (unsigned)batch),
+                                 dim3(kAttnWaves * 64), kargs, 0, stream);
+  if (e != hipSuccess) return LYNX_ELAUNCH;
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&k_attn_combine), dim3((unsigned)(batch * q_heads)),
+                      dim3(kHeadDim), kargs, 0, stream);
+  return e == hipSuccess ? LYNX_OK : LYNX_ELAUNCH;
 }
 
 }  // namespace lynx

@@ -1,0 +1,105 @@
+"""GPU parity of the fused anchor-only decode attention against the oracle.
+
+The oracle (float64) decodes the same anchor segments and evaluates Eq. 1 of
+the technical review (softmax(q K^T / sqrt(d)) V) per query head.  Bar:
+relative L2 of the whole output <= 2e-3 (float32 output); the worst head is
+reported.  Small cases use oracle-encoded codes uploaded to the GPU, so the
+attention is checked independently of the GPU encoder; the full-size case
+(16 sequences x 32768 tokens) uses GPU-encoded codes and samples sequences.
+"""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_lynx_amd import lynx, synth
+from oracle import lynx_oracle as o
+
+pytestmark = pytest.mark.gpu
+REL_L2 = 2e-3
+
+
+def rel_l2(got, ref):
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+def worst_head(got, ref):
+    e = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+    return float(e.max())
+
+
+def upload(u8: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(u8)).cuda()
+
+
+def make_case(B, Hq, Hkv, T, P, C, alpha, seed):
+    kb = np.concatenate([synth.make_kv_np(T, Hkv, 128, seed=seed, layer=b, kv_idx=0) for b in range(B)])
+    vb = np.concatenate([synth.make_kv_np(T, Hkv, 128, seed=seed, layer=b, kv_idx=1) for b in range(B)])
+    ka, _, _ = o.encode(kb, P, C, alpha)
+    va, _, _ = o.encode(vb, P, C, alpha)
+    qb = synth.make_q_np(B, Hq, 128, seed=seed)
+    return qb, ka, va
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,P,C,alpha", [
+    (2, 16, 2, 1024, 256, 64, 255.0),
+    (3, 8, 1, 320, 64, 64, 255.0),       # 5 pages of 64 tokens: ragged split of tiles
+    (2, 12, 4, 512, 256, 128, 63.0),     # group of 3 query heads, chunk of 128
+    (1, 2, 2, 64, 64, 64, 15.0),         # one tile, group of 1
+    (1, 64, 8, 2048, 256, 64, 255.0),    # the full head geometry, short context
+])
+def test_attention_small(gpu, B, Hq, Hkv, T, P, C, alpha):
+    print(f"[attn] B={B} Hq={Hq} Hkv={Hkv} T={T} P={P} C={C} alpha={alpha}", flush=True)
+    qb, ka, va = make_case(B, Hq, Hkv, T, P, C, alpha, seed=T + Hq)
+    ref = o.attention_anchor(qb, ka, va, B, T, Hq, Hkv, 128, P, C, alpha)
+    q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).cuda()
+    k, v = upload(ka), upload(va)
+    out32 = lynx.attn_anchor(q, k, v, T, Hkv, P, C, alpha, out_dtype=torch.float32)
+    out16 = lynx.attn_anchor(q, k, v, T, Hkv, P, C, alpha, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    got = out32.cpu().numpy().astype(np.float64)
+    e, w = rel_l2(got, ref), worst_head(got, ref)
+    print(f"[attn] rel_l2={e:.3e} worst_head={w:.3e}", flush=True)
+    assert e <= REL_L2
+    # the BF16 output is the float32 result rounded to nearest even
+    g16 = out16.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(g16, o.f64_to_bf16_bits(out32.cpu().numpy().astype(np.float64)))
+
+
+def test_attention_sm_scale_argument(gpu):
+    """sm_scale > 0 replaces 1/sqrt(128)."""
+    B, Hq, Hkv, T, P, C = 1, 8, 1, 256, 256, 64
+    qb, ka, va = make_case(B, Hq, Hkv, T, P, C, 255.0, seed=11)
+    ref = o.attention_anchor(qb, ka, va, B, T, Hq, Hkv, 128, P, C, 255.0, sm_scale=0.02)
+    q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).cuda()
+    out = lynx.attn_anchor(q, upload(ka), upload(va), T, Hkv, P, C, 255.0, sm_scale=0.02)
+    torch.cuda.synchronize()
+    assert rel_l2(out.cpu().numpy().astype(np.float64), ref) <= REL_L2
+
+
+def test_attention_full_size_sampled(gpu):
+    """16 sequences x 64 query heads / 8 kv heads x 32768 tokens, P=256, C=64, alpha=255, in
+    the launch configuration the benchmark times; the oracle checks three sequences."""
+    B, Hq, Hkv, T, P, C, alpha = 16, 64, 8, 32768, 256, 64, 255.0
+    print("[attn] full size: generating and encoding K/V on the GPU", flush=True)
+    kv = torch.empty((B * T, Hkv, 128), dtype=torch.bfloat16, device="cuda")
+    ka, va = [], []
+    for kv_idx in (0, 1):
+        for b in range(B):
+            synth.make_kv_torch(T, Hkv, 128, seed=0, layer=b, kv_idx=kv_idx, out=kv[b * T:(b + 1) * T])
+        anc, _ = lynx.encode(kv, P, C, alpha, residual=False)
+        (ka if kv_idx == 0 else va).append(anc)
+    ka, va = ka[0], va[0]
+    q = synth.make_q_torch(B, Hq, 128, seed=0)
+    out = lynx.attn_anchor(q, ka, va, T, Hkv, P, C, alpha, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    npg = T // P
+    qb = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    KA, VA = ka.cpu().numpy(), va.cpu().numpy()
+    got = out.cpu().numpy().astype(np.float64)
+    for b in (0, 7, 15):
+        print(f"[attn] oracle on sequence {b}", flush=True)
+        ref = o.attention_anchor(qb[b:b + 1], KA[b * npg:(b + 1) * npg], VA[b * npg:(b + 1) * npg], 1, T, Hq,
+                                 Hkv, 128, P, C, alpha)
+        e = rel_l2(got[b:b + 1], ref)
+        print(f"[attn] seq {b}: rel_l2={e:.3e} worst_head={worst_head(got[b:b + 1], ref):.3e}", flush=True)
+        assert e <= REL_L2
