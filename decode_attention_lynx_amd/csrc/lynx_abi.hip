@@ -30,7 +30,8 @@ int check_geometry(int n_pages, int P, int Hkv, int D, int C, float alpha, Geome
   if (!std::isfinite(alpha) || !(alpha > 0.0f)) return LYNX_EINVAL;
   if (D != kHeadDim) return LYNX_EUNSUPPORTED;
   if (!pow2_chunk(C)) return LYNX_EUNSUPPORTED;
-  if ((long long)n_pages * Hkv * (kHeadDim / kSlab) * ((P + kTileTokens - 1) / kTileTokens) > 0x7fffffffll)
+  if ((long long)n_pages * Hkv * ((P + kDecTile - 1) / kDecTile) > 0x7fffffffll ||
+      (long long)n_pages * Hkv * (kHeadDim / kSlab) > 0x7fffffffll)
     return LYNX_EUNSUPPORTED;
   g->n_pages = n_pages;
   g->P = P;
@@ -114,8 +115,17 @@ int lynx_encode(const void* kv_dev, int n_pages, int page_tokens, int kv_heads, 
   a.bnd[0] = 0.0;
   for (int j = 1; j <= kCodeMax; ++j) a.bnd[j] = std::expm1(((double)j - 0.5) * L / kCodeMax) / al;
   a.bnd[128] = INFINITY;
-  const dim3 grid((unsigned)(n_pages * kv_heads * (kHeadDim / kSlab)));   // (page, head, slab)
-  return launch(reinterpret_cast<const void*>(&k_encode), grid, &a, static_cast<hipStream_t>(hip_stream));
+  const dim3 grid((unsigned)((long long)n_pages * kv_heads * (kHeadDim / kSlab)));   // (page, head, slab)
+  const void* fn = nullptr;
+  switch (chunk) {
+    case 8: fn = reinterpret_cast<const void*>(&k_encode<8>); break;
+    case 16: fn = reinterpret_cast<const void*>(&k_encode<16>); break;
+    case 32: fn = reinterpret_cast<const void*>(&k_encode<32>); break;
+    case 64: fn = reinterpret_cast<const void*>(&k_encode<64>); break;
+    case 128: fn = reinterpret_cast<const void*>(&k_encode<128>); break;
+    default: fn = reinterpret_cast<const void*>(&k_encode<256>); break;
+  }
+  return launch(fn, grid, &a, static_cast<hipStream_t>(hip_stream));
 }
 
 static int decode_common(bool full, const void* anchor_dev, const void* residual_dev, int n_pages,
@@ -151,8 +161,8 @@ static int decode_common(bool full, const void* anchor_dev, const void* residual
       a.lut[nib] = (float)(S * alaw_mag(16 * vmag + 7, al));
     }
   }
-  const int ntiles = (page_tokens + kTileTokens - 1) / kTileTokens;
-  const dim3 grid((unsigned)(n_pages * kv_heads * (kHeadDim / kSlab) * ntiles));   // (page, head, slab, tile)
+  const int ntiles = (page_tokens + kDecTile - 1) / kDecTile;
+  const dim3 grid((unsigned)((long long)n_pages * kv_heads * ntiles));   // (page, head, 128-token tile)
   const void* fn;
   if (full) fn = out_dtype == LYNX_OUT_F32 ? reinterpret_cast<const void*>(&k_decode<true, true>)
                                            : reinterpret_cast<const void*>(&k_decode<true, false>);

@@ -35,10 +35,9 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int m) {
 // operations, in the same order, as the plain definition (Stage 1 division, then
 // the Stage 2 subtraction and division), and Round(Y) is decided by comparing
 // |X_f| with the exact boundaries bnd[j] (the |X_f| at which Y = j - 1/2), which is
-// Round(Eq. 7) without evaluating a logarithm.
-// Returns the byte I ^ (S < 0 ? 0xF7 : 0x07): high nibble = anchor, low = residual.
-__device__ __noinline__ uint32_t encode_exact(float x, float gmin, double D1, float mu, double D2,
-                                              const double* __restrict__ bnd) {
+// Round(Eq. 7) without evaluating a logarithm.  Returns (I, S) as floats.
+__device__ __noinline__ float2 encode_exact(float x, float gmin, double D1, float mu, double D2,
+                                            const double* __restrict__ bnd) {
   const double xn = ((double)x - (double)gmin) / D1;
   const double xfe = (xn - (double)mu) / D2;
   const double ax = fabs(xfe);
@@ -47,7 +46,7 @@ __device__ __noinline__ uint32_t encode_exact(float x, float gmin, double D1, fl
     const int mid = (lo + hi + 1) >> 1;
     if (ax >= bnd[mid]) lo = mid; else hi = mid - 1;
   }
-  return (uint32_t)lo ^ ((xfe < 0.0) ? 0xF7u : 0x07u);
+  return make_float2((float)lo, (xfe < 0.0) ? -1.0f : 1.0f);
 }
 
 // Pack 8 codes (one token, 8 consecutive channels) into one anchor word and one
@@ -78,16 +77,36 @@ __device__ __forceinline__ void pack8(const float* r, const float* xf, uint32_t*
   *res_w = (ee & 0x0F0F0F0Fu) | ((eo << 4) & 0xF0F0F0F0u);
 }
 
+// Statistics of every 8-token run of one channel, exchanged through LDS:
+// Stage 1 min / max, then per tile the chunk partials (float64 sum, min, max).
+template <int C>
+struct EncodeShared {
+  static constexpr int kChunksPerTile = kTileTokens / C;
+  double bnd[130];
+  float pmin[kTG][kSlab];
+  float pmax[kTG][kSlab];
+  double psum[kTG][kSlab];
+  float gmin[kSlab];
+  double D1[kSlab];
+  double r1[kSlab];
+  float4 cst[kChunksPerTile][kSlab];     // c_hi, k, -c_lo*k, mu (float32 fast path + stored mu)
+  double D2[kChunksPerTile][kSlab];
+};
+
+template <int C>
 __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
+  constexpr int G = C / kTokPerThread;               // token groups (threads) per chunk
+  constexpr int NCT = kTileTokens / C;               // chunks per tile
+  __shared__ EncodeShared<C> sh;
   const Geometry& g = a.g;
-  const int slab = blockIdx.x & 1;
-  const int ph = blockIdx.x >> 1;                  // page * Hkv + head
+  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  const int slab = unit & 1;
+  const int ph = unit >> 1;                        // page * Hkv + head
   const int page = ph / g.Hkv;
   const int h = ph - page * g.Hkv;
-  const int tid = threadIdx.x, dg = tid & (kDG - 1), tg = tid / kDG, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, dg = tid & (kDG - 1), tg = tid / kDG;
   const int H = g.H;
   const int ntiles = (g.P + kTileTokens - 1) / kTileTokens;
-  const int G = g.C / kTokPerThread;               // threads (token groups) per chunk
   const int cbase = h * kHeadDim + slab * kSlab;   // first channel of the slab
 
   const uint16_t* X = a.kv + (size_t)page * g.P * H + cbase + dg * 8;
@@ -97,24 +116,19 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
   uint8_t* anc_codes = anc + code_off;
   uint8_t* res_codes = a.residual ? a.residual + (size_t)page * g.res_seg + code_off : nullptr;
 
-  __shared__ double s_bnd[130];
-  __shared__ float s_rmin[4][kSlab], s_rmax[4][kSlab];
-  __shared__ double s_rsum[4][kSlab];
-  __shared__ float s_gmin[kSlab];
-  __shared__ double s_D1[kSlab], s_r1[kSlab];
-  __shared__ float s_mu[kTileTokens / 8][kSlab];
-  __shared__ double s_D2[kTileTokens / 8][kSlab];
-
-  for (int i = tid; i < 129; i += kThreads) s_bnd[i] = a.bnd[i];
+  for (int i = tid; i < 129; i += kThreads) sh.bnd[i] = a.bnd[i];
 
   uint4 v[kTokPerThread];
   auto load_tile = [&](int t0) {
     const int tok0 = t0 + tg * kTokPerThread;
     if (tok0 < g.P) {
 #pragma unroll
-      for (int i = 0; i < kTokPerThread; ++i)
-        v[i] = ld_stream(X + (size_t)(tok0 + i) * H);
+      for (int i = 0; i < kTokPerThread; ++i) v[i] = ld_stream(X + (size_t)(tok0 + i) * H);
     }
+  };
+  auto put8 = [](float* dst, const float* x) {
+    reinterpret_cast<float4*>(dst)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4*>(dst)[1] = make_float4(x[4], x[5], x[6], x[7]);
   };
 
   // ---- Stage 1: per-channel page min / max over all tokens ([Review] Stage 1)
@@ -139,37 +153,28 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
         }
       }
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-#pragma unroll
-      for (int m = 8; m < 64; m <<= 1) {
-        mn[j] = fminf(mn[j], __shfl_xor(mn[j], m));
-        mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], m));
-      }
-    }
-    if (lane < kDG) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) { s_rmin[wave][dg * 8 + j] = mn[j]; s_rmax[wave][dg * 8 + j] = mx[j]; }
-    }
+    put8(&sh.pmin[tg][dg * 8], mn);
+    put8(&sh.pmax[tg][dg * 8], mx);
   }
   __syncthreads();
   if (tid < kSlab) {
     const int c = tid;
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll 8
+    for (int r = 0; r < kTG; ++r) { lo = fminf(lo, sh.pmin[r][c]); hi = fmaxf(hi, sh.pmax[r][c]); }
     // + 0: a zero minimum / range is stored as +0 whatever the signs of the zeros
-    const float gmin = fminf(fminf(s_rmin[0][c], s_rmin[1][c]), fminf(s_rmin[2][c], s_rmin[3][c])) + 0.0f;
-    const float gmax = fmaxf(fmaxf(s_rmax[0][c], s_rmax[1][c]), fmaxf(s_rmax[2][c], s_rmax[3][c]));
-    const float gscale = (float)(((double)gmax - (double)gmin) + 0.0);   // exact difference, one rounding
+    const float gmin = lo + 0.0f;
+    const float gscale = (float)(((double)hi - (double)gmin) + 0.0);   // exact difference, one rounding
     const double D1 = (double)gscale + kEps;
-    s_gmin[c] = gmin;
-    s_D1[c] = D1;
-    s_r1[c] = 1.0 / D1;
+    sh.gmin[c] = gmin;
+    sh.D1[c] = D1;
+    sh.r1[c] = 1.0 / D1;
     meta[cbase + c] = gmin;
     meta[H + cbase + c] = gscale;
   }
   __syncthreads();
 
   const float alpha = a.alpha, ylog2k = a.ylog2k, zlim = 0.5f - a.ziv;
-  const double cC = (double)g.C, inv_c = 1.0 / (double)g.C;     // 1/C exact (C a power of two)
   float* meta_mu = meta + 2 * H + cbase;
   float* meta_sig = meta + 2 * H + (size_t)g.nck * H + cbase;
 
@@ -179,80 +184,58 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
     if (ntiles > 1) load_tile(t0);
     const int tok0 = t0 + tg * kTokPerThread;
     const bool act = tok0 < g.P;
-    const int kc = (tg * kTokPerThread) / g.C;         // chunk within tile
-    const int kglob = tok0 / g.C;                      // chunk within page
+    const int kc = tg / G;                             // chunk within tile
 
-    double sm[8];
-    float cmn[8], cmx[8];
+    {   // partials over this thread's 8 tokens
+      double sm[8];
+      float cmn[8], cmx[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { sm[j] = 0.0; cmn[j] = INFINITY; cmx[j] = -INFINITY; }
-    if (act) {
+      for (int j = 0; j < 8; ++j) { sm[j] = 0.0; cmn[j] = INFINITY; cmx[j] = -INFINITY; }
+      if (act) {
 #pragma unroll
-      for (int i = 0; i < kTokPerThread; ++i) {
-        const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        for (int i = 0; i < kTokPerThread; ++i) {
+          const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float lo = bf16_lo(q[k]), hi = bf16_hi(q[k]);
-          sm[2 * k] += (double)lo;
-          sm[2 * k + 1] += (double)hi;
-          cmn[2 * k] = fminf(cmn[2 * k], lo);
-          cmx[2 * k] = fmaxf(cmx[2 * k], lo);
-          cmn[2 * k + 1] = fminf(cmn[2 * k + 1], hi);
-          cmx[2 * k + 1] = fmaxf(cmx[2 * k + 1], hi);
+          for (int k = 0; k < 4; ++k) {
+            const float lo = bf16_lo(q[k]), hi = bf16_hi(q[k]);
+            sm[2 * k] += (double)lo;
+            sm[2 * k + 1] += (double)hi;
+            cmn[2 * k] = fminf(cmn[2 * k], lo);
+            cmx[2 * k] = fmaxf(cmx[2 * k], lo);
+            cmn[2 * k + 1] = fminf(cmn[2 * k + 1], hi);
+            cmx[2 * k + 1] = fmaxf(cmx[2 * k + 1], hi);
+          }
         }
       }
+      double2* ps = reinterpret_cast<double2*>(&sh.psum[tg][dg * 8]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ps[k] = make_double2(sm[2 * k], sm[2 * k + 1]);
+      put8(&sh.pmin[tg][dg * 8], cmn);
+      put8(&sh.pmax[tg][dg * 8], cmx);
     }
-    // reduce over the G token groups of the chunk: lanes ^8, ^16, ^32, then across waves
-#pragma unroll
-    for (int m = 8; m < 64; m <<= 1) {
-      if (G >= 2 * (m / 8)) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          sm[j] += shfl_xor_f64(sm[j], m);
-          cmn[j] = fminf(cmn[j], __shfl_xor(cmn[j], m));
-          cmx[j] = fmaxf(cmx[j], __shfl_xor(cmx[j], m));
-        }
-      }
-    }
-    if (G >= 16) {
-      if (lane < kDG) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          s_rsum[wave][dg * 8 + j] = sm[j];
-          s_rmin[wave][dg * 8 + j] = cmn[j];
-          s_rmax[wave][dg * 8 + j] = cmx[j];
-        }
-      }
-      __syncthreads();
-      const int wpc = G / 8;                       // waves per chunk (2 or 4)
-      const int w0 = (wave / wpc) * wpc;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        double s = 0.0;
-        float lo = INFINITY, hi = -INFINITY;
-        for (int w = w0; w < w0 + wpc; ++w) {
-          s += s_rsum[w][dg * 8 + j];
-          lo = fminf(lo, s_rmin[w][dg * 8 + j]);
-          hi = fmaxf(hi, s_rmax[w][dg * 8 + j]);
-        }
-        sm[j] = s; cmn[j] = lo; cmx[j] = hi;
-      }
-    }
+    __syncthreads();
 
-    // chunk metadata ([Review] Stage 2): mu = mean(X_n), sigma = max |X_n - mu|,
-    // both stored as float32 and used in their stored form from here on.  The
-    // mean comes from the float64 sum of the chunk's BF16 values; sigma from the
-    // chunk's extreme values (X_n is monotone in X).
-    float ch[8], ckn[8], kk[8];
+    // chunk metadata ([Review] Stage 2): mu = mean(X_n), sigma = max |X_n - mu|, both
+    // stored as float32 and used in their stored form from here on.  The mean comes
+    // from the float64 sum of the chunk's BF16 values; sigma from the chunk's extreme
+    // values (X_n is monotone in X).  One (chunk, channel) pair per thread and step.
+    const int nct_live = min(NCT, (g.P - t0) / C);
+    for (int p = tid; p < nct_live * kSlab; p += kThreads) {
+      const int ck = p / kSlab, c = p - ck * kSlab;
+      double s = 0.0;
+      float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = dg * 8 + j;
-      const double gmin = (double)s_gmin[c], D1 = s_D1[c], r1 = s_r1[c];
-      const double mean = (sm[j] - cC * gmin) * r1 * inv_c;
+      for (int r = 0; r < G; ++r) {
+        s += sh.psum[ck * G + r][c];
+        lo = fminf(lo, sh.pmin[ck * G + r][c]);
+        hi = fmaxf(hi, sh.pmax[ck * G + r][c]);
+      }
+      const double gmin = (double)sh.gmin[c], D1 = sh.D1[c], r1 = sh.r1[c];
+      const double mean = (s - (double)C * gmin) * r1 * (1.0 / C);     // 1/C exact (C a power of two)
       const float mu32 = (float)mean;
       const double mu = (double)mu32;
-      const double xnmax = ((double)cmx[j] - gmin) * r1;
-      const double xnmin = ((double)cmn[j] - gmin) * r1;
+      const double xnmax = ((double)hi - gmin) * r1;
+      const double xnmin = ((double)lo - gmin) * r1;
       const float sig32 = (float)fmax(fabs(xnmax - mu), fabs(mu - xnmin));
       const double D2 = (double)sig32 + kEps;
       // float32 fast path: X_f = (x - c) * k with the chunk centre c = gmin + mu*D1
@@ -261,76 +244,71 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
       const float c_hi = (float)cen;
       const float c_lo = (float)(cen - (double)c_hi);
       const float k = __builtin_amdgcn_rcpf((float)(D1 * D2));
-      ch[j] = c_hi;
-      kk[j] = k;
-      ckn[j] = 0.0f - c_lo * k;     // +0 when c_lo == 0, so X_f never comes out as -0
-      if (act && (tg % G) == 0) {
-        s_mu[kc][c] = mu32;
-        s_D2[kc][c] = D2;
-        meta_mu[(size_t)kglob * H + c] = mu32;
-        meta_sig[(size_t)kglob * H + c] = sig32;
-      }
+      sh.cst[ck][c] = make_float4(c_hi, k, 0.0f - c_lo * k, mu32);   // +0 when c_lo == 0: X_f is never -0
+      sh.D2[ck][c] = D2;
+      const int kglob = (t0 + ck * C) / C;
+      meta_mu[(size_t)kglob * H + c] = mu32;
+      meta_sig[(size_t)kglob * H + c] = sig32;
     }
     __syncthreads();
 
-    // ---- Stages 3-4 per element: float32 fast path for every element; the rare
-    // elements near a rounding boundary are re-decided in float64 afterwards and
-    // their nibbles patched in place (each thread only touches its own words).
+    // ---- Stages 3-4 per element: float32 fast path; the rare elements whose float32
+    // Y lies within `ziv` of a rounding boundary are re-decided in float64 before packing.
     if (act) {
-      uint32_t tokflags = 0;
+      float ch[8], kk[8], ckn[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float4 cs = sh.cst[kc][dg * 8 + j];
+        ch[j] = cs.x;
+        kk[j] = cs.y;
+        ckn[j] = cs.z;
+      }
 #pragma unroll
       for (int i = 0; i < kTokPerThread; ++i) {
         const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        float r[8], xf[8];
+        float r[8], xf[8], dy[8];
         float dmax = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
           const float f = fmaf(x - ch[j], kk[j], ckn[j]);
           const float tt = fmaf(alpha, fabsf(f), 1.0f);
-          const float Y = __builtin_amdgcn_logf(tt) * ylog2k;      // Eq. 7 in float32
-          const float rr = fminf(__builtin_rintf(Y), (float)kCodeMax);
-          dmax = fmaxf(dmax, fabsf(Y - rr));
+          const float Y = __builtin_amdgcn_logf(tt) * ylog2k;      // Eq. 7 in float32 (Y < 127.5)
+          const float rr = __builtin_rintf(Y);
+          dy[j] = fabsf(Y - rr);
+          dmax = fmaxf(dmax, dy[j]);
           r[j] = rr;
           xf[j] = f;
         }
-        tokflags |= (dmax > zlim) ? (1u << i) : 0u;
+        if (dmax > zlim) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if (dy[j] > zlim) {
+              const int c = dg * 8 + j;
+              const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
+              const float2 e = encode_exact(x, sh.gmin[c], sh.D1[c], sh.cst[kc][c].w, sh.D2[kc][c], sh.bnd);
+              r[j] = e.x;
+              xf[j] = e.y;
+            }
+          }
+        }
         uint32_t aw, rw;
         pack8(r, xf, &aw, &rw);
         const int tok = tok0 + i;
         *reinterpret_cast<uint32_t*>(anc_codes + (size_t)tok * (kHeadDim / 2)) = aw;
         if (res_codes) *reinterpret_cast<uint32_t*>(res_codes + (size_t)tok * (kHeadDim / 2)) = rw;
-        // keep each token's flag test here: left alone the compiler defers every
-        // test to the end of the loop and holds all Y values live
-        asm volatile("" : "+v"(tokflags)::"memory");
-      }
-      while (tokflags) {
-        const int i = __builtin_ctz(tokflags);
-        tokflags &= tokflags - 1;
-        const int tok = tok0 + i;
-        const uint4 w = *reinterpret_cast<const uint4*>(X + (size_t)tok * H);
-        const uint32_t q[4] = {w.x, w.y, w.z, w.w};
-        uint32_t* pa = reinterpret_cast<uint32_t*>(anc_codes + (size_t)tok * (kHeadDim / 2));
-        uint32_t* pr = res_codes ? reinterpret_cast<uint32_t*>(res_codes + (size_t)tok * (kHeadDim / 2)) : nullptr;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
-          const float f = fmaf(x - ch[j], kk[j], ckn[j]);
-          const float tt = fmaf(alpha, fabsf(f), 1.0f);
-          const float Y = __builtin_amdgcn_logf(tt) * ylog2k;
-          const float rr = fminf(__builtin_rintf(Y), (float)kCodeMax);
-          if (fabsf(Y - rr) > zlim) {
-            const int c = dg * 8 + j;
-            const uint32_t e = encode_exact(x, s_gmin[c], s_D1[c], s_mu[kc][c], s_D2[kc][c], s_bnd);
-            *pa = (*pa & ~(0xFu << (4 * j))) | ((e >> 4) << (4 * j));
-            if (pr) *pr = (*pr & ~(0xFu << (4 * j))) | ((e & 0xFu) << (4 * j));
-          }
-        }
       }
     }
     if (ntiles > 1) __syncthreads();   // the LDS partials and chunk tables are reused by the next tile
   }
 }
+
+template __global__ void k_encode<8>(EncodeArgs);
+template __global__ void k_encode<16>(EncodeArgs);
+template __global__ void k_encode<32>(EncodeArgs);
+template __global__ void k_encode<64>(EncodeArgs);
+template __global__ void k_encode<128>(EncodeArgs);
+template __global__ void k_encode<256>(EncodeArgs);
 
 // ---------------------------------------------------------------------------
 // Decode ([Review] Mechanism 2: Q_approx = dequant(Q_anc, gamma, mu, sigma) and
@@ -341,28 +319,29 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
 // ---------------------------------------------------------------------------
 template <bool FULL, bool F32OUT>
 __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
+  // one workgroup = one 128-token tile of one kv head of one page; thread t owns
+  // channels 8*(t % 16) .. +7 and tokens 8*(t / 16) .. +7 of the tile, so the 64-byte
+  // code row of a (head, token) is read whole by 16 neighbouring threads
   const Geometry& g = a.g;
-  const int ntiles = (g.P + kTileTokens - 1) / kTileTokens;
-  int bid = blockIdx.x;
-  const int tile = bid % ntiles;
-  bid /= ntiles;
-  const int slab = bid & 1;
-  const int ph = bid >> 1;
+  const int ntiles = (g.P + kDecTile - 1) / kDecTile;
+  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = unit % ntiles;
+  const int ph = unit / ntiles;
   const int page = ph / g.Hkv;
   const int h = ph - page * g.Hkv;
-  const int tid = threadIdx.x, dg = tid & (kDG - 1), tg = tid / kDG;
+  const int tid = threadIdx.x, dg = tid & (kDecDG - 1), tg = tid / kDecDG;
   const int H = g.H;
-  const int cbase = h * kHeadDim + slab * kSlab;
+  const int cbase = h * kHeadDim;
 
   __shared__ float s_lut[256];
   if (FULL) s_lut[tid] = a.lut[tid];
   else if (tid < 16) s_lut[tid] = a.lut[tid];
 
-  const int tok0 = tile * kTileTokens + tg * kTokPerThread;
+  const int tok0 = tile * kDecTile + tg * kTokPerThread;
   const bool act = tok0 < g.P;
   const uint8_t* anc = a.anchor + (size_t)page * g.anc_seg;
   const float* meta = reinterpret_cast<const float*>(anc + g.codes);
-  const size_t code_off = (size_t)h * g.P * (kHeadDim / 2) + slab * (kSlab / 2) + dg * 4;
+  const size_t code_off = (size_t)h * g.P * (kHeadDim / 2) + dg * 4;
   const uint8_t* anc_codes = anc + code_off;
   const uint8_t* res_codes = FULL ? a.residual + (size_t)page * g.res_seg + code_off : nullptr;
 
@@ -380,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     const float mu[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
     const float sg[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 8; ++j) {     // float64, then one rounding: B may cancel (gamma_min vs mu*D1)
       const double D1 = (double)gs[j] + kEps, D2 = (double)sg[j] + kEps;
       A[j] = (float)(D1 * D2);
       B[j] = (float)((double)gm[j] + (double)mu[j] * D1);
@@ -407,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[j] = fmaf(A[j], s_lut[(wa >> (4 * j)) & 0xF], B[j]);
     }
-    const size_t off = (size_t)(page * g.P + tok) * H + cbase + dg * 8;
+    const size_t off = ((size_t)page * g.P + tok) * H + cbase + dg * 8;
     if (F32OUT) {
       float* dst = static_cast<float*>(a.out) + off;
       st_stream(dst, make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])));

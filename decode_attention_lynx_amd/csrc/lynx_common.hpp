@@ -17,7 +17,10 @@ constexpr int kSlab = 64;            // channels of one kv head handled by one c
 constexpr int kDG = kSlab / 8;       // channel groups of 8 per slab (8)
 constexpr int kTG = kThreads / kDG;  // token groups per tile (32)
 constexpr int kTokPerThread = 8;     // consecutive tokens owned by one codec thread
-constexpr int kTileTokens = kTG * kTokPerThread;   // 256 tokens per codec tile
+constexpr int kTileTokens = kTG * kTokPerThread;   // 256 tokens per encode tile
+constexpr int kDecDG = kHeadDim / 8;                // decode: channel groups of 8 per kv head (16)
+constexpr int kDecTG = kThreads / kDecDG;           // decode: token groups per tile (16)
+constexpr int kDecTile = kDecTG * kTokPerThread;    // decode: 128 tokens per tile
 constexpr double kEps = 1e-6;        // epsilon of both normalisation stages (not given on the pages)
 constexpr int kCodeMax = 127;        // 2^7 - 1 ([Review] Mechanism 1, Stage 3, Eq. 7)
 
@@ -70,6 +73,15 @@ __device__ __forceinline__ uint4 ld_stream(const void* p) {
 __device__ __forceinline__ void st_stream(void* p, uint4 v) {
   const u32x4 w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, static_cast<u32x4*>(p));
+}
+
+// The hardware hands workgroup i to XCD (i mod 8), and each XCD has its own L2.
+// Renumber so that every XCD works through one contiguous range of logical units:
+// neighbouring units (which share cache lines of the code streams) meet in one L2.
+constexpr int kXCDs = 8;
+__device__ __forceinline__ int xcd_remap(int i, int n) {
+  const int q = n / kXCDs, r = n % kXCDs, x = i % kXCDs, k = i / kXCDs;
+  return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -8,6 +8,7 @@
 
 namespace lynx {
 
+template <int C>
 __global__ void k_encode(EncodeArgs a);
 template <bool FULL, bool F32OUT>
 __global__ void k_decode(DecodeArgs a);
