@@ -57,32 +57,12 @@ struct AttnArgs {
   int splits, tiles_per_split, ntiles;
   float qscale;        // sm_scale * log2(e): scores are kept in base 2
   int out_f32;
-  uint16_t lut[16];    // float16 bits of S|x| for each anchor nibble (I = 16*V_mag + 7)
+  uint32_t pair[256];  // float16 pair table: entry b = L[b & 15] | L[b >> 4] << 16 (L = S|x| of a nibble)
 };
 
 __device__ __forceinline__ float dpp_row_ror8(float v) {
   // rotate right by 8 lanes inside each row of 16: column n reads column n ^ 8
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
-}
-
-__device__ __forceinline__ _Float16 lut_at(const uint16_t* s_lut, uint32_t nib) {
-  return __builtin_bit_cast(_Float16, s_lut[nib]);
-}
-
-// 8 consecutive channels of one token (one dword of nibbles) -> MFMA A operand
-__device__ __forceinline__ h8 lookup_row(uint32_t w, const uint16_t* s_lut) {
-  h8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = lut_at(s_lut, (w >> (4 * e)) & 15u);
-  return r;
-}
-
-// nibble j of 8 dwords (8 tokens, same channel) -> MFMA A operand
-__device__ __forceinline__ h8 lookup_col(const uint32_t* w, int j, const uint16_t* s_lut) {
-  h8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = lut_at(s_lut, (w[e] >> (4 * j)) & 15u);
-  return r;
 }
 
 __device__ __forceinline__ float wave_max_g(float v) {   // over the 4 lane groups (l / 16)
@@ -94,6 +74,60 @@ __device__ __forceinline__ float wave_sum_g(float v) {
   return v + __shfl_xor(v, 32);
 }
 
+// the pair-table entry of byte k of w (two nibbles -> two float16 in one dword)
+__device__ __forceinline__ uint32_t pair_at(const uint32_t* s_pair, uint32_t w, int k) {
+  return s_pair[(w >> (8 * k)) & 0xFFu];
+}
+
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// 8 consecutive channels of one token (one dword of nibbles) -> MFMA operand
+__device__ __forceinline__ h8 lookup_row(uint32_t w, const uint32_t* s_pair) {
+  const u32x4v r = {pair_at(s_pair, w, 0), pair_at(s_pair, w, 1), pair_at(s_pair, w, 2), pair_at(s_pair, w, 3)};
+  return __builtin_bit_cast(h8, r);
+}
+
+// one wave's raw inputs for one 64-token tile
+struct TileIn {
+  uint4 kw[4];          // K code rows tin + 16mb + n, bytes 16g .. 16g+15
+  uint32_t vw[16];      // V code dword n of the 16 rows this lane feeds to the value MFMAs
+  float km[8], vm[8];   // gamma_min, gamma_scale, mu, sigma of channels lane and lane+64
+};
+
+__device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int tile, int lane, TileIn& t) {
+  const int n = lane & 15, g = lane >> 4;
+  const int tok = tile * kAttnTile;
+  const int page = tok / a.P;
+  const int tin = tok - page * a.P;
+  const int kc = tin / a.C;
+  const size_t seg = ((size_t)b * a.npages + page) * (size_t)a.anc_seg;
+  const uint8_t* kseg = a.kanc + seg;
+  const uint8_t* vseg = a.vanc + seg;
+  const size_t row0 = ((size_t)kvh * a.P + tin) * (kHeadDim / 2);
+  const uint8_t* kc_ptr = kseg + row0 + 16 * g;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) t.kw[mb] = *reinterpret_cast<const uint4*>(kc_ptr + (16 * mb + n) * (kHeadDim / 2));
+  const uint8_t* vc_ptr = vseg + row0 + 4 * n;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int row = 32 * ks + (r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4));
+      t.vw[8 * ks + r] = *reinterpret_cast<const uint32_t*>(vc_ptr + row * (kHeadDim / 2));
+    }
+  const float* kmeta = reinterpret_cast<const float*>(kseg + a.codes);
+  const float* vmeta = reinterpret_cast<const float*>(vseg + a.codes);
+  const size_t offs[4] = {0, (size_t)a.H, 2 * (size_t)a.H + (size_t)kc * a.H, 2 * (size_t)a.H + (size_t)(a.nck + kc) * a.H};
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int hlf = 0; hlf < 2; ++hlf) {
+      const size_t c = offs[f] + kvh * kHeadDim + lane + 64 * hlf;
+      t.km[2 * f + hlf] = kmeta[c];
+      t.vm[2 * f + hlf] = vmeta[c];
+    }
+}
+
 __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -101,28 +135,29 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
   const int hh = n & 7;                 // query head (within the group) of this column
   const bool lo_col = n >= 8;
 
-  __shared__ uint16_t s_lut[16];
+  __shared__ uint32_t s_pair[256];
+  __shared__ float4 s_kab[kAttnWaves][kHeadDim / 2];   // per wave: (A_K, B_K) of channels 2i, 2i+1
+  __shared__ float4 s_vab[kAttnWaves][kHeadDim / 2];   // per wave: (A_V, B_V) of channels 2i, 2i+1
   __shared__ float s_m[kAttnWaves][kMaxGroup], s_l[kAttnWaves][kMaxGroup];
   __shared__ float s_o[kAttnWaves][kMaxGroup][kHeadDim];
 
-  if (tid < 16) s_lut[tid] = a.lut[tid];
+  s_pair[tid] = a.pair[tid];
 
-  // this lane's query slice: head hh, channels d = 32g .. 32g+31, pre-scaled into base 2
-  float qs[32];
+  // this lane's query slice (head hh, channels 32g .. 32g+31), kept as BF16 pairs
+  uint32_t qw[16];
   {
     const bool live = hh < a.G;
     const uint16_t* qp = a.q + ((size_t)(b * a.Hq + kvh * a.G + (live ? hh : 0))) * kHeadDim + 32 * g;
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
       const uint4 w = *reinterpret_cast<const uint4*>(qp + 8 * v4);
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        qs[8 * v4 + 2 * k] = live ? bf16_lo(u[k]) * a.qscale : 0.0f;
-        qs[8 * v4 + 2 * k + 1] = live ? bf16_hi(u[k]) * a.qscale : 0.0f;
-      }
+      qw[4 * v4 + 0] = live ? w.x : 0u;
+      qw[4 * v4 + 1] = live ? w.y : 0u;
+      qw[4 * v4 + 2] = live ? w.z : 0u;
+      qw[4 * v4 + 3] = live ? w.w : 0u;
     }
   }
+  const float qscale = a.qscale;
   __syncthreads();
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -132,58 +167,57 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
 
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min(a.ntiles, t_begin + a.tiles_per_split);
-  const int cbase = kvh * kHeadDim + 32 * g;
+  float4* kab = s_kab[wave];
+  float4* vab = s_vab[wave];
 
-  for (int tile = t_begin + wave; tile < t_end; tile += kAttnWaves) {
-    const int tok = tile * kAttnTile;
-    const int page = tok / a.P;
-    const int tin = tok - page * a.P;
-    const int kc = tin / a.C;
-    const size_t seg = ((size_t)b * a.npages + page) * (size_t)a.anc_seg;
-    const uint8_t* kseg = a.kanc + seg;
-    const uint8_t* vseg = a.vanc + seg;
-    const float* kmeta = reinterpret_cast<const float*>(kseg + a.codes);
-    const float* vmeta = reinterpret_cast<const float*>(vseg + a.codes);
+  TileIn cur, nxt;
+  int tile = t_begin + wave;
+  if (tile < t_end) load_tile(a, b, kvh, tile, lane, cur);
+  for (; tile < t_end; tile += kAttnWaves) {
+    if (tile + kAttnWaves < t_end) load_tile(a, b, kvh, tile + kAttnWaves, lane, nxt);   // prefetch
 
-    // ---- codes: K rows (token tin + 16mb + n, 16 B at 16g), V dwords (column n of 8 rows per k-step)
-    const uint8_t* kc_ptr = kseg + (size_t)kvh * a.P * (kHeadDim / 2) + (size_t)tin * (kHeadDim / 2) + 16 * g;
-    uint4 kw[4];
+    // ---- the chunk's affine maps for channels lane, lane+64, shared through LDS:
+    //      A = (gamma_scale+eps)(sigma+eps), B = gamma_min + mu (gamma_scale+eps)
+    {
+      float ak[2], bk[2], av[2], bv[2];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) kw[mb] = *reinterpret_cast<const uint4*>(kc_ptr + (16 * mb + n) * (kHeadDim / 2));
-    const uint8_t* vc_ptr = vseg + (size_t)kvh * a.P * (kHeadDim / 2) + (size_t)tin * (kHeadDim / 2) + 4 * n;
-    uint32_t vw[2][8];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int row = 32 * ks + (r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4));
-        vw[ks][r] = *reinterpret_cast<const uint32_t*>(vc_ptr + row * (kHeadDim / 2));
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        const float d1k = cur.km[2 + hlf] + (float)kEps, d2k = cur.km[6 + hlf] + (float)kEps;
+        ak[hlf] = d1k * d2k;
+        bk[hlf] = fmaf(cur.km[4 + hlf], d1k, cur.km[hlf]);
+        const float d1v = cur.vm[2 + hlf] + (float)kEps, d2v = cur.vm[6 + hlf] + (float)kEps;
+        av[hlf] = d1v * d2v;
+        bv[hlf] = fmaf(cur.vm[4 + hlf], d1v, cur.vm[hlf]);
       }
+      // channel c = lane + 64*hlf -> pair slot c/2, component c%2
+      float* kf = reinterpret_cast<float*>(kab);
+      float* vf = reinterpret_cast<float*>(vab);
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        const int c = lane + 64 * hlf;
+        kf[4 * (c >> 1) + (c & 1)] = ak[hlf];
+        kf[4 * (c >> 1) + 2 + (c & 1)] = bk[hlf];
+        vf[4 * (c >> 1) + (c & 1)] = av[hlf];
+        vf[4 * (c >> 1) + 2 + (c & 1)] = bv[hlf];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
 
-    // ---- fold the key chunk's affine map into the query: qt = q*A_K (float16 hi / lo by column), beta = q.B_K
+    // ---- fold the key map into the query: qt = q*A_K (float16 hi / lo by column), beta = q.B_K
     h8 bq[4];
     float beta = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int c0 = cbase + 8 * kk;
-      const float4* pgm = reinterpret_cast<const float4*>(kmeta + c0);
-      const float4* pgs = reinterpret_cast<const float4*>(kmeta + a.H + c0);
-      const float4* pmu = reinterpret_cast<const float4*>(kmeta + 2 * a.H + (size_t)kc * a.H + c0);
-      const float4* psg = reinterpret_cast<const float4*>(kmeta + 2 * a.H + (size_t)(a.nck + kc) * a.H + c0);
-      const float4 gm0 = pgm[0], gm1 = pgm[1], gs0 = pgs[0], gs1 = pgs[1];
-      const float4 mu0 = pmu[0], mu1 = pmu[1], sg0 = psg[0], sg1 = psg[1];
-      const float gm[8] = {gm0.x, gm0.y, gm0.z, gm0.w, gm1.x, gm1.y, gm1.z, gm1.w};
-      const float gs[8] = {gs0.x, gs0.y, gs0.z, gs0.w, gs1.x, gs1.y, gs1.z, gs1.w};
-      const float mu[8] = {mu0.x, mu0.y, mu0.z, mu0.w, mu1.x, mu1.y, mu1.z, mu1.w};
-      const float sg[8] = {sg0.x, sg0.y, sg0.z, sg0.w, sg1.x, sg1.y, sg1.z, sg1.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float D1 = gs[e] + (float)kEps, D2 = sg[e] + (float)kEps;
-        const float x = qs[8 * kk + e];
-        const float qt = x * (D1 * D2);
-        beta = fmaf(x, fmaf(mu[e], D1, gm[e]), beta);
-        const _Float16 hi = (_Float16)qt;
-        bq[kk][e] = lo_col ? (_Float16)(qt - (float)hi) : hi;
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const float4 ab = kab[16 * g + 4 * kk + e2];       // channels 32g + 8kk + 2e2, +1
+        const uint32_t w = qw[4 * kk + e2];
+        const float x0 = bf16_lo(w) * qscale, x1 = bf16_hi(w) * qscale;
+        beta = fmaf(x0, ab.z, fmaf(x1, ab.w, beta));
+        const float q0 = x0 * ab.x, q1 = x1 * ab.y;
+        const _Float16 h0 = (_Float16)q0, h1 = (_Float16)q1;
+        bq[kk][2 * e2] = lo_col ? (_Float16)(q0 - (float)h0) : h0;
+        bq[kk][2 * e2 + 1] = lo_col ? (_Float16)(q1 - (float)h1) : h1;
       }
     }
     beta = wave_sum_g(beta);
@@ -193,10 +227,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-      const uint32_t w4[4] = {kw[mb].x, kw[mb].y, kw[mb].z, kw[mb].w};
+      const uint32_t w4[4] = {cur.kw[mb].x, cur.kw[mb].y, cur.kw[mb].z, cur.kw[mb].w};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lookup_row(w4[kk], s_lut), bq[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lookup_row(w4[kk], s_pair), bq[kk], acc, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[4 * mb + i] = acc[i] + dpp_row_ror8(acc[i]) + beta;
     }
@@ -207,12 +241,12 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
     for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
     mt = wave_max_g(mt);
     const float m_new = fmaxf(m_run, mt);
-    const float corr = exp2f(m_run - m_new);
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
     float lsum = 0.0f;
     h8 pt[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p = exp2f(s[i] - m_new);
+      const float p = __builtin_amdgcn_exp2f(s[i] - m_new);
       lsum += p;
       pt[i >> 3][i & 7] = (_Float16)p;
     }
@@ -224,36 +258,41 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
     m_run = m_new;
     const float lt = wave_sum_g(lsum);
 
-    // ---- values: T^T = L_V (128 x 64 tokens) * p (64 tokens x 16 columns), block j holds d = 8*row + j
+    // ---- values: T^T = L_V (128 x 64 tokens) * p (64 tokens x 16 columns), block j holds d = 8*row + j.
+    // Token pairs (2i, 2i+1) of a k-step are interleaved into pair-table indices per channel.
     f4 tacc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      tacc[j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) tacc[j] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        tacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lookup_col(vw[ks], j, s_lut), pt[ks], tacc[j], 0, 0, 0);
-    }
-
-    // ---- undo the value chunk's affine map: o += A_V * T + B_V * sum(p)
+    for (int ks = 0; ks < 2; ++ks) {
+      uint32_t ev[4], od[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c0 = cbase + 8 * i;      // d = 32g + 8i + j
-      const float4* pgm = reinterpret_cast<const float4*>(vmeta + c0);
-      const float4* pgs = reinterpret_cast<const float4*>(vmeta + a.H + c0);
-      const float4* pmu = reinterpret_cast<const float4*>(vmeta + 2 * a.H + (size_t)kc * a.H + c0);
-      const float4* psg = reinterpret_cast<const float4*>(vmeta + 2 * a.H + (size_t)(a.nck + kc) * a.H + c0);
-      const float4 gm0 = pgm[0], gm1 = pgm[1], gs0 = pgs[0], gs1 = pgs[1];
-      const float4 mu0 = pmu[0], mu1 = pmu[1], sg0 = psg[0], sg1 = psg[1];
-      const float gm[8] = {gm0.x, gm0.y, gm0.z, gm0.w, gm1.x, gm1.y, gm1.z, gm1.w};
-      const float gs[8] = {gs0.x, gs0.y, gs0.z, gs0.w, gs1.x, gs1.y, gs1.z, gs1.w};
-      const float mu[8] = {mu0.x, mu0.y, mu0.z, mu0.w, mu1.x, mu1.y, mu1.z, mu1.w};
-      const float sg[8] = {sg0.x, sg0.y, sg0.z, sg0.w, sg1.x, sg1.y, sg1.z, sg1.w};
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w0 = cur.vw[8 * ks + 2 * i], w1 = cur.vw[8 * ks + 2 * i + 1];
+        ev[i] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);   // byte k: channel 2k of tokens 2i, 2i+1
+        od[i] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);  // byte k: channel 2k+1
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float D1 = gs[j] + (float)kEps, D2 = sg[j] + (float)kEps;
-        o_acc[j][i] = fmaf(D1 * D2, tacc[j][i], fmaf(fmaf(mu[j], D1, gm[j]), lt, o_acc[j][i]));
+        const uint32_t* src = (j & 1) ? od : ev;
+        const u32x4v r = {pair_at(s_pair, src[0], j >> 1), pair_at(s_pair, src[1], j >> 1),
+                          pair_at(s_pair, src[2], j >> 1), pair_at(s_pair, src[3], j >> 1)};
+        tacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, r), pt[ks], tacc[j], 0, 0, 0);
       }
     }
+
+    // ---- undo the value map: o += A_V * T + B_V * sum(p), channel d = 32g + 8i + j
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j2 = 0; j2 < 4; ++j2) {
+        const float4 ab = vab[16 * g + 4 * i + j2];        // channels 32g + 8i + 2j2, +1
+        o_acc[2 * j2][i] = fmaf(ab.x, tacc[2 * j2][i], fmaf(ab.z, lt, o_acc[2 * j2][i]));
+        o_acc[2 * j2 + 1][i] = fmaf(ab.y, tacc[2 * j2 + 1][i], fmaf(ab.w, lt, o_acc[2 * j2 + 1][i]));
+      }
+    }
+    __builtin_amdgcn_wave_barrier();   // the next tile rewrites this wave's (A, B) tables
+    cur = nxt;
   }
 
   // ---- merge the 4 waves (columns 0..G-1 hold the result; 8..15 duplicate them)
@@ -274,7 +313,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
     float o = 0.0f, l = 0.0f;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
-      const float f = (s_m[w][h] == -INFINITY) ? 0.0f : exp2f(s_m[w][h] - M);
+      const float f = (s_m[w][h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
       o = fmaf(s_o[w][h][d], f, o);
       l = fmaf(s_l[w][h], f, l);
     }
@@ -292,9 +331,10 @@ __global__ __launch_bounds__(kHeadDim) void k_attn_combine(AttnArgs a) {
   float M = -INFINITY;
   for (int s = 0; s < a.splits; ++s) M = fmaxf(M, rec[(size_t)s * (kHeadDim + 2)]);
   float o = 0.0f, l = 0.0f;
+#pragma unroll 8
   for (int s = 0; s < a.splits; ++s) {
     const float* r = rec + (size_t)s * (kHeadDim + 2);
-    const float f = (r[0] == -INFINITY) ? 0.0f : exp2f(r[0] - M);
+    const float f = (r[0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(r[0] - M);
     o = fmaf(r[2 + d], f, o);
     l = fmaf(r[1], f, l);
   }
@@ -389,12 +429,14 @@ int attn_anchor_launch(const void* q_dev, const void* k_anchor_dev, const void* 
   a.qscale = (float)(scale * 1.4426950408889634);   // log2(e)
   a.out_f32 = out_dtype == LYNX_OUT_F32;
   const double al = (double)alpha, L = std::log1p(al);
+  uint16_t lut[16];
   for (int nib = 0; nib < 16; ++nib) {
     const int qv = nib >= 8 ? nib - 16 : nib;                 // Q_anc
     const int S = qv < 0 ? -1 : 1, vmag = qv < 0 ? -qv - 1 : qv;
     const double mag = std::expm1((double)(16 * vmag + 7) / kCodeMax * L) / al;
-    a.lut[nib] = f64_to_f16_bits(S * mag);
+    lut[nib] = f64_to_f16_bits(S * mag);
   }
+  for (int bt = 0; bt < 256; ++bt) a.pair[bt] = (uint32_t)lut[bt & 15] | ((uint32_t)lut[bt >> 4] << 16);
   void* kargs[] = {&a};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&k_attn_anchor),
                                  dim3((unsigned)pl.splits, (unsigned)kv_heads, (unsigned)batch),
