@@ -7,6 +7,7 @@
 //            LLM Inference" (technical review of arXiv 2607.01831).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -20,6 +21,10 @@ using namespace lynx;
 namespace {
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// decode workgroups in flight: 8 per compute unit of the 256-CU MI355X; each walks a
+// contiguous range of 128-token tiles
+constexpr long long kDecodeWorkgroups = 2048;
 
 bool pow2_chunk(int c) { return c == 8 || c == 16 || c == 32 || c == 64 || c == 128 || c == 256; }
 
@@ -162,7 +167,8 @@ static int decode_common(bool full, const void* anchor_dev, const void* residual
     }
   }
   const int ntiles = (page_tokens + kDecTile - 1) / kDecTile;
-  const dim3 grid((unsigned)((long long)n_pages * kv_heads * ntiles));   // (page, head, 128-token tile)
+  const long long n_units = (long long)n_pages * kv_heads * ntiles;    // (page, head, 128-token tile)
+  const dim3 grid((unsigned)std::min<long long>(n_units, kDecodeWorkgroups));
   const void* fn;
   if (full) fn = out_dtype == LYNX_OUT_F32 ? reinterpret_cast<const void*>(&k_decode<true, true>)
                                            : reinterpret_cast<const void*>(&k_decode<true, false>);

@@ -74,16 +74,21 @@ __device__ __forceinline__ float wave_sum_g(float v) {
   return v + __shfl_xor(v, 32);
 }
 
-// the pair-table entry of byte k of w (two nibbles -> two float16 in one dword)
-__device__ __forceinline__ uint32_t pair_at(const uint32_t* s_pair, uint32_t w, int k) {
-  return s_pair[(w >> (8 * k)) & 0xFFu];
+// The pair table (256 dwords) is held in 64 copies, entry e of copy r at byte
+// e*256 + 4r, and lane l reads copy l: no two lanes ever meet in a bank.  The byte
+// address (e << 8) | 4l is assembled by one v_perm from the code word (byte k = e)
+// and a register holding 4l in its low byte.
+__device__ __forceinline__ uint32_t pair_at(const uint32_t* s_pair, uint32_t lane4, uint32_t w, int k) {
+  const uint32_t addr = __builtin_amdgcn_perm(lane4, w, 0x0c0c0004u | ((uint32_t)k << 8));
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(s_pair) + addr);
 }
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 // 8 consecutive channels of one token (one dword of nibbles) -> MFMA operand
-__device__ __forceinline__ h8 lookup_row(uint32_t w, const uint32_t* s_pair) {
-  const u32x4v r = {pair_at(s_pair, w, 0), pair_at(s_pair, w, 1), pair_at(s_pair, w, 2), pair_at(s_pair, w, 3)};
+__device__ __forceinline__ h8 lookup_row(uint32_t w, const uint32_t* s_pair, uint32_t lane4) {
+  const u32x4v r = {pair_at(s_pair, lane4, w, 0), pair_at(s_pair, lane4, w, 1), pair_at(s_pair, lane4, w, 2),
+                    pair_at(s_pair, lane4, w, 3)};
   return __builtin_bit_cast(h8, r);
 }
 
@@ -135,13 +140,19 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
   const int hh = n & 7;                 // query head (within the group) of this column
   const bool lo_col = n >= 8;
 
-  __shared__ uint32_t s_pair[256];
-  __shared__ float4 s_kab[kAttnWaves][kHeadDim / 2];   // per wave: (A_K, B_K) of channels 2i, 2i+1
-  __shared__ float4 s_vab[kAttnWaves][kHeadDim / 2];   // per wave: (A_V, B_V) of channels 2i, 2i+1
-  __shared__ float s_m[kAttnWaves][kMaxGroup], s_l[kAttnWaves][kMaxGroup];
-  __shared__ float s_o[kAttnWaves][kMaxGroup][kHeadDim];
+  // LDS: the replicated pair table during the loop, reused for the wave merge after it
+  constexpr int kPairWords = 256 * 64;
+  constexpr int kMergeWords = kAttnWaves * kMaxGroup * (kHeadDim + 2);
+  __shared__ uint32_t s_big[kPairWords > kMergeWords ? kPairWords : kMergeWords];
+  // per wave: (A_K, B_K) and (A_V, B_V) of channels 2i, 2i+1 at slot swz(i), where
+  // swz(16g + t) = 4t + g puts the 4 lane groups' simultaneous reads in different banks
+  __shared__ float4 s_kab[kAttnWaves][kHeadDim / 2];
+  __shared__ float4 s_vab[kAttnWaves][kHeadDim / 2];
+  uint32_t* s_pair = s_big;
 
-  s_pair[tid] = a.pair[tid];
+#pragma unroll 8
+  for (int k = 0; k < 64; ++k) s_pair[k * 256 + tid] = a.pair[4 * k + (tid >> 6)];   // entry 4k + tid/64, copy tid%64
+  const uint32_t lane4 = 4u * (uint32_t)lane;
 
   // this lane's query slice (head hh, channels 32g .. 32g+31), kept as BF16 pairs
   uint32_t qw[16];
@@ -158,6 +169,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
     }
   }
   const float qscale = a.qscale;
+  const float lo_w = lo_col ? 1.0f : 0.0f;
   __syncthreads();
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -177,28 +189,29 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
     if (tile + kAttnWaves < t_end) load_tile(a, b, kvh, tile + kAttnWaves, lane, nxt);   // prefetch
 
     // ---- the chunk's affine maps for channels lane, lane+64, shared through LDS:
-    //      A = (gamma_scale+eps)(sigma+eps), B = gamma_min + mu (gamma_scale+eps)
+    //      A = (gamma_scale+eps)(sigma+eps), B = gamma_min + mu (gamma_scale+eps);
+    //      the key map carries the softmax scale (base 2)
     {
       float ak[2], bk[2], av[2], bv[2];
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
         const float d1k = cur.km[2 + hlf] + (float)kEps, d2k = cur.km[6 + hlf] + (float)kEps;
-        ak[hlf] = d1k * d2k;
-        bk[hlf] = fmaf(cur.km[4 + hlf], d1k, cur.km[hlf]);
+        ak[hlf] = d1k * d2k * qscale;
+        bk[hlf] = fmaf(cur.km[4 + hlf], d1k, cur.km[hlf]) * qscale;
         const float d1v = cur.vm[2 + hlf] + (float)kEps, d2v = cur.vm[6 + hlf] + (float)kEps;
         av[hlf] = d1v * d2v;
         bv[hlf] = fmaf(cur.vm[4 + hlf], d1v, cur.vm[hlf]);
       }
-      // channel c = lane + 64*hlf -> pair slot c/2, component c%2
+      // channel c = lane + 64*hlf -> pair slot i = c/2 at swz(i), component c%2
       float* kf = reinterpret_cast<float*>(kab);
       float* vf = reinterpret_cast<float*>(vab);
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
-        const int c = lane + 64 * hlf;
-        kf[4 * (c >> 1) + (c & 1)] = ak[hlf];
-        kf[4 * (c >> 1) + 2 + (c & 1)] = bk[hlf];
-        vf[4 * (c >> 1) + (c & 1)] = av[hlf];
-        vf[4 * (c >> 1) + 2 + (c & 1)] = bv[hlf];
+        const int c = lane + 64 * hlf, i = c >> 1, slot = 4 * (i & 15) + (i >> 4);
+        kf[4 * slot + (c & 1)] = ak[hlf];
+        kf[4 * slot + 2 + (c & 1)] = bk[hlf];
+        vf[4 * slot + (c & 1)] = av[hlf];
+        vf[4 * slot + 2 + (c & 1)] = bv[hlf];
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -208,31 +221,37 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
     float beta = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
+      uint32_t bw[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        const float4 ab = kab[16 * g + 4 * kk + e2];       // channels 32g + 8kk + 2e2, +1
+        const float4 ab = kab[4 * (4 * kk + e2) + g];      // channels 32g + 8kk + 2e2, +1
         const uint32_t w = qw[4 * kk + e2];
-        const float x0 = bf16_lo(w) * qscale, x1 = bf16_hi(w) * qscale;
+        const float x0 = bf16_lo(w), x1 = bf16_hi(w);
         beta = fmaf(x0, ab.z, fmaf(x1, ab.w, beta));
         const float q0 = x0 * ab.x, q1 = x1 * ab.y;
-        const _Float16 h0 = (_Float16)q0, h1 = (_Float16)q1;
-        bq[kk][2 * e2] = lo_col ? (_Float16)(q0 - (float)h0) : h0;
-        bq[kk][2 * e2 + 1] = lo_col ? (_Float16)(q1 - (float)h1) : h1;
+        // float16 split of the folded query: columns 0..7 take hi = rtz(q), columns
+        // 8..15 take rtz(q - hi); hi + lo carries ~22 bits of q
+        const auto hi = __builtin_amdgcn_cvt_pkrtz(q0, q1);
+        const float r0 = fmaf(-(float)hi[0], lo_w, q0), r1 = fmaf(-(float)hi[1], lo_w, q1);
+        bw[e2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
       }
+      const u32x4v bv4 = {bw[0], bw[1], bw[2], bw[3]};
+      bq[kk] = __builtin_bit_cast(h8, bv4);
     }
     beta = wave_sum_g(beta);
 
     // ---- scores: S^T = L_K (64 tokens x 128) * qt (128 x 16 columns)
     float s[16];
+    const float hb = 0.5f * beta;        // each of the two column halves carries half of beta
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+      f4 acc = f4{hb, hb, hb, hb};
       const uint32_t w4[4] = {cur.kw[mb].x, cur.kw[mb].y, cur.kw[mb].z, cur.kw[mb].w};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lookup_row(w4[kk], s_pair), bq[kk], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lookup_row(w4[kk], s_pair, lane4), bq[kk], acc, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[4 * mb + i] = acc[i] + dpp_row_ror8(acc[i]) + beta;
+      for (int i = 0; i < 4; ++i) s[4 * mb + i] = acc[i] + dpp_row_ror8(acc[i]);
     }
 
     // ---- online softmax (base 2) for head hh over this tile's 64 tokens
@@ -275,8 +294,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t* src = (j & 1) ? od : ev;
-        const u32x4v r = {pair_at(s_pair, src[0], j >> 1), pair_at(s_pair, src[1], j >> 1),
-                          pair_at(s_pair, src[2], j >> 1), pair_at(s_pair, src[3], j >> 1)};
+        const u32x4v r = {pair_at(s_pair, lane4, src[0], j >> 1), pair_at(s_pair, lane4, src[1], j >> 1),
+                          pair_at(s_pair, lane4, src[2], j >> 1), pair_at(s_pair, lane4, src[3], j >> 1)};
         tacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, r), pt[ks], tacc[j], 0, 0, 0);
       }
     }
@@ -286,7 +305,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int j2 = 0; j2 < 4; ++j2) {
-        const float4 ab = vab[16 * g + 4 * i + j2];        // channels 32g + 8i + 2j2, +1
+        const float4 ab = vab[4 * (4 * i + j2) + g];       // channels 32g + 8i + 2j2, +1
         o_acc[2 * j2][i] = fmaf(ab.x, tacc[2 * j2][i], fmaf(ab.z, lt, o_acc[2 * j2][i]));
         o_acc[2 * j2 + 1][i] = fmaf(ab.y, tacc[2 * j2 + 1][i], fmaf(ab.w, lt, o_acc[2 * j2 + 1][i]));
       }
@@ -297,6 +316,11 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
 
   // ---- merge the 4 waves (columns 0..G-1 hold the result; 8..15 duplicate them)
   l_run = wave_sum_g(l_run);
+  __syncthreads();                      // every wave is done with the pair table: reuse its LDS
+  float (*s_m)[kMaxGroup] = reinterpret_cast<float (*)[kMaxGroup]>(s_big);
+  float (*s_l)[kMaxGroup] = reinterpret_cast<float (*)[kMaxGroup]>(s_big + kAttnWaves * kMaxGroup);
+  float (*s_o)[kMaxGroup][kHeadDim] =
+      reinterpret_cast<float (*)[kMaxGroup][kHeadDim]>(s_big + 2 * kAttnWaves * kMaxGroup);
   if (g == 0 && n < kMaxGroup) { s_m[wave][n] = m_run; s_l[wave][n] = l_run; }
   if (n < kMaxGroup) {
 #pragma unroll
