@@ -32,7 +32,8 @@ LAYERS, TOKENS, KVH, D = 32, 16384, 8, 128
 P, C, ALPHA = 256, 64, 255.0
 AB, AHQ, AHKV, AT = 16, 64, 8, 32768
 KERNEL_SOURCES = ["decode_attention_lynx_amd/csrc/lynx_codec.hip", "decode_attention_lynx_amd/csrc/lynx_attn.hip",
-                  "decode_attention_lynx_amd/csrc/lynx_common.hpp", "decode_attention_lynx_amd/csrc/lynx_abi.hip"]
+                  "decode_attention_lynx_amd/csrc/lynx_common.hpp", "decode_attention_lynx_amd/csrc/lynx_abi.hip",
+                  "decode_attention_lynx_amd/csrc/hbm_probe.hip"]
 
 
 def alg_bytes_per_elem(op: str) -> float:
@@ -41,6 +42,93 @@ def alg_bytes_per_elem(op: str) -> float:
     meta = 8.0 / C + 8.0 / P
     return {"encode": 2.0 + 1.0 + meta, "decode_anchor": 0.5 + meta + 2.0, "decode_full": 1.0 + meta + 2.0,
             "attn_anchor": 0.5 + meta, "copy": 4.0}[op]
+
+
+def op_elems(op: str) -> int:
+    """KV elements one launch of an op processes (the copy counts 2-byte elements of 1 GiB)."""
+    return {"encode": LAYERS * 2 * TOKENS * KVH * D, "decode_anchor": LAYERS * 2 * TOKENS * KVH * D,
+            "decode_full": LAYERS * 2 * TOKENS * KVH * D, "attn_anchor": 2 * AB * AT * AHKV * D,
+            "copy": (1 << 30) // 2}[op]
+
+
+# kernels (name, grid size in threads) that make up one launch of each op
+OP_KERNELS = {
+    "encode": [("lynx::k_encode<%d>" % C, LAYERS * 2 * TOKENS // P * KVH * 2 * 256)],
+    "decode_anchor": [("lynx::k_decode<false, false>", None)],
+    "decode_full": [("lynx::k_decode<true, false>", None)],
+    "attn_anchor": [("lynx::k_attn_anchor", None), ("lynx::k_attn_combine", None)],
+    "copy": [("hbm_probe::k_probe_copy", None)],
+}
+
+
+def counter_summary(fetch_csv: str, write_csv: str, out_json: str) -> str:
+    """Per-op HBM bytes per launch from two rocprofv3 --pmc runs of this benchmark (FETCH_SIZE,
+    then WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for the 1 GiB
+    copy kernel.  Writes the per-op record read by load_traffic() and returns a text table."""
+    import csv
+    from collections import defaultdict
+
+    def read(path, counter):
+        acc = defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+                acc[(name, int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch, write = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
+
+    def per_op(table, op):
+        tot = 0.0
+        for name, grid in OP_KERNELS[op]:
+            hits = [v for (n, g), v in table.items() if n == name and (grid is None or g == grid)]
+            if len(hits) != 1:
+                raise RuntimeError(f"counter rows for {name} (grid {grid}): {len(hits)} kernel keys")
+            tot += hits[0]
+        return tot
+
+    gib = float(1 << 30)
+    f_fetch = gib / (per_op(fetch, "copy") * 1024.0)
+    f_write = gib / (per_op(write, "copy") * 1024.0)
+    res = {"calibration": {"fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4),
+                           "copy_bytes_each_way": int(gib)}}
+    lines = [f"calibration (1 GiB copy): FETCH_SIZE x {f_fetch:.4f}, WRITE_SIZE x {f_write:.4f}",
+             f"{'op':15s} {'FETCH KiB':>12s} {'WRITE KiB':>12s} {'HBM bytes':>14s} {'algorithmic':>14s} {'ratio':>7s}"]
+    for op in OP_KERNELS:
+        fk, wk = per_op(fetch, op), per_op(write, op)
+        hbm = fk * 1024.0 * f_fetch + wk * 1024.0 * f_write
+        alg = alg_bytes_per_elem(op) * op_elems(op)
+        res[op] = {"source_hash": kernel_hash(), "bytes_per_launch": int(round(hbm)), "fetch_KiB": round(fk, 1),
+                   "write_KiB": round(wk, 1), "alg_bytes_per_launch": int(alg), "ratio": round(hbm / alg, 4)}
+        lines.append(f"{op:15s} {fk:12.1f} {wk:12.1f} {hbm:14.0f} {alg:14.0f} {hbm / alg:7.4f}")
+    with open(out_json, "w") as f:
+        json.dump(res, f, indent=1)
+    return "\n".join(lines)
+
+
+def trace_summary(trace_csv: str) -> str:
+    """Per (kernel, grid) dispatch durations from a rocprofv3 --kernel-trace CSV of this benchmark."""
+    import csv
+    from collections import defaultdict
+
+    def dims(r, key):       # the trace gives X/Y/Z columns, the counter CSV a single total
+        if key in r:
+            return int(r[key])
+        return int(r[key + "_X"]) * int(r[key + "_Y"]) * int(r[key + "_Z"])
+    acc = defaultdict(list)
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+            if not name.startswith(("lynx::", "hbm_probe::")):
+                continue
+            key = (name, dims(r, "Grid_Size"), dims(r, "Workgroup_Size"))
+            acc[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"{'kernel':40s} {'grid':>10s} {'wg':>4s} {'calls':>5s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for (name, grid, wg), v in sorted(acc.items()):
+        lines.append(f"{name:40s} {grid:10d} {wg:4d} {len(v):5d} {sum(v) / len(v):9.1f} {min(v):9.1f} {max(v):9.1f}")
+    return "\n".join(lines)
 
 
 def kernel_hash() -> str:
@@ -64,6 +152,23 @@ def load_traffic(kernel: str):
     if not rec or rec.get("source_hash") != kernel_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def hbm_probe():
+    import ctypes
+    path = os.path.join(ROOT, "decode_attention_lynx_amd", "libhbmprobe.so")
+    L = ctypes.CDLL(path)
+    for f in ("hbm_probe_copy", "hbm_probe_read", "hbm_probe_write"):
+        getattr(L, f).restype = ctypes.c_int
+    L.hbm_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    L.hbm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    L.hbm_probe_write.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    return L
+
+
+def probe_call(status: int):
+    if status != 0:
+        raise RuntimeError(f"hbm probe failed with status {status}")
 
 
 def cpu_baseline(budget_s: float = 15.0):
@@ -116,7 +221,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ops", default="encode,decode_anchor,decode_full,attn_anchor")
+    ap.add_argument("--counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
+                    help="summarise two rocprofv3 --pmc runs of this benchmark into per-op HBM bytes")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="summarise a rocprofv3 --kernel-trace run of this benchmark per kernel and grid")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
+    if args.counter_summary:
+        print(counter_summary(*args.counter_summary))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Lynx hot path here is single-GPU (the codec and the "
               "attention shard by page / sequence with no exchange); run with --gpus 1", file=sys.stderr)
@@ -154,14 +269,17 @@ def main():
     o_att = torch.empty((AB, AHQ, D), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    copy_src = copy_dst = None
-    if "copy" in ops:       # plain 1 GiB device copy: calibrates the HBM byte counters
-        copy_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        copy_dst = torch.empty_like(copy_src)
+    # plain streaming kernels (libhbmprobe.so): what this HBM sustains, and a 1 GiB copy of
+    # known size against which the byte counters are calibrated
+    probe = hbm_probe()
+    copy_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    copy_dst = torch.empty_like(copy_src)
+    sink = torch.zeros(1 << 14, dtype=torch.uint8, device=dev)
 
     def run(op):
         if op == "copy":
-            copy_dst.copy_(copy_src)
+            probe_call(probe.hbm_probe_copy(copy_src.data_ptr(), copy_dst.data_ptr(), copy_src.numel(),
+                                            torch.cuda.current_stream().cuda_stream))
         elif op == "encode":
             lynx.encode(kv, P, C, ALPHA, anchor_out=anchor, residual_out=residual)
         elif op == "decode_anchor":
@@ -171,8 +289,7 @@ def main():
         elif op == "attn_anchor":
             lynx.attn_anchor(q, att[0], att[1], AT, AHKV, P, C, ALPHA, workspace=ws, out=o_att)
 
-    elems = {"encode": T_all * KVH * D, "decode_anchor": T_all * KVH * D, "decode_full": T_all * KVH * D,
-             "attn_anchor": 2 * AB * AT * AHKV * D, "copy": (1 << 30) // 2}
+    elems = {op: op_elems(op) for op in ops}
     for _ in range(args.warmup):
         for op in ops:
             run(op)
@@ -190,6 +307,24 @@ def main():
         print(f"[bench] step {s + 1}/{args.steps} enqueued", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # measured HBM ceilings (not part of the timed step)
+    def probe_gbs(fn, nbytes):
+        for _ in range(2):
+            fn()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        for _ in range(5):
+            fn()
+        b_.record(stream)
+        torch.cuda.synchronize()
+        return round(nbytes * 5 / (a_.elapsed_time(b_) * 1e6), 1)
+    sptr = lambda: torch.cuda.current_stream().cuda_stream
+    nb = copy_src.numel()
+    hbm = {"read_GBs": probe_gbs(lambda: probe_call(probe.hbm_probe_read(copy_src.data_ptr(), nb, sink.data_ptr(), sptr())), nb),
+           "write_GBs": probe_gbs(lambda: probe_call(probe.hbm_probe_write(copy_dst.data_ptr(), nb, sptr())), nb),
+           "copy_GBs": probe_gbs(lambda: probe_call(probe.hbm_probe_copy(copy_src.data_ptr(), copy_dst.data_ptr(), nb,
+                                                                       sptr())), 2 * nb)}
     ms = {op: sum(a.elapsed_time(b) for a, b in ev[op]) / args.steps for op in ops}
     step_ms = wall * 1e3 / args.steps
     per_op = {}
@@ -211,7 +346,7 @@ def main():
         "config": {"workload": "llama3-8b request codec (32 layers x K,V x 16384 tok x 8 kvh x 128 BF16, P=256, "
                                "C=64, alpha=255: encode + decode_anchor + decode_full) + anchor-only decode "
                                "attention (16 seq x 64 q / 8 kv heads x 128, 32768-token context)",
-                   "ops": per_op, "hbm_peak_GBs": HBM_PEAK_GBS,
+                   "ops": per_op, "hbm_peak_GBs": HBM_PEAK_GBS, "hbm_measured": hbm,
                    "arith": "float32 codec (float64 statistics and boundary cases), float16 MFMA attention "
                             "with float32 accumulation"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

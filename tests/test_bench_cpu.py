@@ -1,0 +1,76 @@
+"""Host logic of bench.py: the rocprofv3 counter and trace summaries (CPU only)."""
+import csv
+import json
+
+import bench
+
+
+def write_rows(path, rows, fields):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def kernel_rows(counter, per_kernel):
+    rows = []
+    for (name, grid), vals in per_kernel.items():
+        for v in vals:
+            rows.append({"Kernel_Name": name, "Grid_Size": grid, "Counter_Name": counter, "Counter_Value": v})
+    return rows
+
+
+def test_counter_summary_calibrates_against_the_copy(tmp_path):
+    enc_grid = bench.OP_KERNELS["encode"][0][1]
+    gib_kib = (1 << 30) / 1024
+    fetch = {("hbm_probe::k_probe_copy(unsigned int const*)", 2097152): [gib_kib / 2] * 3,
+             (f"void lynx::k_encode<{bench.C}>(lynx::EncodeArgs)", enc_grid): [1000.0, 1002.0],
+             (f"void lynx::k_encode<{bench.C}>(lynx::EncodeArgs)", enc_grid // 2): [7.0],   # setup encode, ignored
+             ("void lynx::k_decode<false, false>(lynx::DecodeArgs)", 524288): [10.0],
+             ("void lynx::k_decode<true, false>(lynx::DecodeArgs)", 524288): [20.0],
+             ("lynx::k_attn_anchor(lynx::AttnArgs)", 4096): [30.0],
+             ("lynx::k_attn_combine(lynx::AttnArgs)", 131072): [1.0]}
+    write = {k: [v[0] * 2 for _ in v] for k, v in fetch.items()}
+    fields = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    fp, wp, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "t.json"
+    write_rows(fp, kernel_rows("FETCH_SIZE", fetch), fields)
+    write_rows(wp, kernel_rows("WRITE_SIZE", write), fields)
+    text = bench.counter_summary(str(fp), str(wp), str(out))
+    rec = json.loads(out.read_text())
+    assert abs(rec["calibration"]["fetch_factor"] - 2.0) < 1e-9
+    assert abs(rec["calibration"]["write_factor"] - 1.0) < 1e-9
+    assert rec["encode"]["bytes_per_launch"] == round(1001.0 * 1024 * 2 + 2000.0 * 1024 * 1)
+    assert rec["attn_anchor"]["bytes_per_launch"] == round(31.0 * 1024 * 2 + 62.0 * 1024)
+    assert rec["copy"]["bytes_per_launch"] == 2 << 30
+    assert rec["encode"]["source_hash"] == bench.kernel_hash()
+    assert "encode" in text and "calibration" in text
+
+
+def test_trace_summary_groups_by_kernel_and_grid(tmp_path):
+    xyz = {"Grid_Size_X": 4096, "Grid_Size_Y": 128, "Grid_Size_Z": 1,
+           "Workgroup_Size_X": 256, "Workgroup_Size_Y": 1, "Workgroup_Size_Z": 1}
+    rows = [dict(Kernel_Name="void lynx::k_decode<true, false>(lynx::DecodeArgs)", Start_Timestamp=1000,
+                 End_Timestamp=1000 + d, **xyz) for d in (600000, 700000)]
+    rows.append(dict(Kernel_Name="at::native::foo(int)", Start_Timestamp=0, End_Timestamp=5, **xyz))
+    p = tmp_path / "k.csv"
+    write_rows(p, rows, ["Kernel_Name", "Start_Timestamp", "End_Timestamp"] + list(xyz))
+    text = bench.trace_summary(str(p))
+    assert "at::native" not in text
+    line = [ln for ln in text.splitlines() if "k_decode" in ln][0].split()
+    assert line[-6:-4] == ["524288", "256"]
+    assert line[-4:] == ["2", "650.0", "600.0", "700.0"]
+
+
+def test_load_traffic_rejects_a_stale_source_hash(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "traffic.json").write_text(json.dumps({"encode": {"source_hash": "stale", "bytes_per_launch": 5},
+                                                   "decode_full": {"source_hash": bench.kernel_hash(),
+                                                                   "bytes_per_launch": 7}}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_hash", lambda: json.loads((prof / "traffic.json").read_text())
+                        ["decode_full"]["source_hash"])
+    assert bench.load_traffic("encode") is None
+    assert bench.load_traffic("decode_full") == 7
+    assert bench.load_traffic("attn_anchor") is None
