@@ -117,10 +117,11 @@ int lynx_encode(const void* kv_dev, int n_pages, int page_tokens, int kv_heads, 
   // evaluation's error stays below 4e-5 (bound derived in the design notes and
   // measured on the device); 1e-4 leaves a margin of 2.5x.
   a.ziv = 1e-4f;
+  a.zlim = 0.5f - a.ziv;
   a.bnd[0] = 0.0;
   for (int j = 1; j <= kCodeMax; ++j) a.bnd[j] = std::expm1(((double)j - 0.5) * L / kCodeMax) / al;
   a.bnd[128] = INFINITY;
-  const dim3 grid((unsigned)((long long)n_pages * kv_heads * (kHeadDim / kSlab)));   // (page, head, slab)
+  const long long n_units = (long long)n_pages * kv_heads * (kHeadDim / kSlab);   // (page, head, slab)
   const void* fn = nullptr;
   switch (chunk) {
     case 8: fn = reinterpret_cast<const void*>(&k_encode<8>); break;
@@ -130,6 +131,7 @@ int lynx_encode(const void* kv_dev, int n_pages, int page_tokens, int kv_heads, 
     case 128: fn = reinterpret_cast<const void*>(&k_encode<128>); break;
     default: fn = reinterpret_cast<const void*>(&k_encode<256>); break;
   }
+  const dim3 grid((unsigned)n_units);
   return launch(fn, grid, &a, static_cast<hipStream_t>(hip_stream));
 }
 

@@ -30,23 +30,20 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int m) {
 // Encode ([Review] Mechanism 1, Algorithm 1)
 // ---------------------------------------------------------------------------
 
-// One element's float64 decision, taken where the float32 estimate lies within
-// `ziv` of a rounding boundary of Y.  X_f is formed with the same float64
-// operations, in the same order, as the plain definition (Stage 1 division, then
-// the Stage 2 subtraction and division), and Round(Y) is decided by comparing
-// |X_f| with the exact boundaries bnd[j] (the |X_f| at which Y = j - 1/2), which is
-// Round(Eq. 7) without evaluating a logarithm.  Returns (I, S) as floats.
-__device__ __noinline__ float2 encode_exact(float x, float gmin, double D1, float mu, double D2,
+// One element's float64 decision, taken where the float32 estimate of Y lies within
+// `ziv` of the rounding boundary between codes jb - 1 and jb.  The float32 error is far
+// below the distance to any other boundary, so Round(Y) is one of those two codes:
+// I = jb iff |X_f| >= bnd[jb], the |X_f| at which Y = jb - 1/2 (Round of Eq. 7 without
+// a logarithm).  X_f = (x - c)/(D1*D2) with the chunk centre c = gamma_min + mu*D1 is
+// the Stage 1 and Stage 2 normalisation in one float64 step; its error (a few units of
+// 2^-53 relative to the chunk's spread) only matters within ~1e-14 of the boundary.
+// Returns (I, S) as floats.
+__device__ __forceinline__ float2 encode_exact(float x, float gmin, double D1, float mu, double D2, int jb,
                                             const double* __restrict__ bnd) {
-  const double xn = ((double)x - (double)gmin) / D1;
-  const double xfe = (xn - (double)mu) / D2;
-  const double ax = fabs(xfe);
-  int lo = 0, hi = kCodeMax;                  // largest I with bnd[I] <= ax (bnd[0] = 0)
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (ax >= bnd[mid]) lo = mid; else hi = mid - 1;
-  }
-  return make_float2((float)lo, (xfe < 0.0) ? -1.0f : 1.0f);
+  const double cen = (double)gmin + (double)mu * D1;
+  const double xfe = ((double)x - cen) / (D1 * D2);
+  const int I = fabs(xfe) >= bnd[jb] ? jb : jb - 1;
+  return make_float2((float)I, (xfe < 0.0) ? -1.0f : 1.0f);
 }
 
 // Pack 8 codes (one token, 8 consecutive channels) into one anchor word and one
@@ -79,104 +76,267 @@ __device__ __forceinline__ void pack8(const float* r, const float* xf, uint32_t*
 
 // Statistics of every 8-token run of one channel, exchanged through LDS:
 // Stage 1 min / max, then per tile the chunk partials (float64 sum, min, max).
-// Channel c = 8*dg + j of the slab lives at LDS column j*8 + dg, and rows are
-// padded to 72 columns: the 32 lanes of a half-wave that store one j then hit
-// 32 different banks (8*(token group) + dg), and the column walk of the
-// reducing threads is unit-stride.
-constexpr int kRow = kSlab + 8;
+// Channel c = 8*dg + j of the slab lives at LDS column j*8 + dg of its row, and
+// row r stores column col at col ^ 8*(r % 4): the 32 lanes of a half-wave that
+// store one j (4 token groups x 8 channel groups) then hit 32 different banks,
+// and the column walk of the reducing threads stays a permutation of one row.
+// Rows are not padded, so the tables of a 64-token chunk fit four workgroups
+// in the 160 KB of LDS of a compute unit.
 __device__ __forceinline__ int lds_col(int c) { return (c & 7) * 8 + (c >> 3); }   // channel -> column
 __device__ __forceinline__ int lds_chan(int col) { return (col & 7) * 8 + (col >> 3); }  // column -> channel
+__device__ __forceinline__ int lds_swz(int row, int col) { return col ^ ((row & 3) << 3); }
 
 template <int C>
 struct EncodeShared {
   static constexpr int kChunksPerTile = kTileTokens / C;
   double bnd[130];
-  float pmin[kTG][kRow];
-  float pmax[kTG][kRow];
-  double psum[kTG][kRow];
+  float pmin[kTG][kSlab];
+  float pmax[kTG][kSlab];
+  double psum[kTG][kSlab];
   float gmin[kSlab];                     // by column
   double D1[kSlab];
-  double r1[kSlab];
   float4 cst[kChunksPerTile][kSlab];     // by column: c_hi, k, -c_lo*k, mu (float32 fast path + stored mu)
-  double D2[kChunksPerTile][kSlab];
+  float sig[kChunksPerTile][kSlab];      // stored sigma, by column
 };
 
-template <int C>
-__global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
-  constexpr int G = C / kTokPerThread;               // token groups (threads) per chunk
-  constexpr int NCT = kTileTokens / C;               // chunks per tile
-  __shared__ EncodeShared<C> sh;
+// Addresses of one encode unit: a 64-channel slab of one kv head of one page.
+struct EncodeUnit {
+  const uint16_t* X;      // this thread's first BF16 value (token 0, channel cbase + 8*dg)
+  float* meta;            // the page's float32 metadata
+  uint8_t* anc_codes;     // this thread's anchor word of token 0
+  uint8_t* res_codes;     // this thread's residual word of token 0, or nullptr
+  int cbase;              // first channel of the slab
+};
+
+__device__ __forceinline__ EncodeUnit encode_unit(const EncodeArgs& a, int unit, int dg) {
   const Geometry& g = a.g;
-  const int unit = xcd_remap(blockIdx.x, gridDim.x);
   const int slab = unit & 1;
   const int ph = unit >> 1;                        // page * Hkv + head
   const int page = ph / g.Hkv;
   const int h = ph - page * g.Hkv;
-  const int tid = threadIdx.x, dg = tid & (kDG - 1), tg = tid / kDG;
-  const int H = g.H;
-  const int ntiles = (g.P + kTileTokens - 1) / kTileTokens;
-  const int cbase = h * kHeadDim + slab * kSlab;   // first channel of the slab
-
-  const uint16_t* X = a.kv + (size_t)page * g.P * H + cbase + dg * 8;
+  EncodeUnit u;
+  u.cbase = h * kHeadDim + slab * kSlab;
+  u.X = a.kv + (size_t)page * g.P * g.H + u.cbase + dg * 8;
   uint8_t* anc = a.anchor + (size_t)page * g.anc_seg;
-  float* meta = reinterpret_cast<float*>(anc + g.codes);
+  u.meta = reinterpret_cast<float*>(anc + g.codes);
   const size_t code_off = (size_t)h * g.P * (kHeadDim / 2) + slab * (kSlab / 2) + dg * 4;
-  uint8_t* anc_codes = anc + code_off;
-  uint8_t* res_codes = a.residual ? a.residual + (size_t)page * g.res_seg + code_off : nullptr;
+  u.anc_codes = anc + code_off;
+  u.res_codes = a.residual ? a.residual + (size_t)page * g.res_seg + code_off : nullptr;
+  return u;
+}
+
+// This thread's 8 tokens x 8 channels of the tile starting at token t0 (nothing past P).
+__device__ __forceinline__ void load_tile(uint4 (&v)[kTokPerThread], const uint16_t* X, int t0, int tg,
+                                          const Geometry& g) {
+  const int tok0 = t0 + tg * kTokPerThread;
+  if (tok0 < g.P) {
+#pragma unroll
+    for (int i = 0; i < kTokPerThread; ++i) v[i] = ld_stream(X + (size_t)(tok0 + i) * g.H);
+  }
+}
+
+// The same BF16 -> float unpacking as bf16_lo / bf16_hi, written as a byte permutation.
+// Passes that unpack the same words a second time use this form, so the compiler
+// recomputes the floats there instead of keeping the first pass's copies live.
+__device__ __forceinline__ float bf16_lo_p(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x01000c0cu)); }
+__device__ __forceinline__ float bf16_hi_p(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x03020c0cu)); }
+
+// Per-thread statistics of its 8 tokens x 8 channels, stored to the LDS partial rows:
+// float64 sum, min, max (Stage 2 needs all three; Stage 1 needs min and max).
+template <int C>
+__device__ __forceinline__ void store_partials(EncodeShared<C>& sh, const uint4 (&v)[kTokPerThread], bool act,
+                                               int tg, int dg) {
+  double sm[8];
+  float cmn[8], cmx[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { sm[j] = 0.0; cmn[j] = INFINITY; cmx[j] = -INFINITY; }
+  if (act) {
+#pragma unroll
+    for (int i = 0; i < kTokPerThread; ++i) {
+      const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lo = bf16_lo_p(q[k]), hi = bf16_hi_p(q[k]);
+        sm[2 * k] += (double)lo;
+        sm[2 * k + 1] += (double)hi;
+        cmn[2 * k] = fminf(cmn[2 * k], lo);
+        cmx[2 * k] = fmaxf(cmx[2 * k], lo);
+        cmn[2 * k + 1] = fminf(cmn[2 * k + 1], hi);
+        cmx[2 * k + 1] = fmaxf(cmx[2 * k + 1], hi);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int col = lds_swz(tg, j * 8 + dg);
+    sh.psum[tg][col] = sm[j];
+    sh.pmin[tg][col] = cmn[j];
+    sh.pmax[tg][col] = cmx[j];
+  }
+}
+
+// Stage 1 ([Review] Mechanism 1, Stage 1): per-channel page min / max from the LDS
+// partial rows (threads tid < 64, one LDS column each); gamma_min and gamma_scale are
+// stored as float32, D1 = gamma_scale + eps is kept in float64.
+template <int C>
+__device__ __forceinline__ void page_stats(EncodeShared<C>& sh, float* meta, int cbase, int H, int tid) {
+  if (tid < kSlab) {
+    const int col = tid, c = lds_chan(col);
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll 8
+    for (int r = 0; r < kTG; ++r) {
+      lo = fminf(lo, sh.pmin[r][lds_swz(r, col)]);
+      hi = fmaxf(hi, sh.pmax[r][lds_swz(r, col)]);
+    }
+    // + 0: a zero minimum / range is stored as +0 whatever the signs of the zeros
+    const float gmin = lo + 0.0f;
+    const float gscale = (float)(((double)hi - (double)gmin) + 0.0);   // exact difference, one rounding
+    const double D1 = (double)gscale + kEps;
+    sh.gmin[col] = gmin;
+    sh.D1[col] = D1;
+    meta[cbase + c] = gmin;
+    meta[H + cbase + c] = gscale;
+  }
+}
+
+// Stage 2 chunk metadata ([Review] Mechanism 1, Stage 2) of the chunks in the tile at t0:
+// mu = mean(X_n), sigma = max |X_n - mu|, both stored as float32 and used in their stored
+// form from here on.  The mean comes from the float64 sum of the chunk's BF16 values;
+// sigma from the chunk's extreme values (X_n is monotone in X).  One (chunk, channel)
+// pair per thread and step.
+template <int C>
+__device__ __forceinline__ void chunk_stats(EncodeShared<C>& sh, float* meta, int cbase, int t0, int tid,
+                                            const Geometry& g) {
+  constexpr int G = C / kTokPerThread;               // token groups (threads) per chunk
+  constexpr int NCT = kTileTokens / C;               // chunks per tile
+  float* meta_mu = meta + 2 * g.H + cbase;
+  float* meta_sig = meta + 2 * g.H + (size_t)g.nck * g.H + cbase;
+  const int nct_live = min(NCT, (g.P - t0) / C);
+  for (int p = tid; p < nct_live * kSlab; p += kThreads) {
+    const int ck = p / kSlab, col = p - ck * kSlab, c = lds_chan(col);
+    double s = 0.0;
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      const int row = ck * G + r, pc = lds_swz(row, col);
+      s += sh.psum[row][pc];
+      lo = fminf(lo, sh.pmin[row][pc]);
+      hi = fmaxf(hi, sh.pmax[row][pc]);
+    }
+    const double gmin = (double)sh.gmin[col], D1 = sh.D1[col], r1 = 1.0 / D1;
+    const double mean = (s - (double)C * gmin) * r1 * (1.0 / C);     // 1/C exact (C a power of two)
+    const float mu32 = (float)mean;
+    const double mu = (double)mu32;
+    const double xnmax = ((double)hi - gmin) * r1;
+    const double xnmin = ((double)lo - gmin) * r1;
+    const float sig32 = (float)fmax(fabs(xnmax - mu), fabs(mu - xnmin));
+    const double D2 = (double)sig32 + kEps;
+    // float32 fast path: X_f = (x - c) * k with the chunk centre c = gmin + mu*D1
+    // held as c_hi + c_lo, and k = 1/(D1*D2)
+    const double cen = gmin + mu * D1;
+    const float c_hi = (float)cen;
+    const float c_lo = (float)(cen - (double)c_hi);
+    const float k = __builtin_amdgcn_rcpf((float)(D1 * D2));
+    sh.cst[ck][col] = make_float4(c_hi, k, 0.0f - c_lo * k, mu32);   // +0 when c_lo == 0: X_f is never -0
+    sh.sig[ck][col] = sig32;
+    const int kglob = (t0 + ck * C) / C;
+    meta_mu[(size_t)kglob * g.H + c] = mu32;
+    meta_sig[(size_t)kglob * g.H + c] = sig32;
+  }
+}
+
+// Stages 3-4 ([Review] Mechanism 1, Stages 3-4, Eq. 7 and Eq. 9) for this thread's 8
+// tokens of the tile at t0.  Every element takes the float32 fast path; the rare
+// elements whose float32 Y lies within `ziv` of a rounding boundary are then re-decided
+// in float64 and their two nibbles patched into the packed words, one element at a time
+// (few registers stay live there, which leaves room for four workgroups per CU).
+template <int C>
+__device__ __forceinline__ void encode_tokens(const EncodeShared<C>& sh, const EncodeArgs& a, const EncodeUnit& u,
+                                              const uint4 (&v)[kTokPerThread], int t0, int tg, int dg) {
+  constexpr int G = C / kTokPerThread;
+  const int tok0 = t0 + tg * kTokPerThread;
+  if (tok0 >= a.g.P) return;
+  const int kc = tg / G;                             // chunk within tile
+  const float alpha = a.alpha, ylog2k = a.ylog2k, zlim = a.zlim;
+  // this thread's columns j*8 + dg of the chunk tables: one base each, j an offset
+  const float4* cst_t = &sh.cst[kc][dg];
+  const float* sig_t = &sh.sig[kc][dg];
+  const float* gmin_t = &sh.gmin[dg];
+  const double* D1_t = &sh.D1[dg];
+  float ch[8], kk[8], ckn[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float4 cs = cst_t[j * 8];
+    ch[j] = cs.x;
+    kk[j] = cs.y;
+    ckn[j] = cs.z;
+  }
+  uint32_t* anc_w = reinterpret_cast<uint32_t*>(u.anc_codes + (size_t)tok0 * (kHeadDim / 2));
+  uint32_t* res_w = u.res_codes ? reinterpret_cast<uint32_t*>(u.res_codes + (size_t)tok0 * (kHeadDim / 2)) : nullptr;
+#pragma unroll
+  for (int i = 0; i < kTokPerThread; ++i) {
+    const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    float r[8], xf[8];
+    uint32_t near = 0;                               // bit j: element j lies in the band
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
+      const float f = fmaf(x - ch[j], kk[j], ckn[j]);
+      const float tt = fmaf(alpha, fabsf(f), 1.0f);
+      const float Y = __builtin_amdgcn_logf(tt) * ylog2k;      // Eq. 7 in float32 (Y < 127.5)
+      const float rr = __builtin_rintf(Y);
+      near |= (fabsf(Y - rr) > zlim ? 1u : 0u) << j;
+      r[j] = rr;
+      xf[j] = f;
+    }
+    uint32_t aw, rw;
+    pack8(r, xf, &aw, &rw);
+    while (near) {
+      const int j = __builtin_ctz(near);
+      near &= near - 1;
+      const uint32_t w = (j >> 1) == 0 ? q[0] : (j >> 1) == 1 ? q[1] : (j >> 1) == 2 ? q[2] : q[3];
+      const float x = (j & 1) ? bf16_hi_p(w) : bf16_lo_p(w);
+      const float4 cs = cst_t[j * 8];
+      // the fast path's Y again (same operations), to find the boundary it lies near
+      const float Y = __builtin_amdgcn_logf(fmaf(alpha, fabsf(fmaf(x - cs.x, cs.y, cs.z)), 1.0f)) * ylog2k;
+      const float rr = __builtin_rintf(Y);
+      const int jb = (int)rr + (Y > rr ? 1 : 0);                      // in [1, 128]
+      const float2 e = encode_exact(x, gmin_t[j * 8], D1_t[j * 8], cs.w, (double)sig_t[j * 8] + kEps, jb, sh.bnd);
+      const uint32_t byte = (uint32_t)e.x ^ (e.y < 0.0f ? 0xF7u : 0x07u);   // anchor nibble high, residual low
+      const uint32_t m = 0xFu << (4 * j);
+      aw = (aw & ~m) | ((byte >> 4) << (4 * j));
+      rw = (rw & ~m) | ((byte & 0xFu) << (4 * j));
+    }
+    anc_w[i * (kHeadDim / 8)] = aw;                  // one 64-byte code row per token
+    if (res_w) res_w[i * (kHeadDim / 8)] = rw;
+  }
+}
+
+// General encoder: one workgroup per unit, pages of any length.  Pages longer than
+// one 256-token tile take Stage 1 in a first pass over the page and Stages 2-4 tile
+// by tile in a second.
+template <int C>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C >= 64 ? 4 : 2))) void k_encode(EncodeArgs a) {
+  __shared__ EncodeShared<C> sh;
+  const Geometry& g = a.g;
+  const int tid = threadIdx.x, dg = tid & (kDG - 1), tg = tid / kDG;
+  const EncodeUnit u = encode_unit(a, xcd_remap(blockIdx.x, gridDim.x), dg);
+  const int ntiles = (g.P + kTileTokens - 1) / kTileTokens;
 
   for (int i = tid; i < 129; i += kThreads) sh.bnd[i] = a.bnd[i];
 
   uint4 v[kTokPerThread];
-  auto load_tile = [&](int t0) {
-    const int tok0 = t0 + tg * kTokPerThread;
-    if (tok0 < g.P) {
-#pragma unroll
-      for (int i = 0; i < kTokPerThread; ++i) v[i] = ld_stream(X + (size_t)(tok0 + i) * H);
-    }
-  };
-
-  // Per-thread statistics of its 8 tokens x 8 channels, stored to the LDS partial rows:
-  // float64 sum, min, max (Stage 2 needs all three; Stage 1 needs min and max).
-  auto partials = [&](int t0) {
-    double sm[8];
-    float cmn[8], cmx[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) { sm[j] = 0.0; cmn[j] = INFINITY; cmx[j] = -INFINITY; }
-    if (t0 + tg * kTokPerThread < g.P) {
-#pragma unroll
-      for (int i = 0; i < kTokPerThread; ++i) {
-        const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float lo = bf16_lo(q[k]), hi = bf16_hi(q[k]);
-          sm[2 * k] += (double)lo;
-          sm[2 * k + 1] += (double)hi;
-          cmn[2 * k] = fminf(cmn[2 * k], lo);
-          cmx[2 * k] = fmaxf(cmx[2 * k], lo);
-          cmn[2 * k + 1] = fminf(cmn[2 * k + 1], hi);
-          cmx[2 * k + 1] = fmaxf(cmx[2 * k + 1], hi);
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      sh.psum[tg][j * 8 + dg] = sm[j];
-      sh.pmin[tg][j * 8 + dg] = cmn[j];
-      sh.pmax[tg][j * 8 + dg] = cmx[j];
-    }
-  };
-
-  // ---- Stage 1: per-channel page min / max over all tokens ([Review] Stage 1).  A page
-  // of one tile takes them from the same partials Stage 2 uses; longer pages make a pass.
+  // ---- Stage 1: per-channel page min / max over all tokens.  A page of one tile takes
+  // them from the same partials Stage 2 uses; longer pages make a pass.
   if (ntiles == 1) {
-    load_tile(0);
-    partials(0);
+    load_tile(v, u.X, 0, tg, g);
+    store_partials(sh, v, tg * kTokPerThread < g.P, tg, dg);
   } else {
     float mn[8], mx[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) { mn[j] = INFINITY; mx[j] = -INFINITY; }
     for (int t = 0; t < ntiles; ++t) {
-      load_tile(t * kTileTokens);
+      load_tile(v, u.X, t * kTileTokens, tg, g);
       if (t * kTileTokens + tg * kTokPerThread < g.P) {
 #pragma unroll
         for (int i = 0; i < kTokPerThread; ++i) {
@@ -193,126 +353,26 @@ __global__ __launch_bounds__(kThreads) void k_encode(EncodeArgs a) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { sh.pmin[tg][j * 8 + dg] = mn[j]; sh.pmax[tg][j * 8 + dg] = mx[j]; }
+    for (int j = 0; j < 8; ++j) {
+      sh.pmin[tg][lds_swz(tg, j * 8 + dg)] = mn[j];
+      sh.pmax[tg][lds_swz(tg, j * 8 + dg)] = mx[j];
+    }
   }
   __syncthreads();
-  if (tid < kSlab) {
-    const int col = tid, c = lds_chan(col);
-    float lo = INFINITY, hi = -INFINITY;
-#pragma unroll 8
-    for (int r = 0; r < kTG; ++r) { lo = fminf(lo, sh.pmin[r][col]); hi = fmaxf(hi, sh.pmax[r][col]); }
-    // + 0: a zero minimum / range is stored as +0 whatever the signs of the zeros
-    const float gmin = lo + 0.0f;
-    const float gscale = (float)(((double)hi - (double)gmin) + 0.0);   // exact difference, one rounding
-    const double D1 = (double)gscale + kEps;
-    sh.gmin[col] = gmin;
-    sh.D1[col] = D1;
-    sh.r1[col] = 1.0 / D1;
-    meta[cbase + c] = gmin;
-    meta[H + cbase + c] = gscale;
-  }
+  page_stats(sh, u.meta, u.cbase, g.H, tid);
   __syncthreads();
-
-  const float alpha = a.alpha, ylog2k = a.ylog2k, zlim = 0.5f - a.ziv;
-  float* meta_mu = meta + 2 * H + cbase;
-  float* meta_sig = meta + 2 * H + (size_t)g.nck * H + cbase;
 
   // ---- per tile: Stage 2 chunk statistics, then Stages 3-4 per element
   for (int t = 0; t < ntiles; ++t) {
     const int t0 = t * kTileTokens;
-    const int tok0 = t0 + tg * kTokPerThread;
-    const bool act = tok0 < g.P;
-    const int kc = tg / G;                             // chunk within tile
     if (ntiles > 1) {
-      load_tile(t0);
-      partials(t0);
+      load_tile(v, u.X, t0, tg, g);
+      store_partials(sh, v, t0 + tg * kTokPerThread < g.P, tg, dg);
       __syncthreads();
     }
-
-    // chunk metadata ([Review] Stage 2): mu = mean(X_n), sigma = max |X_n - mu|, both
-    // stored as float32 and used in their stored form from here on.  The mean comes
-    // from the float64 sum of the chunk's BF16 values; sigma from the chunk's extreme
-    // values (X_n is monotone in X).  One (chunk, channel) pair per thread and step.
-    const int nct_live = min(NCT, (g.P - t0) / C);
-    for (int p = tid; p < nct_live * kSlab; p += kThreads) {
-      const int ck = p / kSlab, col = p - ck * kSlab, c = lds_chan(col);
-      double s = 0.0;
-      float lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < G; ++r) {
-        s += sh.psum[ck * G + r][col];
-        lo = fminf(lo, sh.pmin[ck * G + r][col]);
-        hi = fmaxf(hi, sh.pmax[ck * G + r][col]);
-      }
-      const double gmin = (double)sh.gmin[col], D1 = sh.D1[col], r1 = sh.r1[col];
-      const double mean = (s - (double)C * gmin) * r1 * (1.0 / C);     // 1/C exact (C a power of two)
-      const float mu32 = (float)mean;
-      const double mu = (double)mu32;
-      const double xnmax = ((double)hi - gmin) * r1;
-      const double xnmin = ((double)lo - gmin) * r1;
-      const float sig32 = (float)fmax(fabs(xnmax - mu), fabs(mu - xnmin));
-      const double D2 = (double)sig32 + kEps;
-      // float32 fast path: X_f = (x - c) * k with the chunk centre c = gmin + mu*D1
-      // held as c_hi + c_lo, and k = 1/(D1*D2)
-      const double cen = gmin + mu * D1;
-      const float c_hi = (float)cen;
-      const float c_lo = (float)(cen - (double)c_hi);
-      const float k = __builtin_amdgcn_rcpf((float)(D1 * D2));
-      sh.cst[ck][col] = make_float4(c_hi, k, 0.0f - c_lo * k, mu32);   // +0 when c_lo == 0: X_f is never -0
-      sh.D2[ck][col] = D2;
-      const int kglob = (t0 + ck * C) / C;
-      meta_mu[(size_t)kglob * H + c] = mu32;
-      meta_sig[(size_t)kglob * H + c] = sig32;
-    }
+    chunk_stats(sh, u.meta, u.cbase, t0, tid, g);
     __syncthreads();
-
-    // ---- Stages 3-4 per element: float32 fast path; the rare elements whose float32
-    // Y lies within `ziv` of a rounding boundary are re-decided in float64 before packing.
-    if (act) {
-      float ch[8], kk[8], ckn[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float4 cs = sh.cst[kc][j * 8 + dg];
-        ch[j] = cs.x;
-        kk[j] = cs.y;
-        ckn[j] = cs.z;
-      }
-#pragma unroll
-      for (int i = 0; i < kTokPerThread; ++i) {
-        const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        float r[8], xf[8], dy[8];
-        float dmax = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
-          const float f = fmaf(x - ch[j], kk[j], ckn[j]);
-          const float tt = fmaf(alpha, fabsf(f), 1.0f);
-          const float Y = __builtin_amdgcn_logf(tt) * ylog2k;      // Eq. 7 in float32 (Y < 127.5)
-          const float rr = __builtin_rintf(Y);
-          dy[j] = fabsf(Y - rr);
-          dmax = fmaxf(dmax, dy[j]);
-          r[j] = rr;
-          xf[j] = f;
-        }
-        if (dmax > zlim) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            if (dy[j] > zlim) {
-              const int col = j * 8 + dg;
-              const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
-              const float2 e = encode_exact(x, sh.gmin[col], sh.D1[col], sh.cst[kc][col].w, sh.D2[kc][col], sh.bnd);
-              r[j] = e.x;
-              xf[j] = e.y;
-            }
-          }
-        }
-        uint32_t aw, rw;
-        pack8(r, xf, &aw, &rw);
-        const int tok = tok0 + i;
-        *reinterpret_cast<uint32_t*>(anc_codes + (size_t)tok * (kHeadDim / 2)) = aw;
-        if (res_codes) *reinterpret_cast<uint32_t*>(res_codes + (size_t)tok * (kHeadDim / 2)) = rw;
-      }
-    }
+    encode_tokens(sh, a, u, v, t0, tg, dg);
     if (ntiles > 1) __syncthreads();   // the LDS partials and chunk tables are reused by the next tile
   }
 }
