@@ -248,8 +248,8 @@ __device__ __forceinline__ void chunk_stats(EncodeShared<C>& sh, float* meta, in
 // Stages 3-4 ([Review] Mechanism 1, Stages 3-4, Eq. 7 and Eq. 9) for this thread's 8
 // tokens of the tile at t0.  Every element takes the float32 fast path; the rare
 // elements whose float32 Y lies within `ziv` of a rounding boundary are then re-decided
-// in float64 and their two nibbles patched into the packed words, one element at a time
-// (few registers stay live there, which leaves room for four workgroups per CU).
+// in float64 and their two nibbles patched into the packed words (the fast path's
+// per-element values are dead by then, which leaves room for four workgroups per CU).
 template <int C>
 __device__ __forceinline__ void encode_tokens(const EncodeShared<C>& sh, const EncodeArgs& a, const EncodeUnit& u,
                                               const uint4 (&v)[kTokPerThread], int t0, int tg, int dg) {
@@ -277,7 +277,7 @@ __device__ __forceinline__ void encode_tokens(const EncodeShared<C>& sh, const E
   for (int i = 0; i < kTokPerThread; ++i) {
     const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
     float r[8], xf[8];
-    uint32_t near = 0;                               // bit j: element j lies in the band
+    bool near[8];                                    // element j lies in the band (a lane mask each)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
@@ -285,27 +285,35 @@ __device__ __forceinline__ void encode_tokens(const EncodeShared<C>& sh, const E
       const float tt = fmaf(alpha, fabsf(f), 1.0f);
       const float Y = __builtin_amdgcn_logf(tt) * ylog2k;      // Eq. 7 in float32 (Y < 127.5)
       const float rr = __builtin_rintf(Y);
-      near |= (fabsf(Y - rr) > zlim ? 1u : 0u) << j;
+      near[j] = fabsf(Y - rr) > zlim;
       r[j] = rr;
       xf[j] = f;
     }
     uint32_t aw, rw;
     pack8(r, xf, &aw, &rw);
-    while (near) {
-      const int j = __builtin_ctz(near);
-      near &= near - 1;
-      const uint32_t w = (j >> 1) == 0 ? q[0] : (j >> 1) == 1 ? q[1] : (j >> 1) == 2 ? q[2] : q[3];
-      const float x = (j & 1) ? bf16_hi_p(w) : bf16_lo_p(w);
-      const float4 cs = cst_t[j * 8];
-      // the fast path's Y again (same operations), to find the boundary it lies near
-      const float Y = __builtin_amdgcn_logf(fmaf(alpha, fabsf(fmaf(x - cs.x, cs.y, cs.z)), 1.0f)) * ylog2k;
-      const float rr = __builtin_rintf(Y);
-      const int jb = (int)rr + (Y > rr ? 1 : 0);                      // in [1, 128]
-      const float2 e = encode_exact(x, gmin_t[j * 8], D1_t[j * 8], cs.w, (double)sig_t[j * 8] + kEps, jb, sh.bnd);
-      const uint32_t byte = (uint32_t)e.x ^ (e.y < 0.0f ? 0xF7u : 0x07u);   // anchor nibble high, residual low
-      const uint32_t m = 0xFu << (4 * j);
-      aw = (aw & ~m) | ((byte >> 4) << (4 * j));
-      rw = (rw & ~m) | ((byte & 0xFu) << (4 * j));
+    if (near[0] | near[1] | near[2] | near[3] | near[4] | near[5] | near[6] | near[7]) {
+      // the per-lane bit mask is formed here, on this rare path only: `one` comes out of an
+      // opaque step, so the compiler cannot move the mask's eight selects onto the fast path
+      uint32_t one = 1u, bits = 0;
+      asm volatile("" : "+v"(one));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bits |= (near[j] ? one : 0u) << j;
+      do {                                           // one element at a time, lowest first
+        const int j = __builtin_ctz(bits);
+        bits &= bits - 1;
+        const uint32_t w = (j >> 1) == 0 ? q[0] : (j >> 1) == 1 ? q[1] : (j >> 1) == 2 ? q[2] : q[3];
+        const float x = (j & 1) ? bf16_hi_p(w) : bf16_lo_p(w);
+        const float4 cs = cst_t[j * 8];
+        // the fast path's Y again (same operations), to find the boundary it lies near
+        const float Y = __builtin_amdgcn_logf(fmaf(alpha, fabsf(fmaf(x - cs.x, cs.y, cs.z)), 1.0f)) * ylog2k;
+        const float rr = __builtin_rintf(Y);
+        const int jb = (int)rr + (Y > rr ? 1 : 0);                        // in [1, 128]
+        const float2 e = encode_exact(x, gmin_t[j * 8], D1_t[j * 8], cs.w, (double)sig_t[j * 8] + kEps, jb, sh.bnd);
+        const uint32_t byte = (uint32_t)e.x ^ (e.y < 0.0f ? 0xF7u : 0x07u);   // anchor nibble high, residual low
+        const uint32_t m = 0xFu << (4 * j);
+        aw = (aw & ~m) | ((byte >> 4) << (4 * j));
+        rw = (rw & ~m) | ((byte & 0xFu) << (4 * j));
+      } while (bits);
     }
     anc_w[i * (kHeadDim / 8)] = aw;                  // one 64-byte code row per token
     if (res_w) res_w[i * (kHeadDim / 8)] = rw;
