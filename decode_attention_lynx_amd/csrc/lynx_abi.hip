@@ -113,11 +113,10 @@ int lynx_encode(const void* kv_dev, int n_pages, int page_tokens, int kv_heads, 
   const double al = (double)alpha, L = std::log1p(al);
   a.ylog2k = (float)((double)kCodeMax / std::log2(1.0 + al));
   // Band half-width around a rounding boundary of Y inside which the float32
-  // estimate is not trusted and the element is decided in float64.  The float32
-  // evaluation's error stays below 4e-5 (bound derived in the design notes and
-  // measured on the device); 1e-4 leaves a margin of 2.5x.
-  a.ziv = 1e-4f;
-  a.zlim = 0.5f - a.ziv;
+  // estimate is not trusted and the element is decided in float64: 7 units of 2^-16
+  // (1.07e-4).  The float32 evaluation's error stays below 3.1e-5 (bound derived in
+  // the design notes), so the margin is 3.4x.
+  a.zband = 7;
   a.bnd[0] = 0.0;
   for (int j = 1; j <= kCodeMax; ++j) a.bnd[j] = std::expm1(((double)j - 0.5) * L / kCodeMax) / al;
   a.bnd[128] = INFINITY;

@@ -31,7 +31,7 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int m) {
 // ---------------------------------------------------------------------------
 
 // One element's float64 decision, taken where the float32 estimate of Y lies within
-// `ziv` of the rounding boundary between codes jb - 1 and jb.  The float32 error is far
+// the band around the rounding boundary between codes jb - 1 and jb.  The float32 error is far
 // below the distance to any other boundary, so Round(Y) is one of those two codes:
 // I = jb iff |X_f| >= bnd[jb], the |X_f| at which Y = jb - 1/2 (Round of Eq. 7 without
 // a logarithm).  X_f = (x - c)/(D1*D2) with the chunk centre c = gamma_min + mu*D1 is
@@ -48,30 +48,25 @@ __device__ __forceinline__ float2 encode_exact(float x, float gmin, double D1, f
 
 // Pack 8 codes (one token, 8 consecutive channels) into one anchor word and one
 // residual word ([Review] Mechanism 1, Stage 4 and Eq. 9, with the +7 bias at
-// reconstruction; Implementation Notes: even element in the low nibble).
+// reconstruction; Implementation Notes: even element in the low nibble).  Code I of
+// element j is byte 2 of mb[j] (see encode_tokens); its sign is that of xf[j].
 //   anchor nibble   = V_mag ^ (S < 0 ? 0xF : 0)  == (V_mag*S + min(S,0)) & 0xF
 //   residual nibble = (I & 15) ^ 7               == (16*V_mag + 7 - I) & 0xF
-// Bytes are formed as I ^ (S < 0 ? 0xF7 : 0x07): high nibble = anchor, low = residual.
-__device__ __forceinline__ void pack8(const float* r, const float* xf, uint32_t* anc_w, uint32_t* res_w) {
-  uint32_t be = 0, bo = 0;
-  be = __builtin_amdgcn_cvt_pk_u8_f32(r[0], 0, be);
-  be = __builtin_amdgcn_cvt_pk_u8_f32(r[2], 1, be);
-  be = __builtin_amdgcn_cvt_pk_u8_f32(r[4], 2, be);
-  be = __builtin_amdgcn_cvt_pk_u8_f32(r[6], 3, be);
-  bo = __builtin_amdgcn_cvt_pk_u8_f32(r[1], 0, bo);
-  bo = __builtin_amdgcn_cvt_pk_u8_f32(r[3], 1, bo);
-  bo = __builtin_amdgcn_cvt_pk_u8_f32(r[5], 2, bo);
-  bo = __builtin_amdgcn_cvt_pk_u8_f32(r[7], 3, bo);
+// Bytes are formed as I ^ (S < 0 ? 0xF0 : 0): high nibble = anchor, low = I & 15; the
+// residual's ^7 is applied to the whole word at the end.
+__device__ __forceinline__ void pack8(const uint32_t* mb, const float* xf, uint32_t* anc_w, uint32_t* res_w) {
+  const uint32_t be = __builtin_amdgcn_perm(mb[2], mb[0], 0x0c0c0602u) | __builtin_amdgcn_perm(mb[6], mb[4], 0x06020c0cu);
+  const uint32_t bo = __builtin_amdgcn_perm(mb[3], mb[1], 0x0c0c0602u) | __builtin_amdgcn_perm(mb[7], mb[5], 0x06020c0cu);
   // 0xFF bytes where the value is negative: v_perm selectors 9 / 11 replicate the
   // sign bit of its second / first operand (X_f is never -0 here).
   const uint32_t ne = __builtin_amdgcn_perm(__float_as_uint(xf[2]), __float_as_uint(xf[0]), 0x0c0c0b09u) |
                       __builtin_amdgcn_perm(__float_as_uint(xf[6]), __float_as_uint(xf[4]), 0x0b090c0cu);
   const uint32_t no = __builtin_amdgcn_perm(__float_as_uint(xf[3]), __float_as_uint(xf[1]), 0x0c0c0b09u) |
                       __builtin_amdgcn_perm(__float_as_uint(xf[7]), __float_as_uint(xf[5]), 0x0b090c0cu);
-  const uint32_t ee = be ^ ((ne & 0xF0F0F0F0u) | 0x07070707u);
-  const uint32_t eo = bo ^ ((no & 0xF0F0F0F0u) | 0x07070707u);
+  const uint32_t ee = be ^ (ne & 0xF0F0F0F0u);
+  const uint32_t eo = bo ^ (no & 0xF0F0F0F0u);
   *anc_w = ((ee >> 4) & 0x0F0F0F0Fu) | (eo & 0xF0F0F0F0u);
-  *res_w = (ee & 0x0F0F0F0Fu) | ((eo << 4) & 0xF0F0F0F0u);
+  *res_w = ((ee & 0x0F0F0F0Fu) | ((eo << 4) & 0xF0F0F0F0u)) ^ 0x77777777u;
 }
 
 // Statistics of every 8-token run of one channel, exchanged through LDS:
@@ -245,9 +240,22 @@ __device__ __forceinline__ void chunk_stats(EncodeShared<C>& sh, float* meta, in
   }
 }
 
+// Eq. 7 in float32 for X_f = f, returned as the bits of 128 + Y + 1/2 (Y < 127.5, so
+// the float lies in [128, 256) with an ulp of 2^-16): byte 2 is floor(Y + 1/2) =
+// Round(Y) and the low 16 bits are the fraction of Y + 1/2 in units of 2^-16.
+__device__ __forceinline__ uint32_t y_bits(float f, float alpha, float ylog2k) {
+  const float tt = fmaf(alpha, fabsf(f), 1.0f);
+  return __float_as_uint(fmaf(__builtin_amdgcn_logf(tt), ylog2k, 128.5f));
+}
+
+// Y within `zband` units of 2^-16 of a rounding boundary (fraction of Y + 1/2 near 0 or 1).
+__device__ __forceinline__ bool in_band(uint32_t yb, uint32_t zband) {
+  return ((yb + zband) << 16) < (2u * zband << 16);
+}
+
 // Stages 3-4 ([Review] Mechanism 1, Stages 3-4, Eq. 7 and Eq. 9) for this thread's 8
 // tokens of the tile at t0.  Every element takes the float32 fast path; the rare
-// elements whose float32 Y lies within `ziv` of a rounding boundary are then re-decided
+// elements whose float32 Y lies within the band of a rounding boundary are then re-decided
 // in float64 and their two nibbles patched into the packed words (the fast path's
 // per-element values are dead by then, which leaves room for four workgroups per CU).
 template <int C>
@@ -257,7 +265,8 @@ __device__ __forceinline__ void encode_tokens(const EncodeShared<C>& sh, const E
   const int tok0 = t0 + tg * kTokPerThread;
   if (tok0 >= a.g.P) return;
   const int kc = tg / G;                             // chunk within tile
-  const float alpha = a.alpha, ylog2k = a.ylog2k, zlim = a.zlim;
+  const float alpha = a.alpha, ylog2k = a.ylog2k;
+  const uint32_t zband = a.zband;
   // this thread's columns j*8 + dg of the chunk tables: one base each, j an offset
   const float4* cst_t = &sh.cst[kc][dg];
   const float* sig_t = &sh.sig[kc][dg];
@@ -276,21 +285,19 @@ __device__ __forceinline__ void encode_tokens(const EncodeShared<C>& sh, const E
 #pragma unroll
   for (int i = 0; i < kTokPerThread; ++i) {
     const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-    float r[8], xf[8];
+    uint32_t mb[8];
+    float xf[8];
     bool near[8];                                    // element j lies in the band (a lane mask each)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
       const float f = fmaf(x - ch[j], kk[j], ckn[j]);
-      const float tt = fmaf(alpha, fabsf(f), 1.0f);
-      const float Y = __builtin_amdgcn_logf(tt) * ylog2k;      // Eq. 7 in float32 (Y < 127.5)
-      const float rr = __builtin_rintf(Y);
-      near[j] = fabsf(Y - rr) > zlim;
-      r[j] = rr;
+      mb[j] = y_bits(f, alpha, ylog2k);
+      near[j] = in_band(mb[j], zband);
       xf[j] = f;
     }
     uint32_t aw, rw;
-    pack8(r, xf, &aw, &rw);
+    pack8(mb, xf, &aw, &rw);
     if (near[0] | near[1] | near[2] | near[3] | near[4] | near[5] | near[6] | near[7]) {
       // the per-lane bit mask is formed here, on this rare path only: `one` comes out of an
       // opaque step, so the compiler cannot move the mask's eight selects onto the fast path
@@ -304,10 +311,10 @@ __device__ __forceinline__ void encode_tokens(const EncodeShared<C>& sh, const E
         const uint32_t w = (j >> 1) == 0 ? q[0] : (j >> 1) == 1 ? q[1] : (j >> 1) == 2 ? q[2] : q[3];
         const float x = (j & 1) ? bf16_hi_p(w) : bf16_lo_p(w);
         const float4 cs = cst_t[j * 8];
-        // the fast path's Y again (same operations), to find the boundary it lies near
-        const float Y = __builtin_amdgcn_logf(fmaf(alpha, fabsf(fmaf(x - cs.x, cs.y, cs.z)), 1.0f)) * ylog2k;
-        const float rr = __builtin_rintf(Y);
-        const int jb = (int)rr + (Y > rr ? 1 : 0);                        // in [1, 128]
+        // the fast path's Y again (same operations), to find the boundary it lies near:
+        // a fraction of Y + 1/2 near 0 is the boundary below code I, near 1 the one above
+        const uint32_t yb = y_bits(fmaf(x - cs.x, cs.y, cs.z), alpha, ylog2k);
+        const int jb = (int)((yb >> 16) & 0xFFu) + ((yb & 0xFFFFu) >= 0x8000u ? 1 : 0);   // in [1, 128]
         const float2 e = encode_exact(x, gmin_t[j * 8], D1_t[j * 8], cs.w, (double)sig_t[j * 8] + kEps, jb, sh.bnd);
         const uint32_t byte = (uint32_t)e.x ^ (e.y < 0.0f ? 0xF7u : 0x07u);   // anchor nibble high, residual low
         const uint32_t m = 0xFu << (4 * j);

@@ -45,8 +45,9 @@ struct EncodeArgs {
   Geometry g;
   float alpha;           // alpha of Eq. 7
   float ylog2k;          // 127 / log2(1 + alpha), rounded to float
-  float ziv;             // half-width of the band around a rounding boundary sent to float64
-  float zlim;            // 0.5 - ziv: |Y - Round(Y)| above this goes to float64
+  uint32_t zband;        // half-width, in units of 2^-16 of Y, of the band around a rounding
+                         // boundary whose elements are decided in float64
+  float pad0;
   // bnd[j] = |X_f| at which Y = j - 1/2 (j = 1..127): expm1((j - 1/2) ln(1+alpha)/127)/alpha.
   // bnd[0] = 0, bnd[128] = +inf.  Used by the float64 path to decide Round(Y).
   double bnd[129];
