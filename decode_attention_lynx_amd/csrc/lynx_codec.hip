@@ -41,7 +41,13 @@ __device__ __forceinline__ double shfl_xor_f64(double v, int m) {
 __device__ __forceinline__ float2 encode_exact(float x, float gmin, double D1, float mu, double D2, int jb,
                                             const double* __restrict__ bnd) {
   const double cen = (double)gmin + (double)mu * D1;
-  const double xfe = ((double)x - cen) / (D1 * D2);
+  // 1/(D1*D2) by the hardware reciprocal and two Newton steps (the divisor is a
+  // normal number >= eps^2): relative error a few 2^-53
+  const double den = D1 * D2;
+  double rc = __builtin_amdgcn_rcp(den);
+  rc = fma(fma(-den, rc, 1.0), rc, rc);
+  rc = fma(fma(-den, rc, 1.0), rc, rc);
+  const double xfe = ((double)x - cen) * rc;
   const int I = fabs(xfe) >= bnd[jb] ? jb : jb - 1;
   return make_float2((float)I, (xfe < 0.0) ? -1.0f : 1.0f);
 }
@@ -88,6 +94,7 @@ struct EncodeShared {
   float pmin[kTG][kSlab];
   float pmax[kTG][kSlab];
   double psum[kTG][kSlab];
+  uint32_t gpart[kThreads / kSlab][kSlab];  // page min / max of 8 partial rows, two BF16 per word
   float gmin[kSlab];                     // by column
   double D1[kSlab];
   float4 cst[kChunksPerTile][kSlab];     // by column: c_hi, k, -c_lo*k, mu (float32 fast path + stored mu)
@@ -170,31 +177,26 @@ __device__ __forceinline__ void store_partials(EncodeShared<C>& sh, const uint4 
   }
 }
 
-// Stage 1 ([Review] Mechanism 1, Stage 1): per-channel page min / max from the LDS
-// partial rows (threads tid < 64, one LDS column each); gamma_min and gamma_scale are
-// stored as float32, D1 = gamma_scale + eps is kept in float64.
+// Stage 1 ([Review] Mechanism 1, Stage 1), first half: the page min / max of every
+// channel over 8 of the 32 LDS partial rows, one (row group, column) per thread.  The
+// extremes are BF16 values, stored as the two halves of one word.
 template <int C>
-__device__ __forceinline__ void page_stats(EncodeShared<C>& sh, float* meta, int cbase, int H, int tid) {
-  if (tid < kSlab) {
-    const int col = tid, c = lds_chan(col);
-    float lo = INFINITY, hi = -INFINITY;
-#pragma unroll 8
-    for (int r = 0; r < kTG; ++r) {
-      lo = fminf(lo, sh.pmin[r][lds_swz(r, col)]);
-      hi = fmaxf(hi, sh.pmax[r][lds_swz(r, col)]);
-    }
-    // + 0: a zero minimum / range is stored as +0 whatever the signs of the zeros
-    const float gmin = lo + 0.0f;
-    const float gscale = (float)(((double)hi - (double)gmin) + 0.0);   // exact difference, one rounding
-    const double D1 = (double)gscale + kEps;
-    sh.gmin[col] = gmin;
-    sh.D1[col] = D1;
-    meta[cbase + c] = gmin;
-    meta[H + cbase + c] = gscale;
+__device__ __forceinline__ void page_stats(EncodeShared<C>& sh, int tid) {
+  constexpr int kRows = kTG / (kThreads / kSlab);
+  const int col = tid & (kSlab - 1), part = tid / kSlab;
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int r = part * kRows; r < (part + 1) * kRows; ++r) {
+    lo = fminf(lo, sh.pmin[r][lds_swz(r, col)]);
+    hi = fmaxf(hi, sh.pmax[r][lds_swz(r, col)]);
   }
+  sh.gpart[part][col] = (__float_as_uint(hi) & 0xffff0000u) | (__float_as_uint(lo) >> 16);
 }
 
-// Stage 2 chunk metadata ([Review] Mechanism 1, Stage 2) of the chunks in the tile at t0:
+// Stage 1, second half, and Stage 2 ([Review] Mechanism 1, Stages 1-2) of the chunks in
+// the tile at t0.  Each (chunk, channel) thread combines the four partial page extremes
+// of its channel: gamma_min and gamma_scale are stored as float32 (by the chunk-0
+// threads of the first tile), D1 = gamma_scale + eps is used in float64.  Then
 // mu = mean(X_n), sigma = max |X_n - mu|, both stored as float32 and used in their stored
 // form from here on.  The mean comes from the float64 sum of the chunk's BF16 values;
 // sigma from the chunk's extreme values (X_n is monotone in X).  One (chunk, channel)
@@ -211,14 +213,30 @@ __device__ __forceinline__ void chunk_stats(EncodeShared<C>& sh, float* meta, in
     const int ck = p / kSlab, col = p - ck * kSlab, c = lds_chan(col);
     double s = 0.0;
     float lo = INFINITY, hi = -INFINITY;
-#pragma unroll
+#pragma unroll 8
     for (int r = 0; r < G; ++r) {
       const int row = ck * G + r, pc = lds_swz(row, col);
       s += sh.psum[row][pc];
       lo = fminf(lo, sh.pmin[row][pc]);
       hi = fmaxf(hi, sh.pmax[row][pc]);
     }
-    const double gmin = (double)sh.gmin[col], D1 = sh.D1[col], r1 = 1.0 / D1;
+    float plo = INFINITY, phi = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kThreads / kSlab; ++q) {
+      const uint32_t w = sh.gpart[q][col];
+      plo = fminf(plo, __uint_as_float(w << 16));
+      phi = fmaxf(phi, __uint_as_float(w & 0xffff0000u));
+    }
+    // + 0: a zero minimum / range is stored as +0 whatever the signs of the zeros
+    const float gmin32 = plo + 0.0f;
+    const float gscale = (float)(((double)phi - (double)gmin32) + 0.0);   // exact difference, one rounding
+    const double gmin = (double)gmin32, D1 = (double)gscale + kEps, r1 = 1.0 / D1;
+    if (ck == 0 && t0 == 0) {
+      sh.gmin[col] = gmin32;
+      sh.D1[col] = D1;
+      meta[cbase + c] = gmin32;
+      meta[g.H + cbase + c] = gscale;
+    }
     const double mean = (s - (double)C * gmin) * r1 * (1.0 / C);     // 1/C exact (C a power of two)
     const float mu32 = (float)mean;
     const double mu = (double)mu32;
@@ -374,7 +392,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C >= 6
     }
   }
   __syncthreads();
-  page_stats(sh, u.meta, u.cbase, g.H, tid);
+  page_stats(sh, tid);
   __syncthreads();
 
   // ---- per tile: Stage 2 chunk statistics, then Stages 3-4 per element
