@@ -99,43 +99,61 @@ struct TileIn {
   float km[8], vm[8];   // gamma_min, gamma_scale, mu, sigma of channels lane and lane+64
 };
 
-__device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int tile, int lane, TileIn& t) {
+// Per-lane byte offsets of one wave's tile loads; they do not depend on the tile, whose
+// (wave-uniform) base addresses are added to them.
+struct TileOffsets {
+  uint32_t kcode;   // K code rows: 16g + 64n (+ 1024 mb)
+  uint32_t vcode;   // V code rows: 4n + 256g (+ row constants)
+  uint32_t meta;    // float32 metadata: 4*lane (+ 256 for channels lane + 64)
+};
+
+__device__ __forceinline__ TileOffsets tile_offsets(int lane) {
   const int n = lane & 15, g = lane >> 4;
+  TileOffsets o;
+  o.kcode = (uint32_t)(16 * g + n * (kHeadDim / 2));
+  o.vcode = (uint32_t)(4 * n + 4 * g * (kHeadDim / 2));
+  o.meta = (uint32_t)(4 * lane);
+  return o;
+}
+
+// `tile` is wave-uniform: the page, chunk and segment addresses are scalar arithmetic.
+__device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int tile, const TileOffsets& lo,
+                                          TileIn& t) {
   const int tok = tile * kAttnTile;
   const int page = tok / a.P;
   const int tin = tok - page * a.P;
   const int kc = tin / a.C;
   const size_t seg = ((size_t)b * a.npages + page) * (size_t)a.anc_seg;
-  const uint8_t* kseg = a.kanc + seg;
-  const uint8_t* vseg = a.vanc + seg;
   const size_t row0 = ((size_t)kvh * a.P + tin) * (kHeadDim / 2);
-  const uint8_t* kc_ptr = kseg + row0 + 16 * g;
+  const uint8_t* kcb = a.kanc + seg + row0;
+  const uint8_t* vcb = a.vanc + seg + row0;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) t.kw[mb] = *reinterpret_cast<const uint4*>(kc_ptr + (16 * mb + n) * (kHeadDim / 2));
-  const uint8_t* vc_ptr = vseg + row0 + 4 * n;
+  for (int mb = 0; mb < 4; ++mb)
+    t.kw[mb] = *reinterpret_cast<const uint4*>(kcb + lo.kcode + 16 * mb * (kHeadDim / 2));
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int row = 32 * ks + (r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4));
-      t.vw[8 * ks + r] = *reinterpret_cast<const uint32_t*>(vc_ptr + row * (kHeadDim / 2));
+      const int row = 32 * ks + (r < 4 ? r : 12 + r);     // + 4g (in the lane offset)
+      t.vw[8 * ks + r] = *reinterpret_cast<const uint32_t*>(vcb + lo.vcode + row * (kHeadDim / 2));
     }
-  const float* kmeta = reinterpret_cast<const float*>(kseg + a.codes);
-  const float* vmeta = reinterpret_cast<const float*>(vseg + a.codes);
-  const size_t offs[4] = {0, (size_t)a.H, 2 * (size_t)a.H + (size_t)kc * a.H, 2 * (size_t)a.H + (size_t)(a.nck + kc) * a.H};
+  const uint8_t* kmb = a.kanc + seg + a.codes + (size_t)kvh * kHeadDim * 4;
+  const uint8_t* vmb = a.vanc + seg + a.codes + (size_t)kvh * kHeadDim * 4;
+  const size_t offs[4] = {0, (size_t)a.H, 2 * (size_t)a.H + (size_t)kc * a.H,
+                          2 * (size_t)a.H + (size_t)(a.nck + kc) * a.H};
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
     for (int hlf = 0; hlf < 2; ++hlf) {
-      const size_t c = offs[f] + kvh * kHeadDim + lane + 64 * hlf;
-      t.km[2 * f + hlf] = kmeta[c];
-      t.vm[2 * f + hlf] = vmeta[c];
+      t.km[2 * f + hlf] = *reinterpret_cast<const float*>(kmb + offs[f] * 4 + lo.meta + 256 * hlf);
+      t.vm[2 * f + hlf] = *reinterpret_cast<const float*>(vmb + offs[f] * 4 + lo.meta + 256 * hlf);
     }
 }
 
-__global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
+__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_anchor(AttnArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile addressing stays scalar
   const int n = lane & 15, g = lane >> 4;
   const int hh = n & 7;                 // query head (within the group) of this column
   const bool lo_col = n >= 8;
@@ -182,11 +200,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
   float4* kab = s_kab[wave];
   float4* vab = s_vab[wave];
 
-  TileIn cur, nxt;
-  int tile = t_begin + wave;
-  if (tile < t_end) load_tile(a, b, kvh, tile, lane, cur);
-  for (; tile < t_end; tile += kAttnWaves) {
-    if (tile + kAttnWaves < t_end) load_tile(a, b, kvh, tile + kAttnWaves, lane, nxt);   // prefetch
+  const TileOffsets toff = tile_offsets(lane);
+
+  // one 64-token tile of this wave: scores, online softmax, values
+  auto process = [&](const TileIn& cur) {
 
     // ---- the chunk's affine maps for channels lane, lane+64, shared through LDS:
     //      A = (gamma_scale+eps)(sigma+eps), B = gamma_min + mu (gamma_scale+eps);
@@ -311,7 +328,21 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_attn_anchor(AttnArgs a) {
       }
     }
     __builtin_amdgcn_wave_barrier();   // the next tile rewrites this wave's (A, B) tables
-    cur = nxt;
+  };
+
+  // tiles t_begin + wave, +4, ...: two buffers in turn, the next tile's loads in flight
+  // while the current one is processed
+  TileIn ta, tb;
+  int tile = t_begin + wave;
+  if (tile < t_end) load_tile(a, b, kvh, tile, toff, ta);
+  while (tile < t_end) {
+    if (tile + kAttnWaves < t_end) load_tile(a, b, kvh, tile + kAttnWaves, toff, tb);
+    process(ta);
+    tile += kAttnWaves;
+    if (tile >= t_end) break;
+    if (tile + kAttnWaves < t_end) load_tile(a, b, kvh, tile + kAttnWaves, toff, ta);
+    process(tb);
+    tile += kAttnWaves;
   }
 
   // ---- merge the 4 waves (columns 0..G-1 hold the result; 8..15 duplicate them)
