@@ -65,13 +65,24 @@ __device__ __forceinline__ float dpp_row_ror8(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ float wave_max_g(float v) {   // over the 4 lane groups (l / 16)
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+// Reductions over the 4 lane groups (l / 16) with the gfx950 lane-swap instructions:
+// v_permlane32_swap of a value with itself yields, in every lane, the value of lane
+// l and of lane l ^ 32 in its two outputs; v_permlane16_swap does the same for l ^ 16.
+// No LDS round trip, and every lane of a group ends with the same result.
+__device__ __forceinline__ float xor32_pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_max_g(float v) {
+  v = xor32_pair_max(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float wave_sum_g(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 // The pair table (256 dwords) is held in 64 copies, entry e of copy r at byte
@@ -96,7 +107,7 @@ __device__ __forceinline__ h8 lookup_row(uint32_t w, const uint32_t* s_pair, uin
 struct TileIn {
   uint4 kw[4];          // K code rows tin + 16mb + n, bytes 16g .. 16g+15
   uint32_t vw[16];      // V code dword n of the 16 rows this lane feeds to the value MFMAs
-  float km[8], vm[8];   // gamma_min, gamma_scale, mu, sigma of channels lane and lane+64
+  float km[8], vm[8];   // gamma_min, gamma_scale, mu, sigma of channels 2*lane, 2*lane+1
 };
 
 // Per-lane byte offsets of one wave's tile loads; they do not depend on the tile, whose
@@ -104,7 +115,7 @@ struct TileIn {
 struct TileOffsets {
   uint32_t kcode;   // K code rows: 16g + 64n (+ 1024 mb)
   uint32_t vcode;   // V code rows: 4n + 256g (+ row constants)
-  uint32_t meta;    // float32 metadata: 4*lane (+ 256 for channels lane + 64)
+  uint32_t meta;    // float32 metadata of channels 2*lane, 2*lane + 1: 8*lane
 };
 
 __device__ __forceinline__ TileOffsets tile_offsets(int lane) {
@@ -112,7 +123,7 @@ __device__ __forceinline__ TileOffsets tile_offsets(int lane) {
   TileOffsets o;
   o.kcode = (uint32_t)(16 * g + n * (kHeadDim / 2));
   o.vcode = (uint32_t)(4 * n + 4 * g * (kHeadDim / 2));
-  o.meta = (uint32_t)(4 * lane);
+  o.meta = (uint32_t)(8 * lane);
   return o;
 }
 
@@ -142,12 +153,14 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int
   const size_t offs[4] = {0, (size_t)a.H, 2 * (size_t)a.H + (size_t)kc * a.H,
                           2 * (size_t)a.H + (size_t)(a.nck + kc) * a.H};
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
-#pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf) {
-      t.km[2 * f + hlf] = *reinterpret_cast<const float*>(kmb + offs[f] * 4 + lo.meta + 256 * hlf);
-      t.vm[2 * f + hlf] = *reinterpret_cast<const float*>(vmb + offs[f] * 4 + lo.meta + 256 * hlf);
-    }
+  for (int f = 0; f < 4; ++f) {
+    const float2 k2 = *reinterpret_cast<const float2*>(kmb + offs[f] * 4 + lo.meta);
+    const float2 v2 = *reinterpret_cast<const float2*>(vmb + offs[f] * 4 + lo.meta);
+    t.km[2 * f] = k2.x;
+    t.km[2 * f + 1] = k2.y;
+    t.vm[2 * f] = v2.x;
+    t.vm[2 * f + 1] = v2.y;
+  }
 }
 
 __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_anchor(AttnArgs a) {
@@ -160,7 +173,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
 
   // LDS: the replicated pair table during the loop, reused for the wave merge after it
   constexpr int kPairWords = 256 * 64;
-  constexpr int kMergeWords = kAttnWaves * kMaxGroup * (kHeadDim + 2);
+  // merge records: o of head h at word h*kMergeRow + d + d/32 (one pad word per 32
+  // channels: the writes of the 8 heads x 4 lane groups then fall in 32 banks)
+  constexpr int kMergeRow = kHeadDim + 4;
+  constexpr int kMergeWords = kAttnWaves * kMaxGroup * (kMergeRow + 2);
   __shared__ uint32_t s_big[kPairWords > kMergeWords ? kPairWords : kMergeWords];
   // per wave: (A_K, B_K) and (A_V, B_V) of channels 2i, 2i+1 at slot swz(i), where
   // swz(16g + t) = 4t + g puts the 4 lane groups' simultaneous reads in different banks
@@ -205,31 +221,24 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   // one 64-token tile of this wave: scores, online softmax, values
   auto process = [&](const TileIn& cur) {
 
-    // ---- the chunk's affine maps for channels lane, lane+64, shared through LDS:
+    // ---- the chunk's affine maps for channels 2*lane, 2*lane+1, shared through LDS:
     //      A = (gamma_scale+eps)(sigma+eps), B = gamma_min + mu (gamma_scale+eps);
-    //      the key map carries the softmax scale (base 2)
+    //      the key map carries the softmax scale (base 2).  One 16-byte record per
+    //      channel pair, at slot swz(lane).
     {
       float ak[2], bk[2], av[2], bv[2];
 #pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        const float d1k = cur.km[2 + hlf] + (float)kEps, d2k = cur.km[6 + hlf] + (float)kEps;
-        ak[hlf] = d1k * d2k * qscale;
-        bk[hlf] = fmaf(cur.km[4 + hlf], d1k, cur.km[hlf]) * qscale;
-        const float d1v = cur.vm[2 + hlf] + (float)kEps, d2v = cur.vm[6 + hlf] + (float)kEps;
-        av[hlf] = d1v * d2v;
-        bv[hlf] = fmaf(cur.vm[4 + hlf], d1v, cur.vm[hlf]);
+      for (int e = 0; e < 2; ++e) {
+        const float d1k = cur.km[2 + e] + (float)kEps, d2k = cur.km[6 + e] + (float)kEps;
+        ak[e] = d1k * d2k * qscale;
+        bk[e] = fmaf(cur.km[4 + e], d1k, cur.km[e]) * qscale;
+        const float d1v = cur.vm[2 + e] + (float)kEps, d2v = cur.vm[6 + e] + (float)kEps;
+        av[e] = d1v * d2v;
+        bv[e] = fmaf(cur.vm[4 + e], d1v, cur.vm[e]);
       }
-      // channel c = lane + 64*hlf -> pair slot i = c/2 at swz(i), component c%2
-      float* kf = reinterpret_cast<float*>(kab);
-      float* vf = reinterpret_cast<float*>(vab);
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        const int c = lane + 64 * hlf, i = c >> 1, slot = 4 * (i & 15) + (i >> 4);
-        kf[4 * slot + (c & 1)] = ak[hlf];
-        kf[4 * slot + 2 + (c & 1)] = bk[hlf];
-        vf[4 * slot + (c & 1)] = av[hlf];
-        vf[4 * slot + 2 + (c & 1)] = bv[hlf];
-      }
+      const int slot = 4 * (lane & 15) + (lane >> 4);
+      kab[slot] = make_float4(ak[0], ak[1], bk[0], bk[1]);
+      vab[slot] = make_float4(av[0], av[1], bv[0], bv[1]);
     }
     __builtin_amdgcn_wave_barrier();
 
@@ -350,14 +359,14 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   __syncthreads();                      // every wave is done with the pair table: reuse its LDS
   float (*s_m)[kMaxGroup] = reinterpret_cast<float (*)[kMaxGroup]>(s_big);
   float (*s_l)[kMaxGroup] = reinterpret_cast<float (*)[kMaxGroup]>(s_big + kAttnWaves * kMaxGroup);
-  float (*s_o)[kMaxGroup][kHeadDim] =
-      reinterpret_cast<float (*)[kMaxGroup][kHeadDim]>(s_big + 2 * kAttnWaves * kMaxGroup);
+  float (*s_o)[kMaxGroup][kMergeRow] =
+      reinterpret_cast<float (*)[kMaxGroup][kMergeRow]>(s_big + 2 * kAttnWaves * kMaxGroup);
   if (g == 0 && n < kMaxGroup) { s_m[wave][n] = m_run; s_l[wave][n] = l_run; }
   if (n < kMaxGroup) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_o[wave][n][8 * (4 * g + i) + j] = o_acc[j][i];
+      for (int i = 0; i < 4; ++i) s_o[wave][n][8 * (4 * g + i) + j + g] = o_acc[j][i];   // d = 32g + 8i + j
   }
   __syncthreads();
   for (int idx = tid; idx < a.G * kHeadDim; idx += kAttnWaves * 64) {
@@ -369,7 +378,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
       const float f = (s_m[w][h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
-      o = fmaf(s_o[w][h][d], f, o);
+      o = fmaf(s_o[w][h][d + (d >> 5)], f, o);
       l = fmaf(s_l[w][h], f, l);
     }
     float* rec = a.ws + ((size_t)((b * a.Hq + kvh * a.G + h) * a.splits + split)) * (kHeadDim + 2);
