@@ -43,7 +43,6 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnWaves = 4;
-constexpr int kAttnTile = 64;        // tokens per wave iteration
 constexpr int kMaxGroup = 8;         // query heads per kv head handled by one workgroup
 
 struct AttnArgs {
@@ -104,9 +103,10 @@ __device__ __forceinline__ h8 lookup_row(uint32_t w, const uint32_t* s_pair, uin
 }
 
 // one wave's raw inputs for one 64-token tile
+template <int TILE>
 struct TileIn {
-  uint4 kw[4];          // K code rows tin + 16mb + n, bytes 16g .. 16g+15
-  uint32_t vw[16];      // V code dword n of the 16 rows this lane feeds to the value MFMAs
+  uint4 kw[TILE / 16];      // K code rows tin + 16mb + n, bytes 16g .. 16g+15
+  uint32_t vw[TILE / 4];    // V code dword n of the rows this lane feeds to the value MFMAs
   float km[8], vm[8];   // gamma_min, gamma_scale, mu, sigma of channels 2*lane, 2*lane+1
 };
 
@@ -128,9 +128,10 @@ __device__ __forceinline__ TileOffsets tile_offsets(int lane) {
 }
 
 // `tile` is wave-uniform: the page, chunk and segment addresses are scalar arithmetic.
+template <int TILE>
 __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int tile, const TileOffsets& lo,
-                                          TileIn& t) {
-  const int tok = tile * kAttnTile;
+                                          TileIn<TILE>& t) {
+  const int tok = tile * TILE;
   const int page = tok / a.P;
   const int tin = tok - page * a.P;
   const int kc = tin / a.C;
@@ -139,10 +140,10 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int
   const uint8_t* kcb = a.kanc + seg + row0;
   const uint8_t* vcb = a.vanc + seg + row0;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < TILE / 16; ++mb)
     t.kw[mb] = *reinterpret_cast<const uint4*>(kcb + lo.kcode + 16 * mb * (kHeadDim / 2));
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int ks = 0; ks < TILE / 32; ++ks)
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int row = 32 * ks + (r < 4 ? r : 12 + r);     // + 4g (in the lane offset)
@@ -163,6 +164,7 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int
   }
 }
 
+template <int TILE>
 __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_anchor(AttnArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   const TileOffsets toff = tile_offsets(lane);
 
   // one 64-token tile of this wave: scores, online softmax, values
-  auto process = [&](const TileIn& cur) {
+  auto process = [&](const TileIn<TILE>& cur) {
 
     // ---- the chunk's affine maps for channels 2*lane, 2*lane+1, shared through LDS:
     //      A = (gamma_scale+eps)(sigma+eps), B = gamma_min + mu (gamma_scale+eps);
@@ -267,10 +269,11 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
     beta = wave_sum_g(beta);
 
     // ---- scores: S^T = L_K (64 tokens x 128) * qt (128 x 16 columns)
-    float s[16];
+    constexpr int NS = TILE / 4;         // scores per lane: TILE/16 row blocks x 4
+    float s[NS];
     const float hb = 0.5f * beta;        // each of the two column halves carries half of beta
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < TILE / 16; ++mb) {
       f4 acc = f4{hb, hb, hb, hb};
       const uint32_t w4[4] = {cur.kw[mb].x, cur.kw[mb].y, cur.kw[mb].z, cur.kw[mb].w};
 #pragma unroll
@@ -283,14 +286,14 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
     // ---- online softmax (base 2) for head hh over this tile's 64 tokens
     float mt = s[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
+    for (int i = 1; i < NS; ++i) mt = fmaxf(mt, s[i]);
     mt = wave_max_g(mt);
     const float m_new = fmaxf(m_run, mt);
     const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
     float lsum = 0.0f;
-    h8 pt[2];
+    h8 pt[TILE / 32];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NS; ++i) {
       const float p = __builtin_amdgcn_exp2f(s[i] - m_new);
       lsum += p;
       pt[i >> 3][i & 7] = (_Float16)p;
@@ -309,7 +312,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int j = 0; j < 8; ++j) tacc[j] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < TILE / 32; ++ks) {
       uint32_t ev[4], od[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
 
   // tiles t_begin + wave, +4, ...: two buffers in turn, the next tile's loads in flight
   // while the current one is processed
-  TileIn ta, tb;
+  TileIn<TILE> ta, tb;
   int tile = t_begin + wave;
   if (tile < t_end) load_tile(a, b, kvh, tile, toff, ta);
   while (tile < t_end) {
@@ -416,14 +419,18 @@ __global__ __launch_bounds__(kHeadDim) void k_attn_combine(AttnArgs a) {
 namespace {
 
 struct AttnPlan {
-  int splits, tiles_per_split, ntiles;
+  int tile, splits, tiles_per_split, ntiles;
 };
+
+// Tile of a chunk: 64 tokens, or 32 for a chunk of 32; 0 for chunks the kernel does not take.
+int attn_tile(int C) { return C % 64 == 0 ? 64 : (C % 32 == 0 ? 32 : 0); }
 
 bool attn_plan(int batch, int ctx, int Hq, int Hkv, int D, int P, int C, AttnPlan* pl) {
   if (batch <= 0 || ctx <= 0 || Hq <= 0 || Hkv <= 0 || P <= 0 || C <= 0) return false;
   if (ctx % P != 0 || P % C != 0 || Hq % Hkv != 0) return false;
-  if (D != kHeadDim || C % kAttnTile != 0 || Hq / Hkv > kMaxGroup) return false;
-  pl->ntiles = ctx / kAttnTile;
+  pl->tile = attn_tile(C);
+  if (D != kHeadDim || pl->tile == 0 || Hq / Hkv > kMaxGroup) return false;
+  pl->ntiles = ctx / pl->tile;
   const long long units = (long long)batch * Hkv;
   int want = (int)((2048 + units - 1) / units);               // aim for ~2048 workgroups
   want = std::max(1, std::min(want, pl->ntiles));
@@ -455,7 +462,7 @@ int attn_anchor_launch(const void* q_dev, const void* k_anchor_dev, const void* 
   if (ctx_tokens % page_tokens != 0 || page_tokens % chunk != 0 || q_heads % kv_heads != 0) return LYNX_EINVAL;
   if (!std::isfinite(alpha) || !(alpha > 0.0f) || !std::isfinite(sm_scale)) return LYNX_EINVAL;
   if (out_dtype != LYNX_OUT_BF16 && out_dtype != LYNX_OUT_F32) return LYNX_EINVAL;
-  if (head_dim != kHeadDim || chunk % kAttnTile != 0 || q_heads / kv_heads > kMaxGroup || batch > 65535 ||
+  if (head_dim != kHeadDim || attn_tile(chunk) == 0 || q_heads / kv_heads > kMaxGroup || batch > 65535 ||
       kv_heads > 65535)
     return LYNX_EUNSUPPORTED;
   if (batch == 0) return LYNX_OK;
@@ -502,7 +509,9 @@ int attn_anchor_launch(const void* q_dev, const void* k_anchor_dev, const void* 
   }
   for (int bt = 0; bt < 256; ++bt) a.pair[bt] = (uint32_t)lut[bt & 15] | ((uint32_t)lut[bt >> 4] << 16);
   void* kargs[] = {&a};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&k_attn_anchor),
+  const void* fn = pl.tile == 64 ? reinterpret_cast<const void*>(&k_attn_anchor<64>)
+                                 : reinterpret_cast<const void*>(&k_attn_anchor<32>);
+  hipError_t e = hipLaunchKernel(fn,
                                  dim3((unsigned)pl.splits, (unsigned)kv_heads, (unsigned)batch),
                                  dim3(kAttnWaves * 64), kargs, 0, stream);
   if (e != hipSuccess) return LYNX_ELAUNCH;

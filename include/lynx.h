@@ -150,7 +150,8 @@ size_t lynx_attn_workspace_bytes(int batch, int ctx_tokens, int q_heads, int kv_
  *   q_heads      : a multiple of kv_heads; query head hq reads kv head
  *                  hq / (q_heads/kv_heads).  Group size q_heads/kv_heads <= 8.
  *   ctx_tokens   : a positive multiple of page_tokens.
- *   chunk        : a multiple of 64 in this build (else LYNX_EUNSUPPORTED).
+ *   chunk        : a multiple of 32 in this build (else LYNX_EUNSUPPORTED): each
+ *                  wave step covers 64 tokens, or 32 when chunk == 32, inside one chunk.
  *   sm_scale     : > 0, or <= 0 to use 1/sqrt(head_dim).
  *   workspace_dev, ws_bytes : at least lynx_attn_workspace_bytes(...) bytes.
  *   out_dtype    : LYNX_OUT_BF16 or LYNX_OUT_F32.

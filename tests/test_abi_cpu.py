@@ -93,3 +93,51 @@ def test_decode_validation():
     assert df(res=None) == lynx.LYNX_EALIGN
     assert df(dt=-1) == lynx.LYNX_EINVAL
     assert df(n=0, anc=None, res=None, out=None) == lynx.LYNX_OK
+
+
+def attn(B=2, T=1024, Hq=16, Hkv=2, D=128, P=256, C=64, alpha=255.0, sm=0.0, ws_bytes=None, dt=lynx.OUT_F32,
+         q=GOOD, k=GOOD, v=GOOD, ws=GOOD, out=GOOD):
+    if ws_bytes is None:
+        ws_bytes = 0       # too small for any supported case: the ENOSPACE check comes before any launch
+    return lynx.lib().lynx_attn_anchor(q, k, v, B, T, Hq, Hkv, D, P, C, alpha, sm, ws, ws_bytes, dt, out, None)
+
+
+def test_attention_validation():
+    assert attn(T=1000) == lynx.LYNX_EINVAL                    # ctx % P
+    assert attn(P=96, C=64) == lynx.LYNX_EINVAL                # P % C
+    assert attn(Hq=15) == lynx.LYNX_EINVAL                     # Hq % Hkv
+    assert attn(alpha=0.0) == lynx.LYNX_EINVAL
+    assert attn(alpha=float("nan")) == lynx.LYNX_EINVAL
+    assert attn(sm=float("inf")) == lynx.LYNX_EINVAL
+    assert attn(dt=5) == lynx.LYNX_EINVAL
+    assert attn(T=0) == lynx.LYNX_EINVAL
+    assert attn(D=64) == lynx.LYNX_EUNSUPPORTED
+    assert attn(C=16, P=256) == lynx.LYNX_EUNSUPPORTED          # chunk not a multiple of 32
+    assert attn(Hq=18, Hkv=2) == lynx.LYNX_EUNSUPPORTED         # group of 9 query heads
+    assert attn(q=ODD) == lynx.LYNX_EALIGN
+    assert attn(out=None) == lynx.LYNX_EALIGN
+    assert attn(ws=ODD) == lynx.LYNX_EALIGN
+    assert attn() == lynx.LYNX_ENOSPACE
+    assert attn(C=32) == lynx.LYNX_ENOSPACE                     # chunk 32: supported, workspace too small
+    assert attn(B=0) == lynx.LYNX_OK                            # nothing to do
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,P,C", [(16, 32768, 64, 8, 256, 64), (2, 1024, 16, 2, 256, 64),
+                                            (3, 320, 8, 1, 64, 64), (2, 512, 8, 2, 256, 32), (1, 64, 2, 2, 64, 64)])
+def test_attention_workspace_bytes(B, T, Hq, Hkv, P, C):
+    """One (m, l, o[128]) float32 record per (sequence, query head, context split); the splits
+    cover the context's tiles with no empty split."""
+    ws = lynx.attn_workspace_bytes(B, T, Hq, Hkv, 128, P, C)
+    rec = (128 + 2) * 4
+    assert ws > 0 and ws % (B * Hq * rec) == 0
+    splits = ws // (B * Hq * rec)
+    tile = 64 if C % 64 == 0 else 32
+    ntiles = T // tile
+    per = -(-ntiles // splits)
+    assert 1 <= splits <= ntiles and (splits - 1) * per < ntiles <= splits * per
+
+
+def test_attention_workspace_bytes_unsupported():
+    assert lynx.attn_workspace_bytes(2, 1024, 16, 2, 128, 256, 16) == 0
+    assert lynx.attn_workspace_bytes(2, 1000, 16, 2, 128, 256, 64) == 0
+    assert lynx.attn_workspace_bytes(2, 1024, 16, 2, 64, 256, 64) == 0
