@@ -400,3 +400,54 @@ def attention_anchor(q_bits: np.ndarray, k_anchor: np.ndarray, v_anchor: np.ndar
         Vh = decode_anchor(v_anchor[b], n_pages, P, Hkv, D, C, alpha)[None]
         O[b] = attention(q[b:b + 1], Kh, Vh, sm_scale)[0]
     return O
+
+
+def attention_lse(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float | None = None):
+    """q: [R, Hq, D] (R query tokens); K, V: [T, Hkv, D] (float64), shared by the R queries.
+
+    Returns (O [R, Hq, D], lse [R, Hq]): Eq. 1 per query token and head (R-attn grouping), and the
+    natural-log log-sum-exp of the scaled scores, log(sum_t exp(s_t)) with s_t = scale * q . k_t.
+    """
+    R, Hq, D = q.shape
+    T, Hkv, _ = K.shape
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(D) if sm_scale is None else float(sm_scale)
+    O = np.empty((R, Hq, D), dtype=np.float64)
+    lse = np.empty((R, Hq), dtype=np.float64)
+    for h in range(Hkv):
+        qg = np.asarray(q[:, h * G:(h + 1) * G, :], dtype=np.float64).reshape(R * G, D)
+        s = (qg @ K[:, h, :].T) * scale
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        tot = e.sum(axis=1, keepdims=True)
+        O[:, h * G:(h + 1) * G, :] = ((e / tot) @ V[:, h, :]).reshape(R, G, D)
+        lse[:, h * G:(h + 1) * G] = (m + np.log(tot)).reshape(R, G)
+    return O, lse
+
+
+def attention_verify(q_bits: np.ndarray, k_anchor: np.ndarray, k_residual: np.ndarray, v_anchor: np.ndarray,
+                     v_residual: np.ndarray, batch: int, n_query: int, ctx: int, Hq: int, Hkv: int, D: int,
+                     P: int, C: int, alpha: float, sm_scale: float | None = None):
+    """The verification pass ([Review] Mechanism 3, single parallel verification pass, with Eq. 1): each of
+    the n_query draft tokens of sequence b attends to the ctx context tokens whose K and V are the full
+    decode, Q_full = dequant(Q_anc + Q_res) (Mechanism 2, residual phase).
+
+    q_bits: [B, n_query, Hq, D] BF16 patterns; *_anchor / *_residual: B*ctx/P segments, sequence-major.
+    Returns (O [B, n_query, Hq, D], lse [B, n_query, Hq]) in float64; lse is the natural-log log-sum-exp
+    of each query's scaled scores over the context (what a caller needs to merge this result with the
+    draft tokens' attention over themselves, which is not in the compressed cache).
+    """
+    n_pages = ctx // P
+    q = bf16_bits_to_f64(q_bits)
+    a_sz, r_sz = segment_bytes(P, Hkv, D, C)
+    ka = np.asarray(k_anchor, dtype=np.uint8).reshape(batch, n_pages * a_sz)
+    kr = np.asarray(k_residual, dtype=np.uint8).reshape(batch, n_pages * r_sz)
+    va = np.asarray(v_anchor, dtype=np.uint8).reshape(batch, n_pages * a_sz)
+    vr = np.asarray(v_residual, dtype=np.uint8).reshape(batch, n_pages * r_sz)
+    O = np.empty((batch, n_query, Hq, D), dtype=np.float64)
+    lse = np.empty((batch, n_query, Hq), dtype=np.float64)
+    for b in range(batch):
+        Kh = decode_full(ka[b], kr[b], n_pages, P, Hkv, D, C, alpha)
+        Vh = decode_full(va[b], vr[b], n_pages, P, Hkv, D, C, alpha)
+        O[b], lse[b] = attention_lse(q[b], Kh, Vh, sm_scale)
+    return O, lse

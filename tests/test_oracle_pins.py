@@ -373,6 +373,70 @@ def test_attention_anchor_uses_anchor_decode():
     assert np.max(np.abs(O - o.attention(o.bf16_bits_to_f64(qb), Kh, Vh))) < 1e-12
 
 
+def test_attention_lse_matches_library():
+    """O against torch SDPA and lse against torch.logsumexp of the scaled scores, for R query tokens
+    sharing one K/V (the verification pass's shape)."""
+    rng = np.random.default_rng(5)
+    R, Hq, Hkv, T, D = 3, 8, 2, 33, 16
+    q = rng.standard_normal((R, Hq, D))
+    K, V = rng.standard_normal((T, Hkv, D)), rng.standard_normal((T, Hkv, D))
+    O, lse = o.attention_lse(q, K, V, sm_scale=0.3)
+    G = Hq // Hkv
+    Kt = torch.tensor(K).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]     # [1, Hq, T, D]
+    Vt = torch.tensor(V).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+    qt = torch.tensor(q).permute(1, 0, 2)[None]                                 # [1, Hq, R, D]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, scale=0.3)[0].permute(1, 0, 2)
+    assert np.max(np.abs(O - ref.numpy())) < 1e-12
+    lref = torch.logsumexp(torch.einsum("hrd,htd->hrt", qt[0], Kt[0]) * 0.3, dim=-1).T
+    assert np.max(np.abs(lse - lref.numpy())) < 1e-12
+
+
+def test_attention_lse_closed_forms_and_merge():
+    """Identical keys: uniform weights, O = mean V and lse = s + log T.  Splitting the context in two
+    and merging the halves with their lse gives the whole."""
+    rng = np.random.default_rng(6)
+    R, Hq, Hkv, T, D = 2, 4, 1, 12, 8
+    q = rng.standard_normal((R, Hq, D))
+    K, V = rng.standard_normal((T, Hkv, D)), rng.standard_normal((T, Hkv, D))
+    Ku = np.repeat(K[:1], T, axis=0)
+    O, lse = o.attention_lse(q, Ku, V)
+    s0 = (q @ Ku[0, 0]) / np.sqrt(D)
+    assert np.max(np.abs(O - V[:, 0].mean(axis=0))) < 1e-14
+    assert np.max(np.abs(lse - (s0 + np.log(T)))) < 1e-13
+    O1, l1 = o.attention_lse(q, K[:5], V[:5])
+    O2, l2 = o.attention_lse(q, K[5:], V[5:])
+    Ow, lw = o.attention_lse(q, K, V)
+    M = np.maximum(l1, l2)
+    w1, w2 = np.exp(l1 - M), np.exp(l2 - M)
+    assert np.max(np.abs((O1 * w1[..., None] + O2 * w2[..., None]) / (w1 + w2)[..., None] - Ow)) < 1e-13
+    assert np.max(np.abs(M + np.log(w1 + w2) - lw)) < 1e-13
+
+
+def test_attention_verify_uses_full_decode():
+    """The verification pass is Eq. 1 over the full (anchor + residual) decode; with one query token
+    it is the single-token attention over that decode."""
+    P, C, Hkv, D, B, T, M, Hq = 32, 16, 2, 16, 2, 64, 3, 4
+    kb = np.concatenate([synth.make_kv_np(T, Hkv, D, seed=8, layer=b, kv_idx=0) for b in range(B)])
+    vb = np.concatenate([synth.make_kv_np(T, Hkv, D, seed=8, layer=b, kv_idx=1) for b in range(B)])
+    ka, kr, _ = o.encode(kb, P, C, 63.0)
+    va, vr, _ = o.encode(vb, P, C, 63.0)
+    qb = synth.make_q_np(B * M, Hq, D, seed=2).reshape(B, M, Hq, D)
+    O, lse = o.attention_verify(qb, ka, kr, va, vr, B, M, T, Hq, Hkv, D, P, C, 63.0)
+    Kh = o.decode_full(ka, kr, B * T // P, P, Hkv, D, C, 63.0).reshape(B, T, Hkv, D)
+    Vh = o.decode_full(va, vr, B * T // P, P, Hkv, D, C, 63.0).reshape(B, T, Hkv, D)
+    q = o.bf16_bits_to_f64(qb)
+    for m in range(M):
+        assert np.max(np.abs(O[:, m] - o.attention(q[:, m], Kh, Vh))) < 1e-12
+    # the full decode is closer to the BF16 input than the anchor decode, and so is the attention
+    Kb = o.bf16_bits_to_f64(kb).reshape(B, T, Hkv, D)
+    Vb = o.bf16_bits_to_f64(vb).reshape(B, T, Hkv, D)
+    ref = np.stack([o.attention(q[:, m], Kb, Vb) for m in range(M)], axis=1)
+    Ka = o.decode_anchor(ka, B * T // P, P, Hkv, D, C, 63.0).reshape(B, T, Hkv, D)
+    Va = o.decode_anchor(va, B * T // P, P, Hkv, D, C, 63.0).reshape(B, T, Hkv, D)
+    Oa = np.stack([o.attention(q[:, m], Ka, Va) for m in range(M)], axis=1)
+    assert np.linalg.norm(O - ref) < np.linalg.norm(Oa - ref)
+
+
 def test_signed_zero_metadata_is_plus_zero():
     """Reading R-zero: a channel of +-0 values stores gamma_min = gamma_scale = +0 and encodes to
     (I, S) = (0, +1) everywhere, as the constant-channel closed form."""
