@@ -8,6 +8,9 @@ One step =
   decode_full   the same request back to BF16 from anchor + residual
   attn_anchor   16 sequences x 64 query heads / 8 kv heads x 32768-token context
                 over anchor segments (P = 256, C = 64, alpha = 255)
+Timed after the step, on its own (not part of `value`):
+  attn_verify   the verification pass over full codes: the same 16 sequences with
+                64 draft tokens each, anchor + residual segments
 Inputs are synthetic (Laplacian + per-channel offset + x100 outlier channels,
 seeded) and resident in HBM before the timed region.
 
@@ -31,9 +34,11 @@ HBM_PEAK_GBS = 8000.0
 LAYERS, TOKENS, KVH, D = 32, 16384, 8, 128
 P, C, ALPHA = 256, 64, 255.0
 AB, AHQ, AHKV, AT = 16, 64, 8, 32768
+AM = 64                      # draft tokens per sequence in the verification pass
+MFMA_PEAK_TFLOPS = 2500.0    # dense float16 / bfloat16 MFMA
 KERNEL_SOURCES = ["decode_attention_lynx_amd/csrc/lynx_codec.hip", "decode_attention_lynx_amd/csrc/lynx_attn.hip",
                   "decode_attention_lynx_amd/csrc/lynx_common.hpp", "decode_attention_lynx_amd/csrc/lynx_abi.hip",
-                  "decode_attention_lynx_amd/csrc/hbm_probe.hip"]
+                  "decode_attention_lynx_amd/csrc/hbm_probe.hip", "decode_attention_lynx_amd/csrc/lynx_verify.hip"]
 
 
 def alg_bytes_per_elem(op: str) -> float:
@@ -41,13 +46,19 @@ def alg_bytes_per_elem(op: str) -> float:
     float32 metadata 8/C + 8/P B)."""
     meta = 8.0 / C + 8.0 / P
     return {"encode": 2.0 + 1.0 + meta, "decode_anchor": 0.5 + meta + 2.0, "decode_full": 1.0 + meta + 2.0,
-            "attn_anchor": 0.5 + meta, "copy": 4.0}[op]
+            "attn_anchor": 0.5 + meta, "attn_verify": 1.0 + meta, "copy": 4.0}[op]
+
+
+def op_flops(op: str) -> float:
+    """Algorithmic flops of one launch: 2 x (q.k) + 2 x (p.v) per (query, head, context token, channel)."""
+    return {"attn_verify": 4.0 * AB * AM * AHQ * AT * D}.get(op, 0.0)
 
 
 def op_elems(op: str) -> int:
     """KV elements one launch of an op processes (the copy counts 2-byte elements of 1 GiB)."""
     return {"encode": LAYERS * 2 * TOKENS * KVH * D, "decode_anchor": LAYERS * 2 * TOKENS * KVH * D,
             "decode_full": LAYERS * 2 * TOKENS * KVH * D, "attn_anchor": 2 * AB * AT * AHKV * D,
+            "attn_verify": 2 * AB * AT * AHKV * D,
             "copy": (1 << 30) // 2}[op]
 
 
@@ -57,6 +68,7 @@ OP_KERNELS = {
     "decode_anchor": [("lynx::k_decode<false, false>", None)],
     "decode_full": [("lynx::k_decode<true, false>", None)],
     "attn_anchor": [("lynx::k_attn_anchor", None), ("lynx::k_attn_combine", None)],
+    "attn_verify": [("lynx::k_verify", None), ("lynx::k_verify_combine", None)],
     "copy": [("hbm_probe::k_probe_copy", None)],
 }
 
@@ -97,6 +109,8 @@ def counter_summary(fetch_csv: str, write_csv: str, out_json: str) -> str:
     lines = [f"calibration (1 GiB copy): FETCH_SIZE x {f_fetch:.4f}, WRITE_SIZE x {f_write:.4f}",
              f"{'op':15s} {'FETCH KiB':>12s} {'WRITE KiB':>12s} {'HBM bytes':>14s} {'algorithmic':>14s} {'ratio':>7s}"]
     for op in OP_KERNELS:
+        if not any(n == name for name, _ in OP_KERNELS[op] for (n, _g) in fetch):
+            continue        # not run in these profiles
         fk, wk = per_op(fetch, op), per_op(write, op)
         hbm = fk * 1024.0 * f_fetch + wk * 1024.0 * f_write
         alg = alg_bytes_per_elem(op) * op_elems(op)
@@ -221,6 +235,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ops", default="encode,decode_anchor,decode_full,attn_anchor")
+    ap.add_argument("--next-ops", default="attn_verify",
+                    help="ops timed after the step, on their own (empty: none)")
     ap.add_argument("--counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="summarise two rocprofv3 --pmc runs of this benchmark into per-op HBM bytes")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
@@ -256,17 +272,25 @@ def main():
     residual = torch.empty((n_pages, r_sz), dtype=torch.uint8, device=dev)
     out_a = torch.empty_like(kv)
     out_f = torch.empty_like(kv)
-    # attention inputs: anchor segments of 16 sequences x 32768 tokens, encoded once
+    next_ops = [x for x in args.next_ops.split(",") if x]
+    # attention inputs: segments of 16 sequences x 32768 tokens, encoded once (the residual
+    # stream only when the verification pass is timed)
     akv = torch.empty((AB * AT, AHKV, D), dtype=torch.bfloat16, device=dev)
-    att = {}
+    att, att_res = {}, {}
     for kv_idx in (0, 1):
         for b in range(AB):
             synth.make_kv_torch(AT, AHKV, D, seed=1, layer=b, kv_idx=kv_idx, out=akv[b * AT:(b + 1) * AT])
-        att[kv_idx], _ = lynx.encode(akv, P, C, ALPHA, residual=False)
+        att[kv_idx], att_res[kv_idx] = lynx.encode(akv, P, C, ALPHA, residual="attn_verify" in next_ops + ops)
     del akv
     q = synth.make_q_torch(AB, AHQ, D, seed=0)
     ws = torch.empty(lynx.attn_workspace_bytes(AB, AT, AHQ, AHKV, D, P, C), dtype=torch.uint8, device=dev)
     o_att = torch.empty((AB, AHQ, D), dtype=torch.bfloat16, device=dev)
+    if "attn_verify" in next_ops + ops:
+        qv = synth.make_q_torch(AB * AM, AHQ, D, seed=2).view(AB, AM, AHQ, D)
+        ws_v = torch.empty(lynx.attn_verify_workspace_bytes(AB, AM, AT, AHQ, AHKV, D, P, C), dtype=torch.uint8,
+                           device=dev)
+        o_ver = torch.empty((AB, AM, AHQ, D), dtype=torch.bfloat16, device=dev)
+        lse_ver = torch.empty((AB, AM, AHQ), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     # plain streaming kernels (libhbmprobe.so): what this HBM sustains, and a 1 GiB copy of
@@ -288,6 +312,11 @@ def main():
             lynx.decode_full(anchor, residual, n_pages, P, KVH, D, C, ALPHA, out=out_f)
         elif op == "attn_anchor":
             lynx.attn_anchor(q, att[0], att[1], AT, AHKV, P, C, ALPHA, workspace=ws, out=o_att)
+        elif op == "attn_verify":
+            lynx.attn_verify(qv, att[0], att_res[0], att[1], att_res[1], AT, AHKV, P, C, ALPHA, workspace=ws_v,
+                             out=o_ver, lse=lse_ver)
+        else:
+            raise ValueError(f"unknown op {op}")
 
     elems = {op: op_elems(op) for op in ops}
     for _ in range(args.warmup):
@@ -307,6 +336,20 @@ def main():
         print(f"[bench] step {s + 1}/{args.steps} enqueued", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # ops beyond the step, timed on their own with the same warmup and step counts
+    nev = {}
+    for op in next_ops:
+        for _ in range(args.warmup):
+            run(op)
+        nev[op] = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+        for s in range(args.steps):
+            nev[op][s][0].record(stream)
+            run(op)
+            nev[op][s][1].record(stream)
+        torch.cuda.synchronize()
+        print(f"[bench] {op}: {args.steps} launches timed", file=sys.stderr, flush=True)
 
     # measured HBM ceilings (not part of the timed step)
     def probe_gbs(fn, nbytes):
@@ -333,6 +376,15 @@ def main():
         per_op[op] = {"ms": round(ms[op], 4), "bf16_equiv_GBs": round(2.0 * elems[op] / ms[op] / 1e6, 1),
                       "alg_GBs": round(alg / ms[op] / 1e6, 1), "frac_hbm_peak": round(alg / ms[op] / 1e6 / HBM_PEAK_GBS, 4),
                       "alg_bytes_per_launch": int(alg)}
+    next_rep = {}
+    for op in next_ops:
+        t = sum(a.elapsed_time(b) for a, b in nev[op]) / args.steps
+        fl = op_flops(op)
+        next_rep[op] = {"ms": round(t, 4), "TFLOPs": round(fl / t / 1e9, 1),
+                        "frac_mfma_peak": round(fl / t / 1e9 / MFMA_PEAK_TFLOPS, 4),
+                        "alg_GBs": round(alg_bytes_per_elem(op) * op_elems(op) / t / 1e6, 1),
+                        "alg_flops_per_launch": fl,
+                        "alg_bytes_per_launch": int(alg_bytes_per_elem(op) * op_elems(op))}
     path_ops = [op for op in ops if op != "copy"]
     total_bf16 = sum(2.0 * elems[op] for op in path_ops)
     value = total_bf16 / (step_ms / 1e3) / 1e9
@@ -347,6 +399,9 @@ def main():
                                "C=64, alpha=255: encode + decode_anchor + decode_full) + anchor-only decode "
                                "attention (16 seq x 64 q / 8 kv heads x 128, 32768-token context)",
                    "ops": per_op, "hbm_peak_GBs": HBM_PEAK_GBS, "hbm_measured": hbm,
+                   "beyond_step": {"workload": f"verification pass over full codes ({AB} seq x {AM} draft tokens "
+                                               f"x {AHQ} q / {AHKV} kv heads x {D}, {AT}-token context); "
+                                               "bound: mfma", "ops": next_rep},
                    "arith": "float32 codec (float64 statistics and boundary cases), float16 MFMA attention "
                             "with float32 accumulation"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

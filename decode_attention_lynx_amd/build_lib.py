@@ -6,7 +6,7 @@ import subprocess
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["csrc/lynx_abi.hip", "csrc/lynx_codec.hip", "csrc/lynx_attn.hip"]
+SOURCES = ["csrc/lynx_abi.hip", "csrc/lynx_codec.hip", "csrc/lynx_attn.hip", "csrc/lynx_verify.hip"]
 OUT = os.path.join(PKG, "liblynx.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",

@@ -205,4 +205,19 @@ int lynx_attn_anchor(const void* q_dev, const void* k_anchor_dev, const void* v_
                             static_cast<hipStream_t>(hip_stream));
 }
 
+size_t lynx_attn_verify_workspace_bytes(int batch, int n_query, int ctx_tokens, int q_heads, int kv_heads,
+                                        int head_dim, int page_tokens, int chunk) {
+  return verify_workspace_bytes(batch, n_query, ctx_tokens, q_heads, kv_heads, head_dim, page_tokens, chunk);
+}
+
+int lynx_attn_verify(const void* q_dev, const void* k_anchor_dev, const void* k_residual_dev,
+                     const void* v_anchor_dev, const void* v_residual_dev, int batch, int n_query, int ctx_tokens,
+                     int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk, float alpha,
+                     float sm_scale, void* workspace_dev, size_t ws_bytes, int out_dtype, void* out_dev,
+                     float* lse_dev, void* hip_stream) {
+  return verify_launch(q_dev, k_anchor_dev, k_residual_dev, v_anchor_dev, v_residual_dev, batch, n_query,
+                       ctx_tokens, q_heads, kv_heads, head_dim, page_tokens, chunk, alpha, sm_scale, workspace_dev,
+                       ws_bytes, out_dtype, out_dev, lse_dev, static_cast<hipStream_t>(hip_stream));
+}
+
 }  // extern "C"

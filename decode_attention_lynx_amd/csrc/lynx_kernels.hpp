@@ -21,4 +21,12 @@ int attn_anchor_launch(const void* q_dev, const void* k_anchor_dev, const void* 
                        float alpha, float sm_scale, void* workspace_dev, size_t ws_bytes, int out_dtype,
                        void* out_dev, hipStream_t stream);
 
+// Verification-pass attention over full codes (lynx_verify.hip).
+size_t verify_workspace_bytes(int batch, int n_query, int ctx_tokens, int q_heads, int kv_heads, int head_dim,
+                              int page_tokens, int chunk);
+int verify_launch(const void* q_dev, const void* k_anchor_dev, const void* k_residual_dev, const void* v_anchor_dev,
+                  const void* v_residual_dev, int batch, int n_query, int ctx_tokens, int q_heads, int kv_heads,
+                  int head_dim, int page_tokens, int chunk, float alpha, float sm_scale, void* workspace_dev,
+                  size_t ws_bytes, int out_dtype, void* out_dev, float* lse_dev, hipStream_t stream);
+
 }  // namespace lynx

@@ -22,7 +22,7 @@ OUT_F32 = 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblynx.so")
 EXPORTS = ("lynx_strerror", "lynx_stream_sizes", "lynx_encode", "lynx_decode_anchor", "lynx_decode_full",
-           "lynx_attn_workspace_bytes", "lynx_attn_anchor")
+           "lynx_attn_workspace_bytes", "lynx_attn_anchor", "lynx_attn_verify_workspace_bytes", "lynx_attn_verify")
 
 _lib = None
 
@@ -58,6 +58,11 @@ def lib() -> ctypes.CDLL:
         L.lynx_attn_anchor.restype = c_int
         L.lynx_attn_anchor.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                        c_float, c_float, c_void, c_size, c_int, c_void, c_void]
+        L.lynx_attn_verify_workspace_bytes.restype = c_size
+        L.lynx_attn_verify_workspace_bytes.argtypes = [c_int] * 8
+        L.lynx_attn_verify.restype = c_int
+        L.lynx_attn_verify.argtypes = [c_void, c_void, c_void, c_void, c_void] + [c_int] * 8 + [
+            c_float, c_float, c_void, c_size, c_int, c_void, c_void, c_void]
         _lib = L
     return _lib
 
@@ -153,3 +158,35 @@ def attn_anchor(q, k_anchor, v_anchor, ctx_tokens: int, kv_heads: int, page_toke
                                   page_tokens, chunk, alpha, sm_scale, _ptr(workspace), workspace.numel(), code,
                                   _ptr(out), _stream(stream)), "lynx_attn_anchor")
     return out
+
+
+def attn_verify_workspace_bytes(batch: int, n_query: int, ctx_tokens: int, q_heads: int, kv_heads: int,
+                                head_dim: int, page_tokens: int, chunk: int) -> int:
+    return int(lib().lynx_attn_verify_workspace_bytes(batch, n_query, ctx_tokens, q_heads, kv_heads, head_dim,
+                                                      page_tokens, chunk))
+
+
+def attn_verify(q, k_anchor, k_residual, v_anchor, v_residual, ctx_tokens: int, kv_heads: int, page_tokens: int,
+                chunk: int, alpha: float, sm_scale: float = 0.0, out_dtype=None, want_lse: bool = True,
+                workspace=None, out=None, lse=None, stream=None):
+    """q: CUDA bfloat16 [B, M, Hq, D]; K/V anchor and residual: B*ctx/P segments each.
+
+    Returns (O [B, M, Hq, D], lse float32 [B, M, Hq] natural log, or None when want_lse is False)."""
+    import torch
+    B, M, Hq, D = q.shape
+    ws = attn_verify_workspace_bytes(B, M, ctx_tokens, Hq, kv_heads, D, page_tokens, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
+    dt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, M, Hq, D), dtype=dt, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((B, M, Hq), dtype=torch.float32, device=q.device)
+    if not want_lse:
+        lse = None
+    code = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    _check(lib().lynx_attn_verify(_ptr(q), _ptr(k_anchor), _ptr(k_residual), _ptr(v_anchor), _ptr(v_residual), B, M,
+                                  ctx_tokens, Hq, kv_heads, D, page_tokens, chunk, alpha, sm_scale, _ptr(workspace),
+                                  workspace.numel(), code, _ptr(out), _ptr(lse), _stream(stream)),
+           "lynx_attn_verify")
+    return out, lse

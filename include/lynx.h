@@ -164,6 +164,41 @@ int lynx_attn_anchor(const void* q_dev, const void* k_anchor_dev, const void* v_
                      void* workspace_dev, size_t ws_bytes, int out_dtype, void* out_dev,
                      void* hip_stream);
 
+/*
+ * Bytes of workspace lynx_attn_verify needs for this shape, or 0 if the shape is
+ * not supported (see lynx_attn_verify).
+ */
+size_t lynx_attn_verify_workspace_bytes(int batch, int n_query, int ctx_tokens, int q_heads,
+                                        int kv_heads, int head_dim, int page_tokens, int chunk);
+
+/*
+ * The verification pass over full codes ([Review] Mechanism 3, single parallel
+ * verification pass; Mechanism 2, residual phase; Eq. 1): each of the n_query draft
+ * tokens of a sequence attends, per query head, to the sequence's ctx_tokens context
+ * tokens, whose K and V are the full (anchor + residual) reconstruction:
+ *   O[b,m,hq] = softmax(q[b,m,hq] K^T * sm_scale) V,  lse[b,m,hq] = log(sum_t exp(s_t)).
+ * The draft tokens' own keys and values are not in the compressed cache: a caller
+ * merges O with the attention over them through lse (natural logarithm).
+ *   q_dev        : BF16 [batch][n_query][q_heads][head_dim].
+ *   k_anchor_dev, k_residual_dev, v_anchor_dev, v_residual_dev : anchor and residual
+ *                  segments; sequence b's context is the ctx_tokens/page_tokens
+ *                  consecutive segments starting at segment b*(ctx_tokens/page_tokens).
+ *   q_heads      : a multiple of kv_heads (query head hq reads kv head hq / (q_heads/kv_heads)).
+ *   chunk        : a multiple of 64 in this build (else LYNX_EUNSUPPORTED).
+ *   sm_scale     : > 0, or <= 0 to use 1/sqrt(head_dim).
+ *   workspace_dev, ws_bytes : at least lynx_attn_verify_workspace_bytes(...) bytes.
+ *   out_dtype    : LYNX_OUT_BF16 or LYNX_OUT_F32; out_dev [batch][n_query][q_heads][head_dim].
+ *   lse_dev      : float32 [batch][n_query][q_heads], written; may be NULL.
+ * Keys are formed in float32 and carried as BF16 high + low parts (~16 significant
+ * bits); values as float16 table values with the affine map applied in float32.
+ * Supported in this build: head_dim == 128.  Asynchronous on hip_stream.
+ */
+int lynx_attn_verify(const void* q_dev, const void* k_anchor_dev, const void* k_residual_dev,
+                     const void* v_anchor_dev, const void* v_residual_dev, int batch, int n_query,
+                     int ctx_tokens, int q_heads, int kv_heads, int head_dim, int page_tokens,
+                     int chunk, float alpha, float sm_scale, void* workspace_dev, size_t ws_bytes,
+                     int out_dtype, void* out_dev, float* lse_dev, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -141,3 +141,50 @@ def test_attention_workspace_bytes_unsupported():
     assert lynx.attn_workspace_bytes(2, 1024, 16, 2, 128, 256, 16) == 0
     assert lynx.attn_workspace_bytes(2, 1000, 16, 2, 128, 256, 64) == 0
     assert lynx.attn_workspace_bytes(2, 1024, 16, 2, 64, 256, 64) == 0
+
+
+def verify(B=2, M=4, T=1024, Hq=16, Hkv=2, D=128, P=256, C=64, alpha=255.0, sm=0.0, dt=lynx.OUT_F32, q=GOOD,
+           k=GOOD, kr=GOOD, v=GOOD, vr=GOOD, ws=GOOD, out=GOOD, lse=None):
+    # workspace size 0: too small for any supported case, so no call below reaches a launch
+    return lynx.lib().lynx_attn_verify(q, k, kr, v, vr, B, M, T, Hq, Hkv, D, P, C, alpha, sm, ws, 0, dt, out, lse,
+                                       None)
+
+
+def test_verify_validation():
+    assert verify(T=1000) == lynx.LYNX_EINVAL                  # ctx % P
+    assert verify(P=96, C=64) == lynx.LYNX_EINVAL              # P % C
+    assert verify(Hq=15) == lynx.LYNX_EINVAL                   # Hq % Hkv
+    assert verify(M=0) == lynx.LYNX_EINVAL
+    assert verify(alpha=-1.0) == lynx.LYNX_EINVAL
+    assert verify(sm=float("nan")) == lynx.LYNX_EINVAL
+    assert verify(dt=3) == lynx.LYNX_EINVAL
+    assert verify(D=64) == lynx.LYNX_EUNSUPPORTED
+    assert verify(C=32, P=256) == lynx.LYNX_EUNSUPPORTED        # chunk not a multiple of 64
+    assert verify(kr=ODD) == lynx.LYNX_EALIGN
+    assert verify(vr=None) == lynx.LYNX_EALIGN
+    assert verify(lse=ctypes.c_void_p(GOOD.value + 2)) == lynx.LYNX_EALIGN
+    assert verify() == lynx.LYNX_ENOSPACE
+    assert verify(lse=GOOD) == lynx.LYNX_ENOSPACE
+    assert verify(B=0) == lynx.LYNX_OK                          # nothing to do
+
+
+@pytest.mark.parametrize("B,M,T,Hq,Hkv,P,C", [(16, 64, 32768, 64, 8, 256, 64), (2, 4, 1024, 16, 2, 256, 64),
+                                              (1, 17, 256, 64, 8, 256, 64), (3, 1, 320, 8, 1, 64, 64),
+                                              (2, 5, 512, 12, 4, 256, 128)])
+def test_verify_workspace_bytes(B, M, T, Hq, Hkv, P, C):
+    """One (m, l, 0, 0, o[128]) float32 record per (sequence, draft token, query head, context split);
+    the splits cover the context's 64-token tiles with no empty split."""
+    ws = lynx.attn_verify_workspace_bytes(B, M, T, Hq, Hkv, 128, P, C)
+    rec = (128 + 4) * 4
+    assert ws > 0 and ws % (B * M * Hq * rec) == 0
+    splits = ws // (B * M * Hq * rec)
+    ntiles = T // 64
+    per = -(-ntiles // splits)
+    assert 1 <= splits <= ntiles and (splits - 1) * per < ntiles <= splits * per
+
+
+def test_verify_workspace_bytes_unsupported():
+    assert lynx.attn_verify_workspace_bytes(2, 4, 1024, 16, 2, 128, 256, 32) == 0
+    assert lynx.attn_verify_workspace_bytes(2, 4, 1000, 16, 2, 128, 256, 64) == 0
+    assert lynx.attn_verify_workspace_bytes(2, 0, 1024, 16, 2, 128, 256, 64) == 0
+    assert lynx.attn_verify_workspace_bytes(2, 4, 1024, 16, 2, 64, 256, 64) == 0
