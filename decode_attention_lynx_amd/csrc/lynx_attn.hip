@@ -16,9 +16,9 @@
 // a dense contraction over the raw nibble table values, which runs on MFMA.
 // Likewise sum_t p_t v_hat[t,d] = A_V[c,d] sum_t p_t L[n_td] + B_V[c,d] sum_t p_t.
 //
-// Decomposition: one workgroup (4 waves) per (sequence, kv head, context split);
+// Decomposition: one workgroup (8 waves) per (sequence, kv head, context split);
 // each wave walks 64-token tiles (one tile lies inside one chunk because the
-// chunk is a multiple of 64) with an online softmax, the 4 waves merge in LDS
+// chunk is a multiple of 64) with an online softmax, the 8 waves merge in LDS
 // and write one partial (m, l, o[128]) per query head; k_attn_combine merges the
 // splits with the log-sum-exp rule.
 //
@@ -42,7 +42,8 @@ namespace lynx {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kAttnWaves = 4;
+constexpr int kAttnWaves = 8;
+constexpr int kAttnWorkgroups = 256;   // workgroups the context splits aim for
 constexpr int kMaxGroup = 8;         // query heads per kv head handled by one workgroup
 
 struct AttnArgs {
@@ -186,8 +187,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   __shared__ float4 s_vab[kAttnWaves][kHeadDim / 2];
   uint32_t* s_pair = s_big;
 
+  static_assert(kPairWords % (kAttnWaves * 64) == 0, "the table fill covers the table exactly");
 #pragma unroll 8
-  for (int k = 0; k < 64; ++k) s_pair[k * 256 + tid] = a.pair[4 * k + (tid >> 6)];   // entry 4k + tid/64, copy tid%64
+  for (int w = tid; w < kPairWords; w += kAttnWaves * 64) s_pair[w] = a.pair[w >> 6];   // word 64e + r: entry e, copy r
   const uint32_t lane4 = 4u * (uint32_t)lane;
 
   // this lane's query slice (head hh, channels 32g .. 32g+31), kept as BF16 pairs
@@ -342,22 +344,23 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
     __builtin_amdgcn_wave_barrier();   // the next tile rewrites this wave's (A, B) tables
   };
 
-  // tiles t_begin + wave, +4, ...: two buffers in turn, the next tile's loads in flight
-  // while the current one is processed
-  TileIn<TILE> ta, tb;
+  // tiles t_begin + wave, + kAttnWaves, ...: two buffers in turn, the next tile's loads in
+  // flight while the current one is processed
+  TileIn<TILE> tb[2];
   int tile = t_begin + wave;
-  if (tile < t_end) load_tile(a, b, kvh, tile, toff, ta);
+  const int t_last = t_end - 1;    // loads past the wave's last tile re-read that tile (in bounds, unused)
+  load_tile(a, b, kvh, min(tile, t_last), toff, tb[0]);
+  load_tile(a, b, kvh, min(tile + kAttnWaves, t_last), toff, tb[1]);
   while (tile < t_end) {
-    if (tile + kAttnWaves < t_end) load_tile(a, b, kvh, tile + kAttnWaves, toff, tb);
-    process(ta);
-    tile += kAttnWaves;
-    if (tile >= t_end) break;
-    if (tile + kAttnWaves < t_end) load_tile(a, b, kvh, tile + kAttnWaves, toff, ta);
-    process(tb);
-    tile += kAttnWaves;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (tile < t_end) process(tb[i]);
+      load_tile(a, b, kvh, min(tile + 2 * kAttnWaves, t_last), toff, tb[i]);
+      tile += kAttnWaves;
+    }
   }
 
-  // ---- merge the 4 waves (columns 0..G-1 hold the result; 8..15 duplicate them)
+  // ---- merge the waves (columns 0..G-1 hold the result; 8..15 duplicate them)
   l_run = wave_sum_g(l_run);
   __syncthreads();                      // every wave is done with the pair table: reuse its LDS
   float (*s_m)[kMaxGroup] = reinterpret_cast<float (*)[kMaxGroup]>(s_big);
@@ -431,8 +434,10 @@ bool attn_plan(int batch, int ctx, int Hq, int Hkv, int D, int P, int C, AttnPla
   pl->tile = attn_tile(C);
   if (D != kHeadDim || pl->tile == 0 || Hq / Hkv > kMaxGroup) return false;
   pl->ntiles = ctx / pl->tile;
+  // One workgroup per compute unit of the 256-CU gfx950 parts (8 waves fill a CU at this
+  // kernel's register use): long-lived workgroups, one table fill and one merge each.
   const long long units = (long long)batch * Hkv;
-  int want = (int)((2048 + units - 1) / units);               // aim for ~2048 workgroups
+  int want = (int)((kAttnWorkgroups + units - 1) / units);
   want = std::max(1, std::min(want, pl->ntiles));
   pl->tiles_per_split = (pl->ntiles + want - 1) / want;
   pl->splits = (pl->ntiles + pl->tiles_per_split - 1) / pl->tiles_per_split;   // no empty split
