@@ -14,16 +14,21 @@
 // with L[n] the signed alpha-law value of the 8-bit full code n (anchor nibble |
 // residual nibble << 4) and c the chunk of token t.
 //
-// Decomposition: one workgroup (8 waves) per (sequence, kv head, block of 128 query
+// Decomposition: one workgroup (8 waves) per (sequence, kv head, block of 256 query
 // rows, context split); query row r = m*G + h (draft token m, query head h of the
-// group).  Per 64-token tile the workgroup first decodes the tile once into LDS:
-//   * keys as K_hat = A*L + B in float32, stored as BF16 high and low parts
-//     (K_hat ~ hi + lo to ~16 bits), row-major [token][channel];
+// group); each wave owns 32 rows as two MFMA column groups of 16.  The context is
+// walked in 64-token tiles (a tile lies inside one chunk, the chunk being a multiple
+// of 64).  Each tile is decoded once into LDS for all rows:
+//   * keys as K_hat * scale * log2(e) in float32, stored as BF16 high and low parts
+//     (K_hat ~ hi + lo to 16 bits), row-major [token][channel];
 //   * values as the raw table values L (float16), transposed [channel][token];
-// then each wave takes 16 query rows:
+// and the decode of tile i+1 runs in the same step as the products over tile i
+// (two LDS buffers, one barrier per tile), so the decode's vector work overlaps
+// the matrix work.  Per tile and wave:
 //   scores  S^T[token, row] = K_hi q + K_lo q on MFMA 16x16x32 bf16 (the BF16 query
-//           is exact in this format);
-//   online softmax in base 2 per row;
+//           is exact in this format); each key fragment read feeds both groups;
+//   online softmax in base 2 per row, the running maximum moved only when a tile
+//           raises it by more than 8 (probabilities stay below 2^8, exact in range);
 //   values  T^T[d, row] = sum_t L_V[d, t] p[t, row] on MFMA 16x16x32 f16, and
 //           O += A_V T + B_V sum(p) (the value map applied after the product).
 // Each wave writes a partial (m, l, o[128]) per row and split; k_verify_combine
@@ -42,15 +47,22 @@ namespace {
 
 typedef _Float16 vh8 __attribute__((ext_vector_type(8)));
 typedef __bf16 vb8 __attribute__((ext_vector_type(8)));
+typedef __bf16 vb2 __attribute__((ext_vector_type(2)));
+typedef _Float16 vh2 __attribute__((ext_vector_type(2)));
+typedef float vf2 __attribute__((ext_vector_type(2)));
 typedef float vf4 __attribute__((ext_vector_type(4)));
 typedef uint32_t vu4 __attribute__((ext_vector_type(4)));
 
 constexpr int kVWaves = 8;                 // waves per workgroup
 constexpr int kVThreads = kVWaves * 64;
-constexpr int kVRows = 16 * kVWaves;       // query rows per workgroup (16 per wave)
+constexpr int kVGroups = 2;                // MFMA column groups (16 rows each) per wave
+constexpr int kVRows = 16 * kVGroups * kVWaves;   // query rows per workgroup (256)
 constexpr int kVTile = 64;                 // context tokens per step
 constexpr int kLutCopies = 16;             // copies of each table entry (lane l reads copy l % 16)
 constexpr int kRec = kHeadDim + 4;         // floats per partial record (o 16-byte aligned)
+constexpr int kVWorkgroups = 256;          // workgroups the context splits aim for (one per CU)
+constexpr float kLazyMax = 8.0f;           // the running maximum moves only beyond this (base 2)
+constexpr float kF16Safe = 60000.0f;       // largest |value| stored as float16 (maximum 65504)
 
 struct VerifyArgs {
   const uint16_t* q;                       // [B][M][Hq][128] BF16
@@ -67,7 +79,6 @@ struct VerifyArgs {
   float qscale;                            // sm_scale * log2(e): scores kept in base 2
   int out_f32;
   float lut32[256];                        // S|x| of the full code n = anchor | residual << 4
-  uint16_t lut16[256];                     // the same, float16 (round to nearest even)
 };
 
 // Reductions over the 4 lane groups (l / 16) with the gfx950 lane-swap instructions.
@@ -84,49 +95,159 @@ __device__ __forceinline__ float group_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// BF16 of a float, round to nearest even (finite inputs)
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// BF16 pair (round to nearest even, one v_cvt_pk_bf16_f32) of two floats, lo = a
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  const vf2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, vb2));
 }
 
-// One tile's raw inputs for this thread.
-struct VerifyIn {
-  uint2 ka, kr;          // key codes: token t/8, channels 16*(t%8) .. +15
-  uint32_t va[2], vr[2]; // value codes: tokens 2*(t/16), +1; channels 8*(t%16) .. +7
-  float meta[4];         // threads < 256: gamma_min, gamma_scale, mu, sigma of one channel
+
+// One tile's raw codes for this thread.
+struct CodeIn {
+  uint2 ka, kr;          // key codes: token tid/8, channels 16*(tid%8) .. +15
+  uint32_t va[2], vr[2]; // value codes: tokens 2*(tid%32), +1; channels 8*(tid/32) .. +7
 };
 
-__device__ __forceinline__ void verify_load(const VerifyArgs& a, int b, int kvh, int tile, int tid, VerifyIn& in) {
+struct TileAddr {
+  size_t seg;     // segment index of the tile's page
+  size_t row0;    // byte offset of the tile's first code row of this kv head
+  int kc;         // chunk of the tile within its page
+};
+
+__device__ __forceinline__ TileAddr tile_addr(const VerifyArgs& a, int b, int kvh, int tile) {
   const int tok = tile * kVTile;
   const int page = tok / a.P;
   const int tin = tok - page * a.P;
-  const int kc = tin / a.C;
-  const size_t pg = (size_t)b * a.npages + page;
-  const size_t row0 = ((size_t)kvh * a.P + tin) * (kHeadDim / 2);
+  TileAddr t;
+  t.seg = (size_t)b * a.npages + page;
+  t.row0 = ((size_t)kvh * a.P + tin) * (kHeadDim / 2);
+  t.kc = tin / a.C;
+  return t;
+}
+
+__device__ __forceinline__ void load_codes(const VerifyArgs& a, int b, int kvh, int tile, int tid, CodeIn& in) {
+  const TileAddr ta = tile_addr(a, b, kvh, tile);
   {
-    const int t = tid >> 3, e8 = tid & 7;
-    const size_t off = row0 + (size_t)t * (kHeadDim / 2) + 8 * e8;
-    in.ka = *reinterpret_cast<const uint2*>(a.kanc + pg * a.anc_seg + off);
-    in.kr = *reinterpret_cast<const uint2*>(a.kres + pg * a.codes + off);
+    const size_t off = ta.row0 + (size_t)(tid >> 3) * (kHeadDim / 2) + 8 * (tid & 7);
+    in.ka = *reinterpret_cast<const uint2*>(a.kanc + ta.seg * a.anc_seg + off);
+    in.kr = *reinterpret_cast<const uint2*>(a.kres + ta.seg * a.codes + off);
   }
-  {
-    const int c8 = tid & 15, tq = tid >> 4;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const size_t off = row0 + (size_t)(2 * tq + r) * (kHeadDim / 2) + 4 * c8;
-      in.va[r] = *reinterpret_cast<const uint32_t*>(a.vanc + pg * a.anc_seg + off);
-      in.vr[r] = *reinterpret_cast<const uint32_t*>(a.vres + pg * a.codes + off);
+  for (int r = 0; r < 2; ++r) {
+    const size_t off = ta.row0 + (size_t)(2 * (tid & 31) + r) * (kHeadDim / 2) + 4 * (tid >> 5);
+    in.va[r] = *reinterpret_cast<const uint32_t*>(a.vanc + ta.seg * a.anc_seg + off);
+    in.vr[r] = *reinterpret_cast<const uint32_t*>(a.vres + ta.seg * a.codes + off);
+  }
+}
+
+// Threads 0..127 read the metadata of key channel tid, threads 128..255 of value channel
+// tid - 128: gamma_min, gamma_scale, mu and sigma of the tile's chunk.
+__device__ __forceinline__ float4 load_meta(const VerifyArgs& a, int b, int kvh, int tile, int tid) {
+  const TileAddr ta = tile_addr(a, b, kvh, tile);
+  const int c = tid & (kHeadDim - 1);
+  const uint8_t* seg = (tid < kHeadDim ? a.kanc : a.vanc) + ta.seg * a.anc_seg + a.codes;
+  const float* meta = reinterpret_cast<const float*>(seg) + kvh * kHeadDim + c;
+  return make_float4(meta[0], meta[a.H], meta[2 * (size_t)a.H + (size_t)ta.kc * a.H],
+                     meta[2 * (size_t)a.H + (size_t)(a.nck + ta.kc) * a.H]);
+}
+
+// (A, B) of one channel; the key map carries the softmax scale
+__device__ __forceinline__ float2 affine(float4 m, float scale) {
+  const float d1 = m.y + (float)kEps, d2 = m.w + (float)kEps;
+  return make_float2(d1 * d2 * scale, fmaf(m.z, d1, m.x) * scale);
+}
+
+struct alignas(16) VerifyLds {
+  float lut[256 * kLutCopies];             // float32 table, entry e copy c at e*16 + c
+  uint32_t kh[2][kVTile * 64];             // K_hat BF16 high parts, [token][channel pair], per buffer
+  uint32_t kl[2][kVTile * 64];             // K_hat BF16 low parts
+  uint32_t lv[2][kHeadDim * (kVTile / 2)]; // V_hat * 2^-E as float16, [channel][token pair]
+  float2 abk[2][kHeadDim];                 // (A_K, B_K) per channel, scaled, per buffer
+  float2 abv[2][kHeadDim];                 // (A_V, B_V) per channel, per buffer
+  int vexp[2][2];                          // per value-map wave: the exponent its channels need
+};
+
+// Smallest e >= 0 with (|A| + |B|) 2^-e <= kF16Safe: a bound on |V_hat| 2^-e over the chunk,
+// since |L| <= 1.
+__device__ __forceinline__ int value_exponent(float2 ab) {
+  const float bound = fabsf(ab.x) + fabsf(ab.y);
+  if (bound <= kF16Safe) return 0;
+  if (!(bound < INFINITY)) return 126;
+  int ex;
+  (void)frexpf(bound / kF16Safe, &ex);     // bound / kF16Safe <= 2^ex
+  return ex;
+}
+
+// Maps of one tile for the map threads (0..127 keys, 128..255 values), into slot `buf`.
+__device__ __forceinline__ void write_maps(VerifyLds& L, int buf, float4 meta, float qscale, int tid) {
+  if (tid < kHeadDim) {
+    L.abk[buf][tid] = affine(meta, qscale);
+  } else {
+    const float2 ab = affine(meta, 1.0f);
+    L.abv[buf][tid - kHeadDim] = ab;
+    int e = value_exponent(ab);
+    if (__builtin_amdgcn_ballot_w64(e > 0) != 0) {      // values beyond the float16 range: rare
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) e = max(e, __shfl_xor(e, m));
+    }
+    if ((tid & 63) == 0) L.vexp[buf][(tid >> 6) - 2] = e;
+  }
+}
+
+// Decode this thread's part of one tile into buffer `buf` (maps of slot `buf`); values are
+// scaled by 2^-E.
+__device__ __forceinline__ void decode_tile(VerifyLds& L, int buf, const CodeIn& in, int E, int tid, int lcopy) {
+  {
+    // keys: token t = tid/8, channels 16*(tid%8) + k, K_hat = A*L + B split into BF16 hi + lo;
+    // row t holds 16 columns of 16 B (8 channels each), column c16 at c16 ^ (t & 15)
+    const int t = tid >> 3, e8 = tid & 7;
+    const uint32_t aw[2] = {in.ka.x, in.ka.y}, rw[2] = {in.kr.x, in.kr.y};
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      // byte k of ev / od: full code of channel 2k / 2k+1 of this word
+      const uint32_t ev = (aw[w] & 0x0F0F0F0Fu) | ((rw[w] << 4) & 0xF0F0F0F0u);
+      const uint32_t od = ((aw[w] >> 4) & 0x0F0F0F0Fu) | (rw[w] & 0xF0F0F0F0u);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int ch = 16 * e8 + 8 * w + 2 * k;
+        const float2 ab0 = L.abk[buf][ch], ab1 = L.abk[buf][ch + 1];
+        const float x0 = fmaf(ab0.x, L.lut[((ev >> (8 * k)) & 0xFFu) * kLutCopies + lcopy], ab0.y);
+        const float x1 = fmaf(ab1.x, L.lut[((od >> (8 * k)) & 0xFFu) * kLutCopies + lcopy], ab1.y);
+        const uint32_t h = bf16x2(x0, x1);
+        hi[4 * w + k] = h;
+        lo[4 * w + k] = bf16x2(x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xFFFF0000u));
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c16 = (2 * e8 + h) ^ (t & 15);
+      *reinterpret_cast<uint4*>(&L.kh[buf][t * 64 + 4 * c16]) = make_uint4(hi[4 * h], hi[4 * h + 1], hi[4 * h + 2], hi[4 * h + 3]);
+      *reinterpret_cast<uint4*>(&L.kl[buf][t * 64 + 4 * c16]) = make_uint4(lo[4 * h], lo[4 * h + 1], lo[4 * h + 2], lo[4 * h + 3]);
     }
   }
-  if (tid < 2 * kHeadDim) {
-    const int c = tid & (kHeadDim - 1);
-    const uint8_t* seg = (tid < kHeadDim ? a.kanc : a.vanc) + pg * a.anc_seg + a.codes;
-    const float* meta = reinterpret_cast<const float*>(seg) + kvh * kHeadDim + c;
-    in.meta[0] = meta[0];
-    in.meta[1] = meta[a.H];
-    in.meta[2] = meta[2 * (size_t)a.H + (size_t)kc * a.H];
-    in.meta[3] = meta[2 * (size_t)a.H + (size_t)(a.nck + kc) * a.H];
+  {
+    // values: channels 8*(tid/32) + j, tokens 2*(tid%32), +1: V_hat = A*L + B (times 2^-E)
+    // as float16 pairs, transposed.  Row d holds 16 units of 8 B (4 tokens); unit u sits at
+    // u ^ (d & 15).  A wave's 64 lanes write 2 channels x 32 token pairs: at most 2 lanes
+    // per bank.
+    const int c8 = tid >> 5, tq = tid & 31;
+    const uint32_t ev0 = (in.va[0] & 0x0F0F0F0Fu) | ((in.vr[0] << 4) & 0xF0F0F0F0u);
+    const uint32_t od0 = ((in.va[0] >> 4) & 0x0F0F0F0Fu) | (in.vr[0] & 0xF0F0F0F0u);
+    const uint32_t ev1 = (in.va[1] & 0x0F0F0F0Fu) | ((in.vr[1] << 4) & 0xF0F0F0F0u);
+    const uint32_t od1 = ((in.va[1] >> 4) & 0x0F0F0F0Fu) | (in.vr[1] & 0xF0F0F0F0u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sh = 8 * (j >> 1);
+      const uint32_t i0 = (((j & 1) ? od0 : ev0) >> sh) & 0xFFu;
+      const uint32_t i1 = (((j & 1) ? od1 : ev1) >> sh) & 0xFFu;
+      const int d = 8 * c8 + j;
+      float2 ab = L.abv[buf][d];
+      if (E != 0) ab = make_float2(ldexpf(ab.x, -E), ldexpf(ab.y, -E));
+      const vf2 x = {fmaf(ab.x, L.lut[i0 * kLutCopies + lcopy], ab.y), fmaf(ab.x, L.lut[i1 * kLutCopies + lcopy], ab.y)};
+      const int unit = (tq >> 1) ^ (d & 15);
+      L.lv[buf][d * (kVTile / 2) + 2 * unit + (tq & 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, vh2));
+    }
   }
 }
 
@@ -139,192 +260,189 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
 
-  __shared__ float s_lut[256 * kLutCopies];          // float32 table, entry e copy c at e*16 + c
-  __shared__ uint16_t s_lut16[256 * kLutCopies];     // float16 table
-  __shared__ uint32_t s_kh[kVTile * 64];             // K_hat BF16 high parts, [token][channel pair]
-  __shared__ uint32_t s_kl[kVTile * 64];             // K_hat BF16 low parts
-  __shared__ uint32_t s_lv[kHeadDim * (kVTile / 2)]; // L_V float16, [channel][token pair]
-  __shared__ float2 s_abk[kHeadDim];                 // (A_K, B_K) per channel
-  __shared__ float2 s_abv[kHeadDim];                 // (A_V, B_V) per channel
+  __shared__ VerifyLds L;
 
-  for (int i = tid; i < 256 * kLutCopies; i += kVThreads) {
-    s_lut[i] = a.lut32[i / kLutCopies];
-    s_lut16[i] = a.lut16[i / kLutCopies];
-  }
+  for (int i = tid; i < 256 * kLutCopies; i += kVThreads) L.lut[i] = a.lut32[i / kLutCopies];
   const int lcopy = tid & (kLutCopies - 1);
 
-  // this lane's query row (column n of the wave's MFMA tiles) and its BF16 operand:
-  // channels 32kk + 8g .. +7 for k-step kk
-  const int row = rb * kVRows + wave * 16 + n;
-  const bool row_live = row < a.R;
-  vb8 qop[4];
-  {
-    const int m = row_live ? row / a.G : 0, hh = row_live ? row - (row / a.G) * a.G : 0;
+  // this wave's query rows: group gq of the wave, column n; BF16 operand channels 32kk + 8g .. +7
+  const int row_base = rb * kVRows + wave * (16 * kVGroups);
+  const bool wave_live = row_base < a.R;                  // wave-uniform
+  vb8 qop[kVGroups][4];
+#pragma unroll
+  for (int gq = 0; gq < kVGroups; ++gq) {
+    const int row = row_base + 16 * gq + n;
+    const bool live = row < a.R;
+    const int m = live ? row / a.G : 0, hh = live ? row - m * a.G : 0;
     const uint16_t* qp = a.q + ((size_t)(b * a.M + m) * a.Hq + kvh * a.G + hh) * kHeadDim + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       uint4 w = *reinterpret_cast<const uint4*>(qp + 32 * kk);
-      if (!row_live) w = make_uint4(0u, 0u, 0u, 0u);
+      if (!live) w = make_uint4(0u, 0u, 0u, 0u);
       const vu4 wv = {w.x, w.y, w.z, w.w};
-      qop[kk] = __builtin_bit_cast(vb8, wv);
+      qop[gq][kk] = __builtin_bit_cast(vb8, wv);
     }
   }
-  const float qscale = a.qscale;
 
-  float m_run = -INFINITY, l_run = 0.0f;
-  vf4 o_acc[8];
+  // Online softmax state per row (base 2).  The key products start from -m_run, so they
+  // yield s - m_run directly; m_run moves only when a tile exceeds it by more than
+  // kLazyMax.  o_acc is held in units of 2^E_acc (the values' range exponent).
+  float m_run[kVGroups], l_run[kVGroups];
+  vf4 cinit[kVGroups];
+  vf4 o_acc[kVGroups][8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) o_acc[j] = vf4{0.f, 0.f, 0.f, 0.f};
+  for (int gq = 0; gq < kVGroups; ++gq) {
+    m_run[gq] = -INFINITY;
+    l_run[gq] = 0.0f;
+    cinit[gq] = vf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o_acc[gq][j] = vf4{0.f, 0.f, 0.f, 0.f};
+  }
+  int E_acc = 0;
 
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min(a.ntiles, t_begin + a.tiles_per_split);
-  VerifyIn in;
-  if (t_begin < t_end) verify_load(a, b, kvh, t_begin, tid, in);
+  const int t_last = t_end - 1;         // loads past the split's end re-read its last tile (unused)
+  const int nt = t_end - t_begin;
 
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    __syncthreads();   // the previous tile's LDS tables are no longer read (and the lookup tables are filled)
+  // prologue: maps of tiles 0 and 1, codes of tiles 0 and 1, tile 0 decoded into buffer 0
+  const bool mapper = tid < 2 * kHeadDim;
+  float4 meta = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (mapper) {
+    write_maps(L, 0, load_meta(a, b, kvh, t_begin, tid), a.qscale, tid);
+    write_maps(L, 1, load_meta(a, b, kvh, min(t_begin + 1, t_last), tid), a.qscale, tid);
+    meta = load_meta(a, b, kvh, min(t_begin + 2, t_last), tid);
+  }
+  CodeIn cin;
+  load_codes(a, b, kvh, t_begin, tid, cin);
+  __syncthreads();                       // the table and the maps of tiles 0 and 1 are in LDS
+  int E_cur = max(L.vexp[0][0], L.vexp[0][1]);
+  decode_tile(L, 0, cin, E_cur, tid, lcopy);
+  load_codes(a, b, kvh, min(t_begin + 1, t_last), tid, cin);
 
-    // ---- the chunk's affine maps, one channel of K or V per thread
-    if (tid < 2 * kHeadDim) {
-      const float d1 = in.meta[1] + (float)kEps, d2 = in.meta[3] + (float)kEps;
-      const float2 ab = make_float2(d1 * d2, fmaf(in.meta[2], d1, in.meta[0]));
-      if (tid < kHeadDim) s_abk[tid] = ab;
-      else s_abv[tid - kHeadDim] = ab;
-    }
-    __syncthreads();
+  // step i (buffer par = i & 1): decode tile i+1 into the other buffer, products over tile i,
+  // maps of tile i+2 into slot par
+  auto step = [&](int i, int par) {
+    __syncthreads();   // buffer par is decoded; buffer 1-par and maps slot par are free
+    const int E_nxt = max(E_cur, max(L.vexp[1 - par][0], L.vexp[1 - par][1]));
+    decode_tile(L, 1 - par, cin, E_nxt, tid, lcopy);
+    load_codes(a, b, kvh, min(t_begin + i + 2, t_last), tid, cin);
 
-    // ---- decode the tile into LDS
-    {
-      // keys: token t = tid/8, channels 16*(tid%8) + k; K_hat = A*L + B, split into BF16 hi + lo
-      const int t = tid >> 3, e8 = tid & 7;
-      const uint32_t kw[2] = {in.ka.x, in.ka.y}, rw[2] = {in.kr.x, in.kr.y};
-      uint32_t hi[8], lo[8];
+    if (wave_live) {
+      if (E_cur > E_acc) {                       // rare: the values' range grew
 #pragma unroll
-      for (int w = 0; w < 2; ++w) {
+        for (int gq = 0; gq < kVGroups; ++gq)
 #pragma unroll
-        for (int k = 0; k < 8; k += 2) {
-          float kh[2];
+          for (int j = 0; j < 8; ++j) o_acc[gq][j] *= ldexpf(1.0f, E_acc - E_cur);
+        E_acc = E_cur;
+      }
+      // ---- scores minus m_run, S^T[token, row] of both groups: tokens 16mb + 4g + e, row n
+      float s[kVGroups][16];
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int sh = 4 * (k + e);
-            const uint32_t idx = ((kw[w] >> sh) & 0xFu) | (((rw[w] >> sh) & 0xFu) << 4);
-            const float2 ab = s_abk[16 * e8 + 8 * w + k + e];
-            kh[e] = fmaf(ab.x, s_lut[idx * kLutCopies + lcopy], ab.y);
+      for (int mb = 0; mb < 4; ++mb) {
+        vf4 acc[kVGroups];
+#pragma unroll
+        for (int gq = 0; gq < kVGroups; ++gq) acc[gq] = cinit[gq];
+        const int t = 16 * mb + n;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int c16 = (4 * kk + g) ^ n;          // (t & 15) == n
+          const uint4 wh = *reinterpret_cast<const uint4*>(&L.kh[par][t * 64 + 4 * c16]);
+          const uint4 wl = *reinterpret_cast<const uint4*>(&L.kl[par][t * 64 + 4 * c16]);
+          const vu4 vh = {wh.x, wh.y, wh.z, wh.w}, vl = {wl.x, wl.y, wl.z, wl.w};
+#pragma unroll
+          for (int gq = 0; gq < kVGroups; ++gq) {
+            acc[gq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(vb8, vh), qop[gq][kk], acc[gq], 0, 0, 0);
+            acc[gq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(vb8, vl), qop[gq][kk], acc[gq], 0, 0, 0);
           }
-          const uint32_t h0 = bf16_bits(kh[0]), h1 = bf16_bits(kh[1]);
-          const uint32_t l0 = bf16_bits(kh[0] - __uint_as_float(h0 << 16));
-          const uint32_t l1 = bf16_bits(kh[1] - __uint_as_float(h1 << 16));
-          hi[4 * w + k / 2] = h0 | (h1 << 16);
-          lo[4 * w + k / 2] = l0 | (l1 << 16);
         }
-      }
-      // row t holds 64 channel pairs = 16 columns of 16 B; column c16 at c16 ^ (t & 15)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c16 = (2 * e8 + h) ^ (t & 15);
-        *reinterpret_cast<uint4*>(&s_kh[t * 64 + 4 * c16]) = make_uint4(hi[4 * h], hi[4 * h + 1], hi[4 * h + 2], hi[4 * h + 3]);
-        *reinterpret_cast<uint4*>(&s_kl[t * 64 + 4 * c16]) = make_uint4(lo[4 * h], lo[4 * h + 1], lo[4 * h + 2], lo[4 * h + 3]);
-      }
-    }
-    {
-      // values: channels 8*(tid%16) + j, tokens 2*(tid/16), +1; L as float16 pairs, transposed.
-      // Row d holds 16 units of 8 B (4 tokens each); unit u at u ^ (d & 15).
-      const int c8 = tid & 15, tq = tid >> 4;
+        for (int gq = 0; gq < kVGroups; ++gq)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t i0 = ((in.va[0] >> (4 * j)) & 0xFu) | (((in.vr[0] >> (4 * j)) & 0xFu) << 4);
-        const uint32_t i1 = ((in.va[1] >> (4 * j)) & 0xFu) | (((in.vr[1] >> (4 * j)) & 0xFu) << 4);
-        const uint32_t v = (uint32_t)s_lut16[i0 * kLutCopies + lcopy] | ((uint32_t)s_lut16[i1 * kLutCopies + lcopy] << 16);
-        const int d = 8 * c8 + j;
-        const int unit = (tq >> 1) ^ (d & 15);
-        s_lv[d * (kVTile / 2) + 2 * unit + (tq & 1)] = v;
+          for (int e = 0; e < 4; ++e) s[gq][4 * mb + e] = acc[gq][e];
+        __builtin_amdgcn_sched_barrier(0);   // bound the key fragments held in registers
       }
-    }
-    // the next tile's raw inputs are loaded while this one is used
-    if (tile + 1 < t_end) verify_load(a, b, kvh, tile + 1, tid, in);
-    __syncthreads();
 
-    // ---- scores for this wave's 16 rows: S^T[token, row], tokens 16mb + 4g + i
-    float s[16];
+      // ---- online softmax: p = 2^(s - m_run), the maximum moved (and o, l rescaled) only
+      //      where the tile exceeds it by more than kLazyMax, so p < 2^kLazyMax
+      vh8 pt[kVGroups][2];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      vf4 acc = vf4{0.f, 0.f, 0.f, 0.f};
-      const int t = 16 * mb + n;
+      for (int gq = 0; gq < kVGroups; ++gq) {
+        float mt = s[gq][0];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int c16 = (4 * kk + g) ^ n;          // (t & 15) == n
-        const uint4 wh = *reinterpret_cast<const uint4*>(&s_kh[t * 64 + 4 * c16]);
-        const uint4 wl = *reinterpret_cast<const uint4*>(&s_kl[t * 64 + 4 * c16]);
-        const vu4 vh = {wh.x, wh.y, wh.z, wh.w}, vl = {wl.x, wl.y, wl.z, wl.w};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(vb8, vh), qop[kk], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(vb8, vl), qop[kk], acc, 0, 0, 0);
+        for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[gq][e]);
+        mt = group_max(mt);                               // tile maximum minus m_run (or itself)
+        const float base = m_run[gq] == -INFINITY ? 0.0f : m_run[gq];
+        const bool up = mt + base > m_run[gq] + kLazyMax;
+        const float sub = up ? mt : 0.0f;                 // where the maximum moves
+        if (__builtin_amdgcn_ballot_w64(up) != 0) {
+          const float corr = up ? __builtin_amdgcn_exp2f(m_run[gq] - (mt + base)) : 1.0f;
+          if (up) {
+            m_run[gq] = mt + base;
+            cinit[gq] = vf4{-m_run[gq], -m_run[gq], -m_run[gq], -m_run[gq]};
+          }
+          l_run[gq] *= corr;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o_acc[gq][j] *= corr;
+        }
+        float lsum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = __builtin_amdgcn_exp2f(s[gq][e] - sub);
+          lsum += p;
+          pt[gq][e >> 3][e & 7] = (_Float16)p;
+        }
+        l_run[gq] += lsum;
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[4 * mb + i] = acc[i] * qscale;
-    }
 
-    // ---- online softmax (base 2) for row n over the tile's 64 tokens
-    float mt = s[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, s[i]);
-    mt = group_max(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-    float lsum = 0.0f;
-    vh8 pt[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(s[i] - m_new);
-      lsum += p;
-      pt[i >> 3][i & 7] = (_Float16)p;
-    }
-    l_run = fmaf(l_run, corr, lsum);
-    if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o_acc[j] *= corr;
-    }
-    m_run = m_new;
-    const float lt = group_sum(lsum);
-
-    // ---- values: T^T[d, row] = sum_t L_V[d, t] p[t, row], d = 16j + 4g + i of the output block j.
-    // The k index of step ks runs over tokens 32ks + 4g + 0..3 then 32ks + 16 + 4g + 0..3 (the
-    // layout of the probabilities in pt[ks]); the table values are read in the same order.
-    vf4 tacc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tacc[j] = vf4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+      // ---- values: O^T[d, row] += sum_t V_hat[d, t] p[t, row], d = 16j + 4g + e of block j.
+      // The k index of step ks runs over tokens 32ks + 4g + 0..3 then 32ks + 16 + 4g + 0..3
+      // (the layout of the probabilities); the values are read in the same order.
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int d = 16 * j + n;
-        const int u0 = (8 * ks + g) ^ (d & 15), u1 = (8 * ks + 4 + g) ^ (d & 15);
-        const uint2 w0 = *reinterpret_cast<const uint2*>(&s_lv[d * (kVTile / 2) + 2 * u0]);
-        const uint2 w1 = *reinterpret_cast<const uint2*>(&s_lv[d * (kVTile / 2) + 2 * u1]);
-        const vu4 va4 = {w0.x, w0.y, w1.x, w1.y};
-        tacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(vh8, va4), pt[ks], tacc[j], 0, 0, 0);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int u0 = (8 * ks + g) ^ n, u1 = (8 * ks + 4 + g) ^ n;     // (d & 15) == n
+          const uint2 w0 = *reinterpret_cast<const uint2*>(&L.lv[par][d * (kVTile / 2) + 2 * u0]);
+          const uint2 w1 = *reinterpret_cast<const uint2*>(&L.lv[par][d * (kVTile / 2) + 2 * u1]);
+          const vu4 va4 = {w0.x, w0.y, w1.x, w1.y};
+#pragma unroll
+          for (int gq = 0; gq < kVGroups; ++gq)
+            o_acc[gq][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(vh8, va4), pt[gq][ks], o_acc[gq][j], 0, 0, 0);
+        }
       }
     }
-    // ---- undo the value map: o += A_V * T + B_V * sum(p)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float4 ab01 = *reinterpret_cast<const float4*>(&s_abv[16 * j + 4 * g]);
-      const float4 ab23 = *reinterpret_cast<const float4*>(&s_abv[16 * j + 4 * g + 2]);
-      o_acc[j][0] = fmaf(ab01.x, tacc[j][0], fmaf(ab01.y, lt, o_acc[j][0]));
-      o_acc[j][1] = fmaf(ab01.z, tacc[j][1], fmaf(ab01.w, lt, o_acc[j][1]));
-      o_acc[j][2] = fmaf(ab23.x, tacc[j][2], fmaf(ab23.y, lt, o_acc[j][2]));
-      o_acc[j][3] = fmaf(ab23.z, tacc[j][3], fmaf(ab23.w, lt, o_acc[j][3]));
+
+    // ---- maps of tile i+2 into slot par (read by the decode in step i+1)
+    if (mapper) {
+      write_maps(L, par, meta, a.qscale, tid);
+      meta = load_meta(a, b, kvh, min(t_begin + i + 3, t_last), tid);
     }
+    E_cur = E_nxt;
+  };
+
+  for (int i = 0; i < nt; i += 2) {
+    step(i, 0);
+    if (i + 1 < nt) step(i + 1, 1);
   }
 
-  // ---- this split's partial record for the lane's row: (m, l, o[d]) with d = 16j + 4g + i
-  l_run = group_sum(l_run);
-  if (row_live) {
-    const int m = row / a.G, hh = row - m * a.G;
-    float* rec = a.ws + ((size_t)((b * a.M + m) * a.Hq + kvh * a.G + hh) * a.splits + split) * kRec;
-    if (g == 0) *reinterpret_cast<float4*>(rec) = make_float4(m_run, l_run, 0.0f, 0.0f);
+  // ---- this split's partial records for the lane's rows: (m, l, o[d]) with d = 16j + 4g + e
+  const float oscale = ldexpf(1.0f, E_acc);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<float4*>(rec + 4 + 16 * j + 4 * g) = make_float4(o_acc[j][0], o_acc[j][1], o_acc[j][2], o_acc[j][3]);
+  for (int gq = 0; gq < kVGroups; ++gq) {
+    const float l = group_sum(l_run[gq]);
+    const int row = row_base + 16 * gq + n;
+    if (row < a.R) {
+      const int m = row / a.G, hh = row - m * a.G;
+      float* rec = a.ws + ((size_t)((b * a.M + m) * a.Hq + kvh * a.G + hh) * a.splits + split) * kRec;
+      if (g == 0) *reinterpret_cast<float4*>(rec) = make_float4(m_run[gq], l, 0.0f, 0.0f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<float4*>(rec + 4 + 16 * j + 4 * g) =
+            make_float4(o_acc[gq][j][0] * oscale, o_acc[gq][j][1] * oscale, o_acc[gq][j][2] * oscale,
+                        o_acc[gq][j][3] * oscale);
+    }
   }
 }
 
@@ -369,7 +487,7 @@ bool verify_plan(int batch, int n_query, int ctx, int Hq, int Hkv, int D, int P,
   pl->rowblocks = (int)((R + kVRows - 1) / kVRows);
   pl->ntiles = ctx / kVTile;
   const long long units = (long long)batch * Hkv * pl->rowblocks;
-  int want = (int)((1024 + units - 1) / units);               // aim for ~1024 workgroups
+  int want = (int)((kVWorkgroups + units - 1) / units);
   want = std::max(1, std::min(want, pl->ntiles));
   pl->tiles_per_split = (pl->ntiles + want - 1) / want;
   pl->splits = (pl->ntiles + pl->tiles_per_split - 1) / pl->tiles_per_split;
@@ -450,8 +568,6 @@ int verify_launch(const void* q_dev, const void* k_anchor_dev, const void* k_res
     const int I = 16 * vmag + 7 - vres;
     const double v = S * std::expm1((double)I / kCodeMax * L) / al;
     a.lut32[idx] = (float)v;
-    const _Float16 h = (_Float16)v;
-    a.lut16[idx] = __builtin_bit_cast(uint16_t, h);
   }
   void* kargs[] = {&a};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&k_verify),
