@@ -140,21 +140,29 @@ __device__ __forceinline__ void load_codes(const VerifyArgs& a, int b, int kvh, 
   }
 }
 
-// Threads 0..127 read the metadata of key channel tid, threads 128..255 of value channel
-// tid - 128: gamma_min, gamma_scale, mu and sigma of the tile's chunk.
-__device__ __forceinline__ float4 load_meta(const VerifyArgs& a, int b, int kvh, int tile, int tid) {
+// gamma_min, gamma_scale, mu and sigma of channels 2l, 2l+1 of the tile's chunk, for lane l
+// of wave 0 (keys) or wave 1 (values)
+struct MetaIn {
+  float2 gmin, gscale, mu, sigma;
+};
+
+__device__ __forceinline__ MetaIn load_meta(const VerifyArgs& a, int b, int kvh, int tile, int tid) {
   const TileAddr ta = tile_addr(a, b, kvh, tile);
-  const int c = tid & (kHeadDim - 1);
-  const uint8_t* seg = (tid < kHeadDim ? a.kanc : a.vanc) + ta.seg * a.anc_seg + a.codes;
+  const int c = 2 * (tid & 63);
+  const uint8_t* seg = (tid < 64 ? a.kanc : a.vanc) + ta.seg * a.anc_seg + a.codes;
   const float* meta = reinterpret_cast<const float*>(seg) + kvh * kHeadDim + c;
-  return make_float4(meta[0], meta[a.H], meta[2 * (size_t)a.H + (size_t)ta.kc * a.H],
-                     meta[2 * (size_t)a.H + (size_t)(a.nck + ta.kc) * a.H]);
+  MetaIn m;
+  m.gmin = *reinterpret_cast<const float2*>(meta);
+  m.gscale = *reinterpret_cast<const float2*>(meta + a.H);
+  m.mu = *reinterpret_cast<const float2*>(meta + 2 * (size_t)a.H + (size_t)ta.kc * a.H);
+  m.sigma = *reinterpret_cast<const float2*>(meta + 2 * (size_t)a.H + (size_t)(a.nck + ta.kc) * a.H);
+  return m;
 }
 
 // (A, B) of one channel; the key map carries the softmax scale
-__device__ __forceinline__ float2 affine(float4 m, float scale) {
-  const float d1 = m.y + (float)kEps, d2 = m.w + (float)kEps;
-  return make_float2(d1 * d2 * scale, fmaf(m.z, d1, m.x) * scale);
+__device__ __forceinline__ float2 affine(float gmin, float gscale, float mu, float sigma, float scale) {
+  const float d1 = gscale + (float)kEps, d2 = sigma + (float)kEps;
+  return make_float2(d1 * d2 * scale, fmaf(mu, d1, gmin) * scale);
 }
 
 struct alignas(16) VerifyLds {
@@ -162,9 +170,9 @@ struct alignas(16) VerifyLds {
   uint32_t kh[2][kVTile * 64];             // K_hat BF16 high parts, [token][channel pair], per buffer
   uint32_t kl[2][kVTile * 64];             // K_hat BF16 low parts
   uint32_t lv[2][kHeadDim * (kVTile / 2)]; // V_hat * 2^-E as float16, [channel][token pair]
-  float2 abk[2][kHeadDim];                 // (A_K, B_K) per channel, scaled, per buffer
-  float2 abv[2][kHeadDim];                 // (A_V, B_V) per channel, per buffer
-  int vexp[2][2];                          // per value-map wave: the exponent its channels need
+  float2 abk[2][kHeadDim + kHeadDim / 16]; // (A_K, B_K) of channel c at c + c/16, scaled, per buffer
+  float2 abv[2][kHeadDim];                 // (A_V, B_V) 2^-E per channel, per buffer
+  int vexp[2];                             // E of the tile in each slot
 };
 
 // Smallest e >= 0 with (|A| + |B|) 2^-e <= kF16Safe: a bound on |V_hat| 2^-e over the chunk,
@@ -178,25 +186,36 @@ __device__ __forceinline__ int value_exponent(float2 ab) {
   return ex;
 }
 
-// Maps of one tile for the map threads (0..127 keys, 128..255 values), into slot `buf`.
-__device__ __forceinline__ void write_maps(VerifyLds& L, int buf, float4 meta, float qscale, int tid) {
-  if (tid < kHeadDim) {
-    L.abk[buf][tid] = affine(meta, qscale);
+// Maps of one tile into slot `buf`: wave 0 writes the key maps of channels 2l, 2l+1, wave 1
+// the value maps, scaled by 2^-E with E the running maximum of the tiles' range exponents
+// (held in E_map by wave 1).
+__device__ __forceinline__ void write_maps(VerifyLds& L, int buf, const MetaIn& m, float qscale, int tid,
+                                           int& E_map) {
+  const int l = tid & 63;
+  if (tid < 64) {
+    const int c = 2 * l + (l >> 3);       // channel 2l at 2l + 2l/16
+    L.abk[buf][c] = affine(m.gmin.x, m.gscale.x, m.mu.x, m.sigma.x, qscale);
+    L.abk[buf][c + 1] = affine(m.gmin.y, m.gscale.y, m.mu.y, m.sigma.y, qscale);
   } else {
-    const float2 ab = affine(meta, 1.0f);
-    L.abv[buf][tid - kHeadDim] = ab;
-    int e = value_exponent(ab);
-    if (__builtin_amdgcn_ballot_w64(e > 0) != 0) {      // values beyond the float16 range: rare
+    float2 ab0 = affine(m.gmin.x, m.gscale.x, m.mu.x, m.sigma.x, 1.0f);
+    float2 ab1 = affine(m.gmin.y, m.gscale.y, m.mu.y, m.sigma.y, 1.0f);
+    int e = max(value_exponent(ab0), value_exponent(ab1));
+    if (__builtin_amdgcn_ballot_w64(e > E_map) != 0) {   // values beyond the range so far: rare
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) e = max(e, __shfl_xor(e, m));
+      for (int sh = 32; sh >= 1; sh >>= 1) e = max(e, __shfl_xor(e, sh));
+      E_map = max(E_map, e);
     }
-    if ((tid & 63) == 0) L.vexp[buf][(tid >> 6) - 2] = e;
+    if (E_map != 0) {
+      ab0 = make_float2(ldexpf(ab0.x, -E_map), ldexpf(ab0.y, -E_map));
+      ab1 = make_float2(ldexpf(ab1.x, -E_map), ldexpf(ab1.y, -E_map));
+    }
+    *reinterpret_cast<float4*>(&L.abv[buf][2 * l]) = make_float4(ab0.x, ab0.y, ab1.x, ab1.y);
+    if (l == 0) L.vexp[buf] = E_map;
   }
 }
 
-// Decode this thread's part of one tile into buffer `buf` (maps of slot `buf`); values are
-// scaled by 2^-E.
-__device__ __forceinline__ void decode_tile(VerifyLds& L, int buf, const CodeIn& in, int E, int tid, int lcopy) {
+// Decode this thread's part of one tile into buffer `buf` (maps of slot `buf`).
+__device__ __forceinline__ void decode_tile(VerifyLds& L, int buf, const CodeIn& in, int tid, int lcopy) {
   {
     // keys: token t = tid/8, channels 16*(tid%8) + k, K_hat = A*L + B split into BF16 hi + lo;
     // row t holds 16 columns of 16 B (8 channels each), column c16 at c16 ^ (t & 15)
@@ -211,7 +230,8 @@ __device__ __forceinline__ void decode_tile(VerifyLds& L, int buf, const CodeIn&
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int ch = 16 * e8 + 8 * w + 2 * k;
-        const float2 ab0 = L.abk[buf][ch], ab1 = L.abk[buf][ch + 1];
+        // the 8 threads of a token read 8 channels 16 apart: the padding puts them in 8 banks
+        const float2 ab0 = L.abk[buf][ch + e8], ab1 = L.abk[buf][ch + 1 + e8];
         const float x0 = fmaf(ab0.x, L.lut[((ev >> (8 * k)) & 0xFFu) * kLutCopies + lcopy], ab0.y);
         const float x1 = fmaf(ab1.x, L.lut[((od >> (8 * k)) & 0xFFu) * kLutCopies + lcopy], ab1.y);
         const uint32_t h = bf16x2(x0, x1);
@@ -242,8 +262,7 @@ __device__ __forceinline__ void decode_tile(VerifyLds& L, int buf, const CodeIn&
       const uint32_t i0 = (((j & 1) ? od0 : ev0) >> sh) & 0xFFu;
       const uint32_t i1 = (((j & 1) ? od1 : ev1) >> sh) & 0xFFu;
       const int d = 8 * c8 + j;
-      float2 ab = L.abv[buf][d];
-      if (E != 0) ab = make_float2(ldexpf(ab.x, -E), ldexpf(ab.y, -E));
+      const float2 ab = L.abv[buf][d];
       const vf2 x = {fmaf(ab.x, L.lut[i0 * kLutCopies + lcopy], ab.y), fmaf(ab.x, L.lut[i1 * kLutCopies + lcopy], ab.y)};
       const int unit = (tq >> 1) ^ (d & 15);
       L.lv[buf][d * (kVTile / 2) + 2 * unit + (tq & 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, vh2));
@@ -306,36 +325,29 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
   const int nt = t_end - t_begin;
 
   // prologue: maps of tiles 0 and 1, codes of tiles 0 and 1, tile 0 decoded into buffer 0
-  const bool mapper = tid < 2 * kHeadDim;
-  float4 meta = make_float4(0.f, 0.f, 0.f, 0.f);
+  const bool mapper = wave < 2;          // wave-uniform
+  MetaIn meta;
+  int E_map = 0;
   if (mapper) {
-    write_maps(L, 0, load_meta(a, b, kvh, t_begin, tid), a.qscale, tid);
-    write_maps(L, 1, load_meta(a, b, kvh, min(t_begin + 1, t_last), tid), a.qscale, tid);
+    write_maps(L, 0, load_meta(a, b, kvh, t_begin, tid), a.qscale, tid, E_map);
+    write_maps(L, 1, load_meta(a, b, kvh, min(t_begin + 1, t_last), tid), a.qscale, tid, E_map);
     meta = load_meta(a, b, kvh, min(t_begin + 2, t_last), tid);
   }
   CodeIn cin;
   load_codes(a, b, kvh, t_begin, tid, cin);
   __syncthreads();                       // the table and the maps of tiles 0 and 1 are in LDS
-  int E_cur = max(L.vexp[0][0], L.vexp[0][1]);
-  decode_tile(L, 0, cin, E_cur, tid, lcopy);
+  E_acc = L.vexp[0];
+  decode_tile(L, 0, cin, tid, lcopy);
   load_codes(a, b, kvh, min(t_begin + 1, t_last), tid, cin);
 
   // step i (buffer par = i & 1): decode tile i+1 into the other buffer, products over tile i,
   // maps of tile i+2 into slot par
   auto step = [&](int i, int par) {
     __syncthreads();   // buffer par is decoded; buffer 1-par and maps slot par are free
-    const int E_nxt = max(E_cur, max(L.vexp[1 - par][0], L.vexp[1 - par][1]));
-    decode_tile(L, 1 - par, cin, E_nxt, tid, lcopy);
+    decode_tile(L, 1 - par, cin, tid, lcopy);
     load_codes(a, b, kvh, min(t_begin + i + 2, t_last), tid, cin);
 
     if (wave_live) {
-      if (E_cur > E_acc) {                       // rare: the values' range grew
-#pragma unroll
-        for (int gq = 0; gq < kVGroups; ++gq)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) o_acc[gq][j] *= ldexpf(1.0f, E_acc - E_cur);
-        E_acc = E_cur;
-      }
       // ---- scores minus m_run, S^T[token, row] of both groups: tokens 16mb + 4g + e, row n
       float s[kVGroups][16];
 #pragma unroll
@@ -414,12 +426,20 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
       }
     }
 
+    // ---- o in the units of tile i+1 (rare: the values' range grew)
+    const int E_nxt = L.vexp[1 - par];
+    if (E_nxt > E_acc) {
+#pragma unroll
+      for (int gq = 0; gq < kVGroups; ++gq)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o_acc[gq][j] *= ldexpf(1.0f, E_acc - E_nxt);
+      E_acc = E_nxt;
+    }
     // ---- maps of tile i+2 into slot par (read by the decode in step i+1)
     if (mapper) {
-      write_maps(L, par, meta, a.qscale, tid);
+      write_maps(L, par, meta, a.qscale, tid, E_map);
       meta = load_meta(a, b, kvh, min(t_begin + i + 3, t_last), tid);
     }
-    E_cur = E_nxt;
   };
 
   for (int i = 0; i < nt; i += 2) {

@@ -117,6 +117,29 @@ def test_verify_without_lse_and_sm_scale(gpu):
           "sm_scale")
 
 
+def test_verify_values_beyond_float16_range(gpu):
+    """Values the kernel cannot hold as float16 (|V| up to ~2*10^6 from token 1088 on) take its
+    power-of-two range exponent.  With 8 sequences of 32 one-tile pages the context splits hold
+    2 tiles each, so the exponent grows inside a split (tiles 16 -> 17); the bar is unchanged."""
+    B, M, Hq, Hkv, T, P, C, alpha = 8, 4, 16, 2, 2048, 64, 64, 255.0
+    kb = np.concatenate([synth.make_kv_np(T, Hkv, 128, seed=21, layer=b, kv_idx=0) for b in range(B)])
+    vf = np.concatenate([o.bf16_bits_to_f64(synth.make_kv_np(T, Hkv, 128, seed=21, layer=b, kv_idx=1))
+                         for b in range(B)]).reshape(B, T, Hkv, 128)
+    vf[:, 17 * 64:] *= 4096.0                  # a power of two: the BF16 values stay exact
+    assert np.abs(vf).max() > 65504.0
+    vb = o.f64_to_bf16_bits(vf.reshape(B * T, Hkv, 128))
+    ka, kr, _ = o.encode(kb, P, C, alpha)
+    va, vr, _ = o.encode(vb, P, C, alpha)
+    qb = synth.make_q_np(B * M, Hq, 128, seed=21).reshape(B, M, Hq, 128)
+    ref_o, ref_lse = o.attention_verify(qb, ka, kr, va, vr, B, M, T, Hq, Hkv, 128, P, C, alpha)
+    out, lse = lynx.attn_verify(bf16_tensor(qb), upload(ka), upload(kr), upload(va), upload(vr), T, Hkv, P, C,
+                                alpha)
+    torch.cuda.synchronize()
+    bound = lse_bound(qb, ka, kr, B, M, T, Hq, Hkv, P, C, alpha)
+    check(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_lse, bound,
+          "range")
+
+
 def test_verify_lse_merges_context_halves(gpu):
     """The LSE returned for two halves of a context merges to the whole (the rule a caller uses to
     add the draft tokens' own keys): O = (e^{l1} O1 + e^{l2} O2) / (e^{l1} + e^{l2})."""
