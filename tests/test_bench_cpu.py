@@ -22,6 +22,7 @@ def kernel_rows(counter, per_kernel):
 
 
 def test_counter_summary_calibrates_against_the_copy(tmp_path):
+    assert bench.C % 64 == 0          # the names below are those of the 64-token attention tile
     enc_grid = bench.OP_KERNELS["encode"][0][1]
     gib_kib = (1 << 30) / 1024
     fetch = {("hbm_probe::k_probe_copy(unsigned int const*)", 2097152): [gib_kib / 2] * 3,
@@ -29,8 +30,10 @@ def test_counter_summary_calibrates_against_the_copy(tmp_path):
              (f"void lynx::k_encode<{bench.C}>(lynx::EncodeArgs)", enc_grid // 2): [7.0],   # setup encode, ignored
              ("void lynx::k_decode<false, false>(lynx::DecodeArgs)", 524288): [10.0],
              ("void lynx::k_decode<true, false>(lynx::DecodeArgs)", 524288): [20.0],
-             ("lynx::k_attn_anchor(lynx::AttnArgs)", 4096): [30.0],
-             ("lynx::k_attn_combine(lynx::AttnArgs)", 131072): [1.0]}
+             ("void lynx::k_attn_anchor<64>(lynx::AttnArgs)", 4096): [30.0],
+             ("lynx::k_attn_combine(lynx::AttnArgs)", 131072): [1.0],
+             ("lynx::k_verify(lynx::(anonymous namespace)::VerifyArgs)", 131072): [40.0],
+             ("lynx::k_verify_combine(lynx::(anonymous namespace)::VerifyArgs)", 8388608): [2.0]}
     write = {k: [v[0] * 2 for _ in v] for k, v in fetch.items()}
     fields = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
     fp, wp, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "t.json"
@@ -42,6 +45,7 @@ def test_counter_summary_calibrates_against_the_copy(tmp_path):
     assert abs(rec["calibration"]["write_factor"] - 1.0) < 1e-9
     assert rec["encode"]["bytes_per_launch"] == round(1001.0 * 1024 * 2 + 2000.0 * 1024 * 1)
     assert rec["attn_anchor"]["bytes_per_launch"] == round(31.0 * 1024 * 2 + 62.0 * 1024)
+    assert rec["attn_verify"]["bytes_per_launch"] == round(42.0 * 1024 * 2 + 84.0 * 1024)
     assert rec["copy"]["bytes_per_launch"] == 2 << 30
     assert rec["encode"]["source_hash"] == bench.kernel_hash()
     assert "encode" in text and "calibration" in text
