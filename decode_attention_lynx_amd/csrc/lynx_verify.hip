@@ -140,22 +140,27 @@ __device__ __forceinline__ void load_codes(const VerifyArgs& a, int b, int kvh, 
   }
 }
 
-// gamma_min, gamma_scale, mu and sigma of channels 2l, 2l+1 of the tile's chunk, for lane l
-// of wave 0 (keys) or wave 1 (values)
+// gamma_min, gamma_scale, mu and sigma of channels 2l, 2l+1 of the tile's CPT chunks, for
+// lane l of wave 0 (keys) or wave 1 (values)
+template <int CPT>
 struct MetaIn {
-  float2 gmin, gscale, mu, sigma;
+  float2 gmin, gscale, mu[CPT], sigma[CPT];
 };
 
-__device__ __forceinline__ MetaIn load_meta(const VerifyArgs& a, int b, int kvh, int tile, int tid) {
+template <int CPT>
+__device__ __forceinline__ MetaIn<CPT> load_meta(const VerifyArgs& a, int b, int kvh, int tile, int tid) {
   const TileAddr ta = tile_addr(a, b, kvh, tile);
   const int c = 2 * (tid & 63);
   const uint8_t* seg = (tid < 64 ? a.kanc : a.vanc) + ta.seg * a.anc_seg + a.codes;
   const float* meta = reinterpret_cast<const float*>(seg) + kvh * kHeadDim + c;
-  MetaIn m;
+  MetaIn<CPT> m;
   m.gmin = *reinterpret_cast<const float2*>(meta);
   m.gscale = *reinterpret_cast<const float2*>(meta + a.H);
-  m.mu = *reinterpret_cast<const float2*>(meta + 2 * (size_t)a.H + (size_t)ta.kc * a.H);
-  m.sigma = *reinterpret_cast<const float2*>(meta + 2 * (size_t)a.H + (size_t)(a.nck + ta.kc) * a.H);
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    m.mu[k] = *reinterpret_cast<const float2*>(meta + 2 * (size_t)a.H + (size_t)(ta.kc + k) * a.H);
+    m.sigma[k] = *reinterpret_cast<const float2*>(meta + 2 * (size_t)a.H + (size_t)(a.nck + ta.kc + k) * a.H);
+  }
   return m;
 }
 
@@ -165,13 +170,15 @@ __device__ __forceinline__ float2 affine(float gmin, float gscale, float mu, flo
   return make_float2(d1 * d2 * scale, fmaf(mu, d1, gmin) * scale);
 }
 
+// CPT = chunks per 64-token tile (1 for a chunk of 64 or more, 2 for a chunk of 32)
+template <int CPT>
 struct alignas(16) VerifyLds {
   float lut[256 * kLutCopies];             // float32 table, entry e copy c at e*16 + c
   uint32_t kh[2][kVTile * 64];             // K_hat BF16 high parts, [token][channel pair], per buffer
   uint32_t kl[2][kVTile * 64];             // K_hat BF16 low parts
   uint32_t lv[2][kHeadDim * (kVTile / 2)]; // V_hat * 2^-E as float16, [channel][token pair]
-  float2 abk[2][kHeadDim + kHeadDim / 16]; // (A_K, B_K) of channel c at c + c/16, scaled, per buffer
-  float2 abv[2][kHeadDim];                 // (A_V, B_V) 2^-E per channel, per buffer
+  float2 abk[2][CPT][kHeadDim + kHeadDim / 16];  // (A_K, B_K) of channel c at c + c/16, scaled
+  float2 abv[2][CPT][kHeadDim];            // (A_V, B_V) 2^-E per channel
   int vexp[2];                             // E of the tile in each slot
 };
 
@@ -189,37 +196,52 @@ __device__ __forceinline__ int value_exponent(float2 ab) {
 // Maps of one tile into slot `buf`: wave 0 writes the key maps of channels 2l, 2l+1, wave 1
 // the value maps, scaled by 2^-E with E the running maximum of the tiles' range exponents
 // (held in E_map by wave 1).
-__device__ __forceinline__ void write_maps(VerifyLds& L, int buf, const MetaIn& m, float qscale, int tid,
-                                           int& E_map) {
+template <int CPT>
+__device__ __forceinline__ void write_maps(VerifyLds<CPT>& L, int buf, const MetaIn<CPT>& m, float qscale,
+                                           int tid, int& E_map) {
   const int l = tid & 63;
   if (tid < 64) {
     const int c = 2 * l + (l >> 3);       // channel 2l at 2l + 2l/16
-    L.abk[buf][c] = affine(m.gmin.x, m.gscale.x, m.mu.x, m.sigma.x, qscale);
-    L.abk[buf][c + 1] = affine(m.gmin.y, m.gscale.y, m.mu.y, m.sigma.y, qscale);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      L.abk[buf][k][c] = affine(m.gmin.x, m.gscale.x, m.mu[k].x, m.sigma[k].x, qscale);
+      L.abk[buf][k][c + 1] = affine(m.gmin.y, m.gscale.y, m.mu[k].y, m.sigma[k].y, qscale);
+    }
   } else {
-    float2 ab0 = affine(m.gmin.x, m.gscale.x, m.mu.x, m.sigma.x, 1.0f);
-    float2 ab1 = affine(m.gmin.y, m.gscale.y, m.mu.y, m.sigma.y, 1.0f);
-    int e = max(value_exponent(ab0), value_exponent(ab1));
+    float2 ab0[CPT], ab1[CPT];
+    int e = 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      ab0[k] = affine(m.gmin.x, m.gscale.x, m.mu[k].x, m.sigma[k].x, 1.0f);
+      ab1[k] = affine(m.gmin.y, m.gscale.y, m.mu[k].y, m.sigma[k].y, 1.0f);
+      e = max(e, max(value_exponent(ab0[k]), value_exponent(ab1[k])));
+    }
     if (__builtin_amdgcn_ballot_w64(e > E_map) != 0) {   // values beyond the range so far: rare
 #pragma unroll
       for (int sh = 32; sh >= 1; sh >>= 1) e = max(e, __shfl_xor(e, sh));
       E_map = max(E_map, e);
     }
-    if (E_map != 0) {
-      ab0 = make_float2(ldexpf(ab0.x, -E_map), ldexpf(ab0.y, -E_map));
-      ab1 = make_float2(ldexpf(ab1.x, -E_map), ldexpf(ab1.y, -E_map));
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      if (E_map != 0) {
+        ab0[k] = make_float2(ldexpf(ab0[k].x, -E_map), ldexpf(ab0[k].y, -E_map));
+        ab1[k] = make_float2(ldexpf(ab1[k].x, -E_map), ldexpf(ab1[k].y, -E_map));
+      }
+      *reinterpret_cast<float4*>(&L.abv[buf][k][2 * l]) = make_float4(ab0[k].x, ab0[k].y, ab1[k].x, ab1[k].y);
     }
-    *reinterpret_cast<float4*>(&L.abv[buf][2 * l]) = make_float4(ab0.x, ab0.y, ab1.x, ab1.y);
     if (l == 0) L.vexp[buf] = E_map;
   }
 }
 
-// Decode this thread's part of one tile into buffer `buf` (maps of slot `buf`).
-__device__ __forceinline__ void decode_tile(VerifyLds& L, int buf, const CodeIn& in, int tid, int lcopy) {
+// Decode this thread's part of one tile into buffer `buf` (maps of slot `buf`; a tile of CPT
+// chunks takes the map of each token's chunk).
+template <int CPT>
+__device__ __forceinline__ void decode_tile(VerifyLds<CPT>& L, int buf, const CodeIn& in, int tid, int lcopy) {
   {
     // keys: token t = tid/8, channels 16*(tid%8) + k, K_hat = A*L + B split into BF16 hi + lo;
     // row t holds 16 columns of 16 B (8 channels each), column c16 at c16 ^ (t & 15)
     const int t = tid >> 3, e8 = tid & 7;
+    const float2* abk = L.abk[buf][CPT == 1 ? 0 : t / (kVTile / CPT)];   // wave-uniform chunk
     const uint32_t aw[2] = {in.ka.x, in.ka.y}, rw[2] = {in.kr.x, in.kr.y};
     uint32_t hi[8], lo[8];
 #pragma unroll
@@ -231,7 +253,7 @@ __device__ __forceinline__ void decode_tile(VerifyLds& L, int buf, const CodeIn&
       for (int k = 0; k < 4; ++k) {
         const int ch = 16 * e8 + 8 * w + 2 * k;
         // the 8 threads of a token read 8 channels 16 apart: the padding puts them in 8 banks
-        const float2 ab0 = L.abk[buf][ch + e8], ab1 = L.abk[buf][ch + 1 + e8];
+        const float2 ab0 = abk[ch + e8], ab1 = abk[ch + 1 + e8];
         const float x0 = fmaf(ab0.x, L.lut[((ev >> (8 * k)) & 0xFFu) * kLutCopies + lcopy], ab0.y);
         const float x1 = fmaf(ab1.x, L.lut[((od >> (8 * k)) & 0xFFu) * kLutCopies + lcopy], ab1.y);
         const uint32_t h = bf16x2(x0, x1);
@@ -262,7 +284,7 @@ __device__ __forceinline__ void decode_tile(VerifyLds& L, int buf, const CodeIn&
       const uint32_t i0 = (((j & 1) ? od0 : ev0) >> sh) & 0xFFu;
       const uint32_t i1 = (((j & 1) ? od1 : ev1) >> sh) & 0xFFu;
       const int d = 8 * c8 + j;
-      const float2 ab = L.abv[buf][d];
+      const float2 ab = L.abv[buf][CPT == 1 ? 0 : tq / (kVTile / 2 / CPT)][d];   // the tokens' chunk
       const vf2 x = {fmaf(ab.x, L.lut[i0 * kLutCopies + lcopy], ab.y), fmaf(ab.x, L.lut[i1 * kLutCopies + lcopy], ab.y)};
       const int unit = (tq >> 1) ^ (d & 15);
       L.lv[buf][d * (kVTile / 2) + 2 * unit + (tq & 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, vh2));
@@ -272,6 +294,7 @@ __device__ __forceinline__ void decode_tile(VerifyLds& L, int buf, const CodeIn&
 
 }  // namespace
 
+template <int CPT>
 __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y;
   const int b = blockIdx.z / a.rowblocks, rb = blockIdx.z - b * a.rowblocks;
@@ -279,7 +302,7 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
 
-  __shared__ VerifyLds L;
+  __shared__ VerifyLds<CPT> L;
 
   for (int i = tid; i < 256 * kLutCopies; i += kVThreads) L.lut[i] = a.lut32[i / kLutCopies];
   const int lcopy = tid & (kLutCopies - 1);
@@ -326,12 +349,12 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
 
   // prologue: maps of tiles 0 and 1, codes of tiles 0 and 1, tile 0 decoded into buffer 0
   const bool mapper = wave < 2;          // wave-uniform
-  MetaIn meta;
+  MetaIn<CPT> meta;
   int E_map = 0;
   if (mapper) {
-    write_maps(L, 0, load_meta(a, b, kvh, t_begin, tid), a.qscale, tid, E_map);
-    write_maps(L, 1, load_meta(a, b, kvh, min(t_begin + 1, t_last), tid), a.qscale, tid, E_map);
-    meta = load_meta(a, b, kvh, min(t_begin + 2, t_last), tid);
+    write_maps(L, 0, load_meta<CPT>(a, b, kvh, t_begin, tid), a.qscale, tid, E_map);
+    write_maps(L, 1, load_meta<CPT>(a, b, kvh, min(t_begin + 1, t_last), tid), a.qscale, tid, E_map);
+    meta = load_meta<CPT>(a, b, kvh, min(t_begin + 2, t_last), tid);
   }
   CodeIn cin;
   load_codes(a, b, kvh, t_begin, tid, cin);
@@ -438,7 +461,7 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
     // ---- maps of tile i+2 into slot par (read by the decode in step i+1)
     if (mapper) {
       write_maps(L, par, meta, a.qscale, tid, E_map);
-      meta = load_meta(a, b, kvh, min(t_begin + i + 3, t_last), tid);
+      meta = load_meta<CPT>(a, b, kvh, min(t_begin + i + 3, t_last), tid);
     }
   };
 
@@ -495,6 +518,14 @@ __global__ __launch_bounds__(kHeadDim) void k_verify_combine(VerifyArgs a) {
 // ---------------------------------------------------------------------------
 namespace {
 
+// Chunks per 64-token tile: 1 for a chunk that is a multiple of 64, 2 for a chunk of 32 in
+// pages of a multiple of 64 tokens (a tile then holds two whole chunks of one page); 0 otherwise.
+int verify_cpt(int C, int P) {
+  if (C > 0 && C % kVTile == 0) return 1;
+  if (C == kVTile / 2 && P % kVTile == 0) return 2;
+  return 0;
+}
+
 struct VerifyPlan {
   int rowblocks, splits, tiles_per_split, ntiles;
 };
@@ -502,7 +533,7 @@ struct VerifyPlan {
 bool verify_plan(int batch, int n_query, int ctx, int Hq, int Hkv, int D, int P, int C, VerifyPlan* pl) {
   if (batch <= 0 || n_query <= 0 || ctx <= 0 || Hq <= 0 || Hkv <= 0 || P <= 0 || C <= 0) return false;
   if (ctx % P != 0 || P % C != 0 || Hq % Hkv != 0) return false;
-  if (D != kHeadDim || C % kVTile != 0) return false;
+  if (D != kHeadDim || verify_cpt(C, P) == 0) return false;
   const long long R = (long long)n_query * (Hq / Hkv);
   pl->rowblocks = (int)((R + kVRows - 1) / kVRows);
   pl->ntiles = ctx / kVTile;
@@ -532,7 +563,8 @@ int verify_launch(const void* q_dev, const void* k_anchor_dev, const void* k_res
   if (ctx_tokens % page_tokens != 0 || page_tokens % chunk != 0 || q_heads % kv_heads != 0) return LYNX_EINVAL;
   if (!std::isfinite(alpha) || !(alpha > 0.0f) || !std::isfinite(sm_scale)) return LYNX_EINVAL;
   if (out_dtype != LYNX_OUT_BF16 && out_dtype != LYNX_OUT_F32) return LYNX_EINVAL;
-  if (head_dim != kHeadDim || chunk % kVTile != 0 || batch > 65535 || kv_heads > 65535) return LYNX_EUNSUPPORTED;
+  if (head_dim != kHeadDim || verify_cpt(chunk, page_tokens) == 0 || batch > 65535 || kv_heads > 65535)
+    return LYNX_EUNSUPPORTED;
   if (batch == 0) return LYNX_OK;
   VerifyPlan pl;
   if (!verify_plan(batch, n_query, ctx_tokens, q_heads, kv_heads, head_dim, page_tokens, chunk, &pl))
@@ -590,7 +622,9 @@ int verify_launch(const void* q_dev, const void* k_anchor_dev, const void* k_res
     a.lut32[idx] = (float)v;
   }
   void* kargs[] = {&a};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&k_verify),
+  const void* fn = verify_cpt(chunk, page_tokens) == 1 ? reinterpret_cast<const void*>(&k_verify<1>)
+                                                         : reinterpret_cast<const void*>(&k_verify<2>);
+  hipError_t e = hipLaunchKernel(fn,
                                  dim3((unsigned)pl.splits, (unsigned)kv_heads, (unsigned)(batch * pl.rowblocks)),
                                  dim3(kVThreads), kargs, 0, stream);
   if (e != hipSuccess) return LYNX_ELAUNCH;

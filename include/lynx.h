@@ -184,7 +184,8 @@ size_t lynx_attn_verify_workspace_bytes(int batch, int n_query, int ctx_tokens, 
  *                  segments; sequence b's context is the ctx_tokens/page_tokens
  *                  consecutive segments starting at segment b*(ctx_tokens/page_tokens).
  *   q_heads      : a multiple of kv_heads (query head hq reads kv head hq / (q_heads/kv_heads)).
- *   chunk        : a multiple of 64 in this build (else LYNX_EUNSUPPORTED).
+ *   chunk        : a multiple of 64, or 32 with page_tokens a multiple of 64, in this build
+ *                  (else LYNX_EUNSUPPORTED).
  *   sm_scale     : > 0, or <= 0 to use 1/sqrt(head_dim).
  *   workspace_dev, ws_bytes : at least lynx_attn_verify_workspace_bytes(...) bytes.
  *   out_dtype    : LYNX_OUT_BF16 or LYNX_OUT_F32; out_dev [batch][n_query][q_heads][head_dim].

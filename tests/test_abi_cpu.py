@@ -159,7 +159,9 @@ def test_verify_validation():
     assert verify(sm=float("nan")) == lynx.LYNX_EINVAL
     assert verify(dt=3) == lynx.LYNX_EINVAL
     assert verify(D=64) == lynx.LYNX_EUNSUPPORTED
-    assert verify(C=32, P=256) == lynx.LYNX_EUNSUPPORTED        # chunk not a multiple of 64
+    assert verify(C=16, P=256) == lynx.LYNX_EUNSUPPORTED        # chunk neither 32 nor a multiple of 64
+    assert verify(T=960, P=96, C=32) == lynx.LYNX_EUNSUPPORTED   # chunk 32 in pages of 96: tiles cross pages
+    assert verify(C=32, P=256) == lynx.LYNX_ENOSPACE             # chunk 32: supported
     assert verify(kr=ODD) == lynx.LYNX_EALIGN
     assert verify(vr=None) == lynx.LYNX_EALIGN
     assert verify(lse=ctypes.c_void_p(GOOD.value + 2)) == lynx.LYNX_EALIGN
@@ -170,7 +172,7 @@ def test_verify_validation():
 
 @pytest.mark.parametrize("B,M,T,Hq,Hkv,P,C", [(16, 64, 32768, 64, 8, 256, 64), (2, 4, 1024, 16, 2, 256, 64),
                                               (1, 17, 256, 64, 8, 256, 64), (3, 1, 320, 8, 1, 64, 64),
-                                              (2, 5, 512, 12, 4, 256, 128)])
+                                              (2, 5, 512, 12, 4, 256, 128), (2, 4, 1024, 16, 2, 256, 32)])
 def test_verify_workspace_bytes(B, M, T, Hq, Hkv, P, C):
     """One (m, l, 0, 0, o[128]) float32 record per (sequence, draft token, query head, context split);
     the splits cover the context's 64-token tiles with no empty split."""
@@ -184,7 +186,8 @@ def test_verify_workspace_bytes(B, M, T, Hq, Hkv, P, C):
 
 
 def test_verify_workspace_bytes_unsupported():
-    assert lynx.attn_verify_workspace_bytes(2, 4, 1024, 16, 2, 128, 256, 32) == 0
+    assert lynx.attn_verify_workspace_bytes(2, 4, 1024, 16, 2, 128, 256, 16) == 0
+    assert lynx.attn_verify_workspace_bytes(2, 4, 960, 16, 2, 128, 96, 32) == 0
     assert lynx.attn_verify_workspace_bytes(2, 4, 1000, 16, 2, 128, 256, 64) == 0
     assert lynx.attn_verify_workspace_bytes(2, 0, 1024, 16, 2, 128, 256, 64) == 0
     assert lynx.attn_verify_workspace_bytes(2, 4, 1024, 16, 2, 64, 256, 64) == 0

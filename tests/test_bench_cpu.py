@@ -32,7 +32,7 @@ def test_counter_summary_calibrates_against_the_copy(tmp_path):
              ("void lynx::k_decode<true, false>(lynx::DecodeArgs)", 524288): [20.0],
              ("void lynx::k_attn_anchor<64>(lynx::AttnArgs)", 4096): [30.0],
              ("lynx::k_attn_combine(lynx::AttnArgs)", 131072): [1.0],
-             ("lynx::k_verify(lynx::(anonymous namespace)::VerifyArgs)", 131072): [40.0],
+             ("void lynx::k_verify<1>(lynx::(anonymous namespace)::VerifyArgs)", 131072): [40.0],
              ("lynx::k_verify_combine(lynx::(anonymous namespace)::VerifyArgs)", 8388608): [2.0]}
     write = {k: [v[0] * 2 for _ in v] for k, v in fetch.items()}
     fields = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
