@@ -205,6 +205,17 @@ int lynx_attn_anchor(const void* q_dev, const void* k_anchor_dev, const void* v_
                             static_cast<hipStream_t>(hip_stream));
 }
 
+int lynx_attn_anchor_paged(const void* q_dev, const void* k_anchor_pool_dev, const void* v_anchor_pool_dev,
+                           int n_pool_pages, const int32_t* block_table_dev, const int32_t* seq_lens_dev, int batch,
+                           int max_pages_per_seq, int q_heads, int kv_heads, int head_dim, int page_tokens,
+                           int chunk, float alpha, float sm_scale, void* workspace_dev, size_t ws_bytes,
+                           int out_dtype, void* out_dev, void* hip_stream) {
+  return attn_anchor_paged_launch(q_dev, k_anchor_pool_dev, v_anchor_pool_dev, n_pool_pages, block_table_dev,
+                                  seq_lens_dev, batch, max_pages_per_seq, q_heads, kv_heads, head_dim, page_tokens,
+                                  chunk, alpha, sm_scale, workspace_dev, ws_bytes, out_dtype, out_dev,
+                                  static_cast<hipStream_t>(hip_stream));
+}
+
 size_t lynx_attn_verify_workspace_bytes(int batch, int n_query, int ctx_tokens, int q_heads, int kv_heads,
                                         int head_dim, int page_tokens, int chunk) {
   return verify_workspace_bytes(batch, n_query, ctx_tokens, q_heads, kv_heads, head_dim, page_tokens, chunk);

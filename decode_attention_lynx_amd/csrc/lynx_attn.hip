@@ -57,8 +57,21 @@ struct AttnArgs {
   int splits, tiles_per_split, ntiles;
   float qscale;        // sm_scale * log2(e): scores are kept in base 2
   int out_f32;
+  // paged form: sequence b's page p is pool segment block_table[b * max_pages + p] (clamped
+  // into [0, n_pool)), and only its first seq_lens[b] tokens (clamped into [0, T]) count.
+  // Contiguous form: block_table and seq_lens are null, segment b * npages + p, T tokens.
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int max_pages, n_pool;
   uint32_t pair[256];  // float16 pair table: entry b = L[b & 15] | L[b >> 4] << 16 (L = S|x| of a nibble)
 };
+
+// Segment of sequence b's page `page` (uniform: a scalar load in the paged form).
+__device__ __forceinline__ size_t segment_of(const AttnArgs& a, int b, int page) {
+  if (a.block_table == nullptr) return (size_t)b * a.npages + page;
+  const int s = a.block_table[(size_t)b * a.max_pages + page];
+  return (size_t)min(max(s, 0), a.n_pool - 1);
+}
 
 __device__ __forceinline__ float dpp_row_ror8(float v) {
   // rotate right by 8 lanes inside each row of 16: column n reads column n ^ 8
@@ -136,7 +149,7 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int
   const int page = tok / a.P;
   const int tin = tok - page * a.P;
   const int kc = tin / a.C;
-  const size_t seg = ((size_t)b * a.npages + page) * (size_t)a.anc_seg;
+  const size_t seg = segment_of(a, b, page) * (size_t)a.anc_seg;
   const size_t row0 = ((size_t)kvh * a.P + tin) * (kHeadDim / 2);
   const uint8_t* kcb = a.kanc + seg + row0;
   const uint8_t* vcb = a.vanc + seg + row0;
@@ -215,15 +228,17 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
   for (int j = 0; j < 8; ++j) o_acc[j] = f4{0.f, 0.f, 0.f, 0.f};
 
+  // this sequence's context: T tokens, or its own length in the paged form
+  const int seq_len = a.seq_lens == nullptr ? a.T : min(max(a.seq_lens[b], 0), a.T);
   const int t_begin = split * a.tiles_per_split;
-  const int t_end = min(a.ntiles, t_begin + a.tiles_per_split);
+  const int t_end = min((seq_len + TILE - 1) / TILE, t_begin + a.tiles_per_split);   // may be empty
   float4* kab = s_kab[wave];
   float4* vab = s_vab[wave];
 
   const TileOffsets toff = tile_offsets(lane);
 
   // one 64-token tile of this wave: scores, online softmax, values
-  auto process = [&](const TileIn<TILE>& cur) {
+  auto process = [&](const TileIn<TILE>& cur, int tile) {
 
     // ---- the chunk's affine maps for channels 2*lane, 2*lane+1, shared through LDS:
     //      A = (gamma_scale+eps)(sigma+eps), B = gamma_min + mu (gamma_scale+eps);
@@ -283,6 +298,13 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lookup_row(w4[kk], s_pair, lane4), bq[kk], acc, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[4 * mb + i] = acc[i] + dpp_row_ror8(acc[i]);
+    }
+    if ((tile + 1) * TILE > seq_len) {   // the sequence ends inside this tile: mask the tail
+#pragma unroll
+      for (int mb = 0; mb < TILE / 16; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tile * TILE + 16 * mb + 4 * g + i >= seq_len) s[4 * mb + i] = -INFINITY;
     }
 
     // ---- online softmax (base 2) for head hh over this tile's 64 tokens
@@ -349,12 +371,14 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   TileIn<TILE> tb[2];
   int tile = t_begin + wave;
   const int t_last = t_end - 1;    // loads past the wave's last tile re-read that tile (in bounds, unused)
-  load_tile(a, b, kvh, min(tile, t_last), toff, tb[0]);
-  load_tile(a, b, kvh, min(tile + kAttnWaves, t_last), toff, tb[1]);
+  if (t_begin < t_end) {           // workgroup-uniform: a split past a short sequence loads nothing
+    load_tile(a, b, kvh, min(tile, t_last), toff, tb[0]);
+    load_tile(a, b, kvh, min(tile + kAttnWaves, t_last), toff, tb[1]);
+  }
   while (tile < t_end) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if (tile < t_end) process(tb[i]);
+      if (tile < t_end) process(tb[i], tile);
       load_tile(a, b, kvh, min(tile + 2 * kAttnWaves, t_last), toff, tb[i]);
       tile += kAttnWaves;
     }
@@ -408,7 +432,7 @@ __global__ __launch_bounds__(kHeadDim) void k_attn_combine(AttnArgs a) {
     o = fmaf(r[2 + d], f, o);
     l = fmaf(r[1], f, l);
   }
-  const float res = o / l;
+  const float res = l > 0.0f ? o / l : 0.0f;   // an empty context gives 0
   if (a.out_f32) static_cast<float*>(a.out)[(size_t)bh * kHeadDim + d] = res;
   else {
     const uint32_t u = __float_as_uint(res);
@@ -457,10 +481,13 @@ size_t attn_workspace_bytes(int batch, int ctx, int Hq, int Hkv, int D, int P, i
   return (size_t)batch * Hq * pl.splits * (kHeadDim + 2) * sizeof(float);
 }
 
-int attn_anchor_launch(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev, int batch,
-                       int ctx_tokens, int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk,
-                       float alpha, float sm_scale, void* workspace_dev, size_t ws_bytes, int out_dtype,
-                       void* out_dev, hipStream_t stream) {
+namespace {
+
+// Shared by the contiguous and the paged entry points (block_table == nullptr: contiguous).
+int attn_launch(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev, int batch, int ctx_tokens,
+                int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk, float alpha, float sm_scale,
+                void* workspace_dev, size_t ws_bytes, int out_dtype, void* out_dev, const int32_t* block_table,
+                const int32_t* seq_lens, int max_pages, int n_pool, hipStream_t stream) {
   if (batch < 0 || ctx_tokens <= 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 || page_tokens <= 0 ||
       chunk <= 0)
     return LYNX_EINVAL;
@@ -484,6 +511,10 @@ int attn_anchor_launch(const void* q_dev, const void* k_anchor_dev, const void* 
   a.q = static_cast<const uint16_t*>(q_dev);
   a.kanc = static_cast<const uint8_t*>(k_anchor_dev);
   a.vanc = static_cast<const uint8_t*>(v_anchor_dev);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.max_pages = max_pages;
+  a.n_pool = n_pool;
   a.ws = static_cast<float*>(workspace_dev);
   a.out = out_dev;
   a.B = batch;
@@ -523,6 +554,31 @@ int attn_anchor_launch(const void* q_dev, const void* k_anchor_dev, const void* 
   e = hipLaunchKernel(reinterpret_cast<const void*>(&k_attn_combine), dim3((unsigned)(batch * q_heads)),
                       dim3(kHeadDim), kargs, 0, stream);
   return e == hipSuccess ? LYNX_OK : LYNX_ELAUNCH;
+}
+
+}  // namespace
+
+int attn_anchor_launch(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev, int batch,
+                       int ctx_tokens, int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk,
+                       float alpha, float sm_scale, void* workspace_dev, size_t ws_bytes, int out_dtype,
+                       void* out_dev, hipStream_t stream) {
+  return attn_launch(q_dev, k_anchor_dev, v_anchor_dev, batch, ctx_tokens, q_heads, kv_heads, head_dim, page_tokens,
+                     chunk, alpha, sm_scale, workspace_dev, ws_bytes, out_dtype, out_dev, nullptr, nullptr, 0, 0,
+                     stream);
+}
+
+int attn_anchor_paged_launch(const void* q_dev, const void* k_anchor_pool, const void* v_anchor_pool, int n_pool,
+                             const int32_t* block_table, const int32_t* seq_lens, int batch, int max_pages,
+                             int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk, float alpha,
+                             float sm_scale, void* workspace_dev, size_t ws_bytes, int out_dtype, void* out_dev,
+                             hipStream_t stream) {
+  if (n_pool <= 0 || max_pages <= 0 || page_tokens <= 0) return LYNX_EINVAL;
+  if ((long long)max_pages * page_tokens > 0x7fffffffll) return LYNX_EUNSUPPORTED;
+  auto al4 = [](const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+  if (!al4(block_table) || !al4(seq_lens)) return LYNX_EALIGN;
+  return attn_launch(q_dev, k_anchor_pool, v_anchor_pool, batch, max_pages * page_tokens, q_heads, kv_heads,
+                     head_dim, page_tokens, chunk, alpha, sm_scale, workspace_dev, ws_bytes, out_dtype, out_dev,
+                     block_table, seq_lens, max_pages, n_pool, stream);
 }
 
 }  // namespace lynx

@@ -22,7 +22,8 @@ OUT_F32 = 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblynx.so")
 EXPORTS = ("lynx_strerror", "lynx_stream_sizes", "lynx_encode", "lynx_decode_anchor", "lynx_decode_full",
-           "lynx_attn_workspace_bytes", "lynx_attn_anchor", "lynx_attn_verify_workspace_bytes", "lynx_attn_verify")
+           "lynx_attn_workspace_bytes", "lynx_attn_anchor", "lynx_attn_verify_workspace_bytes", "lynx_attn_verify",
+           "lynx_attn_anchor_paged")
 
 _lib = None
 
@@ -58,6 +59,9 @@ def lib() -> ctypes.CDLL:
         L.lynx_attn_anchor.restype = c_int
         L.lynx_attn_anchor.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                        c_float, c_float, c_void, c_size, c_int, c_void, c_void]
+        L.lynx_attn_anchor_paged.restype = c_int
+        L.lynx_attn_anchor_paged.argtypes = [c_void, c_void, c_void, c_int, c_void, c_void] + [c_int] * 7 + [
+            c_float, c_float, c_void, c_size, c_int, c_void, c_void]
         L.lynx_attn_verify_workspace_bytes.restype = c_size
         L.lynx_attn_verify_workspace_bytes.argtypes = [c_int] * 8
         L.lynx_attn_verify.restype = c_int
@@ -157,6 +161,28 @@ def attn_anchor(q, k_anchor, v_anchor, ctx_tokens: int, kv_heads: int, page_toke
     _check(lib().lynx_attn_anchor(_ptr(q), _ptr(k_anchor), _ptr(v_anchor), B, ctx_tokens, Hq, kv_heads, D,
                                   page_tokens, chunk, alpha, sm_scale, _ptr(workspace), workspace.numel(), code,
                                   _ptr(out), _stream(stream)), "lynx_attn_anchor")
+    return out
+
+
+def attn_anchor_paged(q, k_pool, v_pool, block_table, seq_lens, kv_heads: int, page_tokens: int, chunk: int,
+                      alpha: float, sm_scale: float = 0.0, out_dtype=None, workspace=None, out=None, stream=None):
+    """q: CUDA bfloat16 [B, Hq, D]; k_pool / v_pool: [n_pool, anchor_seg] uint8; block_table: CUDA int32
+    [B, max_pages]; seq_lens: CUDA int32 [B].  Returns O [B, Hq, D]."""
+    import torch
+    B, Hq, D = q.shape
+    n_pool = k_pool.shape[0]
+    max_pages = block_table.shape[1]
+    ws = attn_workspace_bytes(B, max_pages * page_tokens, Hq, kv_heads, D, page_tokens, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
+    dt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=dt, device=q.device)
+    code = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    _check(lib().lynx_attn_anchor_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), n_pool, _ptr(block_table),
+                                        _ptr(seq_lens), B, max_pages, Hq, kv_heads, D, page_tokens, chunk, alpha,
+                                        sm_scale, _ptr(workspace), workspace.numel(), code, _ptr(out),
+                                        _stream(stream)), "lynx_attn_anchor_paged")
     return out
 
 

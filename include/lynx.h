@@ -56,6 +56,7 @@
 #define LYNX_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -163,6 +164,31 @@ int lynx_attn_anchor(const void* q_dev, const void* k_anchor_dev, const void* v_
                      int page_tokens, int chunk, float alpha, float sm_scale,
                      void* workspace_dev, size_t ws_bytes, int out_dtype, void* out_dev,
                      void* hip_stream);
+
+/*
+ * lynx_attn_anchor over a paged cache with per-sequence lengths (the paged-attention
+ * block layout of the serving engines the pages integrate with, [Review] Implementation
+ * Notes: KV page granularity of 256 tokens as in paged attention).
+ *   k_anchor_pool_dev, v_anchor_pool_dev : n_pool_pages anchor segments each (one page of
+ *                  page_tokens tokens per segment, as lynx_encode writes them).
+ *   block_table_dev : int32 [batch][max_pages_per_seq], device; entry (b, p) is the pool
+ *                  segment holding page p of sequence b.  Entries past a sequence's last
+ *                  page are not read; an entry outside [0, n_pool_pages) is clamped into it
+ *                  (no out-of-range access; the result for that sequence is then unspecified).
+ *   seq_lens_dev : int32 [batch], device; sequence b attends to its first seq_lens[b] tokens
+ *                  (clamped into [0, max_pages_per_seq * page_tokens]); the tail of its last
+ *                  page is masked.  A zero length gives an output of 0.
+ * The other arguments are those of lynx_attn_anchor, with ctx_tokens replaced by
+ * max_pages_per_seq * page_tokens; the workspace size is
+ * lynx_attn_workspace_bytes(batch, max_pages_per_seq * page_tokens, ...).
+ * Errors: those of lynx_attn_anchor; LYNX_EINVAL for n_pool_pages or max_pages_per_seq <= 0;
+ * LYNX_EALIGN for a null or misaligned block_table_dev / seq_lens_dev.
+ */
+int lynx_attn_anchor_paged(const void* q_dev, const void* k_anchor_pool_dev, const void* v_anchor_pool_dev,
+                           int n_pool_pages, const int32_t* block_table_dev, const int32_t* seq_lens_dev, int batch,
+                           int max_pages_per_seq, int q_heads, int kv_heads, int head_dim, int page_tokens,
+                           int chunk, float alpha, float sm_scale, void* workspace_dev, size_t ws_bytes,
+                           int out_dtype, void* out_dev, void* hip_stream);
 
 /*
  * Bytes of workspace lynx_attn_verify needs for this shape, or 0 if the shape is

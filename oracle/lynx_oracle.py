@@ -402,6 +402,29 @@ def attention_anchor(q_bits: np.ndarray, k_anchor: np.ndarray, v_anchor: np.ndar
     return O
 
 
+def attention_anchor_paged(q_bits: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_table: np.ndarray,
+                           seq_lens: np.ndarray, Hq: int, Hkv: int, D: int, P: int, C: int, alpha: float,
+                           sm_scale: float | None = None) -> np.ndarray:
+    """Eq. 1 over a paged anchor cache with per-sequence lengths.
+
+    q_bits [B, Hq, D]; k_pool / v_pool: pool of anchor segments [n_pool, anchor_seg]; block_table
+    [B, max_pages] (entry (b, p) = pool segment of page p of sequence b); seq_lens [B].  Sequence b's
+    context is the first seq_lens[b] tokens of its pages in order; an empty context gives O = 0.
+    """
+    q = bf16_bits_to_f64(q_bits)
+    B = q.shape[0]
+    O = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n <= 0:
+            continue
+        pages = [int(x) for x in block_table[b, :(n + P - 1) // P]]
+        Kh = decode_anchor(np.asarray(k_pool)[pages], len(pages), P, Hkv, D, C, alpha)[:n][None]
+        Vh = decode_anchor(np.asarray(v_pool)[pages], len(pages), P, Hkv, D, C, alpha)[:n][None]
+        O[b] = attention(q[b:b + 1], Kh, Vh, sm_scale)[0]
+    return O
+
+
 def attention_lse(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float | None = None):
     """q: [R, Hq, D] (R query tokens); K, V: [T, Hkv, D] (float64), shared by the R queries.
 

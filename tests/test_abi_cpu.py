@@ -191,3 +191,22 @@ def test_verify_workspace_bytes_unsupported():
     assert lynx.attn_verify_workspace_bytes(2, 4, 1000, 16, 2, 128, 256, 64) == 0
     assert lynx.attn_verify_workspace_bytes(2, 0, 1024, 16, 2, 128, 256, 64) == 0
     assert lynx.attn_verify_workspace_bytes(2, 4, 1024, 16, 2, 64, 256, 64) == 0
+
+
+def paged(B=2, maxp=4, Hq=16, Hkv=2, D=128, P=256, C=64, n_pool=8, alpha=255.0, bt=GOOD, sl=GOOD, q=GOOD,
+          k=GOOD, v=GOOD, ws=GOOD, out=GOOD):
+    # workspace size 0: too small for any supported case, so no call below reaches a launch
+    return lynx.lib().lynx_attn_anchor_paged(q, k, v, n_pool, bt, sl, B, maxp, Hq, Hkv, D, P, C, alpha, 0.0, ws, 0,
+                                             lynx.OUT_F32, out, None)
+
+
+def test_attention_paged_validation():
+    assert paged(n_pool=0) == lynx.LYNX_EINVAL
+    assert paged(maxp=0) == lynx.LYNX_EINVAL
+    assert paged(P=96, C=64) == lynx.LYNX_EINVAL                 # P % C
+    assert paged(bt=None) == lynx.LYNX_EALIGN
+    assert paged(sl=ctypes.c_void_p(GOOD.value + 2)) == lynx.LYNX_EALIGN
+    assert paged(D=64) == lynx.LYNX_EUNSUPPORTED
+    assert paged(maxp=1 << 24) == lynx.LYNX_EUNSUPPORTED          # max_pages * P overflows int
+    assert paged() == lynx.LYNX_ENOSPACE
+    assert paged(B=0) == lynx.LYNX_OK

@@ -105,3 +105,35 @@ def test_attention_full_size_sampled(gpu):
         e = rel_l2(got[b:b + 1], ref)
         print(f"[attn] seq {b}: rel_l2={e:.3e} worst_head={worst_head(got[b:b + 1], ref):.3e}", flush=True)
         assert e <= REL_L2
+
+
+@pytest.mark.parametrize("C", [64, 32])
+def test_attention_paged_variable_lengths(gpu, C):
+    """A shuffled pool of pages behind a block table, with lengths that end inside a tile, on a
+    tile edge, inside a page, at one token and at zero (output 0)."""
+    B, Hq, Hkv, P, maxp, alpha = 6, 16, 2, 256, 4, 255.0
+    lens = np.array([1, 63, 64, 300, maxp * P, 0], dtype=np.int32)
+    print(f"[attn-paged] C={C} lens={lens.tolist()}", flush=True)
+    T = maxp * P
+    kb = np.concatenate([synth.make_kv_np(T, Hkv, 128, seed=31, layer=b, kv_idx=0) for b in range(B)])
+    vb = np.concatenate([synth.make_kv_np(T, Hkv, 128, seed=31, layer=b, kv_idx=1) for b in range(B)])
+    ka, _, _ = o.encode(kb, P, C, alpha)
+    va, _, _ = o.encode(vb, P, C, alpha)
+    perm = np.random.default_rng(C).permutation(B * maxp)
+    inv = np.argsort(perm)
+    bt = inv[np.arange(B * maxp).reshape(B, maxp)].astype(np.int32)
+    bt[0, 1:] = -1                                   # pages past a sequence's end are not read
+    qb = synth.make_q_np(B, Hq, 128, seed=31)
+    ref = o.attention_anchor_paged(qb, ka[perm], va[perm], bt, lens, Hq, Hkv, 128, P, C, alpha)
+    q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).cuda()
+    out = lynx.attn_anchor_paged(q, upload(ka[perm]), upload(va[perm]), torch.from_numpy(bt).cuda(),
+                                 torch.from_numpy(lens).cuda(), Hkv, P, C, alpha, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        if lens[b] == 0:
+            assert np.all(got[b] == 0.0)
+            continue
+        e = rel_l2(got[b], ref[b])
+        print(f"[attn-paged] seq {b} len {lens[b]}: rel_l2={e:.3e}", flush=True)
+        assert e <= REL_L2

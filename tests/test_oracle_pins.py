@@ -446,3 +446,31 @@ def test_signed_zero_metadata_is_plus_zero():
     enc = o.encode_page(X, 16, 255.0)
     assert np.all(enc["gmin"].view(np.uint32) == 0) and np.all(enc["gscale"].view(np.uint32) == 0)
     assert np.all(enc["I"] == 0) and np.all(enc["S"] == 1)
+
+
+def test_attention_anchor_paged_matches_contiguous():
+    """The paged oracle is a gather: an identity block table with full lengths, a shuffled pool,
+    and lengths at page boundaries all reduce to the contiguous attention; an empty context is 0."""
+    from decode_attention_lynx_amd import synth
+    B, Hq, Hkv, T, P, C, alpha = 3, 8, 2, 512, 128, 64, 255.0
+    kb = np.concatenate([synth.make_kv_np(T, Hkv, 128, seed=4, layer=b, kv_idx=0) for b in range(B)])
+    vb = np.concatenate([synth.make_kv_np(T, Hkv, 128, seed=4, layer=b, kv_idx=1) for b in range(B)])
+    ka, _, _ = o.encode(kb, P, C, alpha)
+    va, _, _ = o.encode(vb, P, C, alpha)
+    qb = synth.make_q_np(B, Hq, 128, seed=4)
+    npg = T // P
+    ref = o.attention_anchor(qb, ka, va, B, T, Hq, Hkv, 128, P, C, alpha)
+    ident = np.arange(B * npg).reshape(B, npg)
+    full = np.full(B, T)
+    assert np.allclose(o.attention_anchor_paged(qb, ka, va, ident, full, Hq, Hkv, 128, P, C, alpha), ref,
+                       rtol=0, atol=1e-12)
+    perm = np.random.default_rng(0).permutation(B * npg)
+    inv = np.argsort(perm)                          # pool slot of original page j is inv[j]
+    bt = inv[ident]
+    assert np.allclose(o.attention_anchor_paged(qb, ka[perm], va[perm], bt, full, Hq, Hkv, 128, P, C, alpha),
+                       ref, rtol=0, atol=1e-12)
+    # a length of two pages equals the contiguous attention over those two pages
+    two = o.attention_anchor(qb[:1], ka[:2], va[:2], 1, 2 * P, Hq, Hkv, 128, P, C, alpha)
+    got = o.attention_anchor_paged(qb, ka, va, ident, np.array([2 * P, 0, T]), Hq, Hkv, 128, P, C, alpha)
+    assert np.allclose(got[0], two[0], rtol=0, atol=1e-12)
+    assert np.all(got[1] == 0.0)
