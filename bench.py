@@ -11,6 +11,9 @@ One step =
 Timed after the step, on its own (not part of `value`):
   attn_verify   the verification pass over full codes: the same 16 sequences with
                 64 draft tokens each, anchor + residual segments
+  encode_to_host the request encoded in groups of 256 pages, each group's anchor and
+                residual segments copied to pinned host memory while the next group is
+                encoded (two streams), against a plain device-to-host copy of the same bytes
 Inputs are synthetic (Laplacian + per-channel offset + x100 outlier channels,
 seeded) and resident in HBM before the timed region.
 
@@ -35,6 +38,7 @@ LAYERS, TOKENS, KVH, D = 32, 16384, 8, 128
 P, C, ALPHA = 256, 64, 255.0
 AB, AHQ, AHKV, AT = 16, 64, 8, 32768
 AM = 64                      # draft tokens per sequence in the verification pass
+PIPE_GROUP = 256             # pages per group of the pipelined encode to host memory
 MFMA_PEAK_TFLOPS = 2500.0    # dense float16 / bfloat16 MFMA
 KERNEL_SOURCES = ["decode_attention_lynx_amd/csrc/lynx_codec.hip", "decode_attention_lynx_amd/csrc/lynx_attn.hip",
                   "decode_attention_lynx_amd/csrc/lynx_common.hpp", "decode_attention_lynx_amd/csrc/lynx_abi.hip",
@@ -235,7 +239,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ops", default="encode,decode_anchor,decode_full,attn_anchor")
-    ap.add_argument("--next-ops", default="attn_verify",
+    ap.add_argument("--next-ops", default="attn_verify,encode_to_host",
                     help="ops timed after the step, on their own (empty: none)")
     ap.add_argument("--counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="summarise two rocprofv3 --pmc runs of this benchmark into per-op HBM bytes")
@@ -291,6 +295,12 @@ def main():
                            device=dev)
         o_ver = torch.empty((AB, AM, AHQ, D), dtype=torch.bfloat16, device=dev)
         lse_ver = torch.empty((AB, AM, AHQ), dtype=torch.float32, device=dev)
+    if "encode_to_host" in next_ops + ops:
+        anchor_h = torch.empty((n_pages, a_sz), dtype=torch.uint8, pin_memory=True)
+        residual_h = torch.empty((n_pages, r_sz), dtype=torch.uint8, pin_memory=True)
+        staging = torch.empty(lynx.lib().lynx_encode_to_host_staging_bytes(PIPE_GROUP, P, KVH, D, C),
+                              dtype=torch.uint8, device=dev)
+        copy_stream = torch.cuda.Stream()
     torch.cuda.synchronize()
 
     # plain streaming kernels (libhbmprobe.so): what this HBM sustains, and a 1 GiB copy of
@@ -312,6 +322,16 @@ def main():
             lynx.decode_full(anchor, residual, n_pages, P, KVH, D, C, ALPHA, out=out_f)
         elif op == "attn_anchor":
             lynx.attn_anchor(q, att[0], att[1], AT, AHKV, P, C, ALPHA, workspace=ws, out=o_att)
+        elif op == "encode_to_host":
+            # one request per call, drained before the next is queued: with many requests queued
+            # ahead on the two streams the copies were measured to slow down several times
+            lynx.encode_to_host(kv, P, C, ALPHA, PIPE_GROUP, anchor_host=anchor_h, residual_host=residual_h,
+                                staging=staging, compute_stream=torch.cuda.current_stream(), copy_stream=copy_stream)
+            torch.cuda.current_stream().wait_stream(copy_stream)
+            copy_stream.synchronize()
+        elif op == "d2h_copy":      # reference: the same bytes, already encoded, copied device -> host
+            anchor_h.copy_(anchor, non_blocking=True)
+            residual_h.copy_(residual, non_blocking=True)
         elif op == "attn_verify":
             lynx.attn_verify(qv, att[0], att_res[0], att[1], att_res[1], AT, AHKV, P, C, ALPHA, workspace=ws_v,
                              out=o_ver, lse=lse_ver)
@@ -340,7 +360,8 @@ def main():
     # ops beyond the step, timed on their own with the same warmup and step counts
     nev = {}
     for op in next_ops:
-        for _ in range(args.warmup):
+        # the host-copy pipeline's first runs pay for first-touch of the pinned pages: warm longer
+        for _ in range(max(args.warmup, 5) if op == "encode_to_host" else args.warmup):
             run(op)
         nev[op] = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(args.steps)]
@@ -349,7 +370,8 @@ def main():
             run(op)
             nev[op][s][1].record(stream)
         torch.cuda.synchronize()
-        print(f"[bench] {op}: {args.steps} launches timed", file=sys.stderr, flush=True)
+        print(f"[bench] {op}: {args.steps} launches timed, ms: "
+              + " ".join(f"{a.elapsed_time(b):.3f}" for a, b in nev[op]), file=sys.stderr, flush=True)
 
     # measured HBM ceilings (not part of the timed step)
     def probe_gbs(fn, nbytes):
@@ -377,8 +399,27 @@ def main():
                       "alg_GBs": round(alg / ms[op] / 1e6, 1), "frac_hbm_peak": round(alg / ms[op] / 1e6 / HBM_PEAK_GBS, 4),
                       "alg_bytes_per_launch": int(alg)}
     next_rep = {}
+    if "encode_to_host" in next_ops:
+        # the plain copy it is measured against (not part of any step)
+        for _ in range(2):
+            run("d2h_copy")
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(args.steps):
+            run("d2h_copy")
+        c1.record(stream)
+        torch.cuda.synchronize()
+        d2h_ms = c0.elapsed_time(c1) / args.steps
     for op in next_ops:
         t = sum(a.elapsed_time(b) for a, b in nev[op]) / args.steps
+        if op == "encode_to_host":
+            nbytes = n_pages * (a_sz + r_sz)
+            next_rep[op] = {"ms": round(t, 4), "host_GBs": round(nbytes / t / 1e6, 2),
+                            "bf16_equiv_GBs": round(2.0 * op_elems("encode") / t / 1e6, 1),
+                            "group_pages": PIPE_GROUP, "d2h_copy_ms": round(d2h_ms, 4),
+                            "d2h_copy_GBs": round(nbytes / d2h_ms / 1e6, 2),
+                            "copy_over_pipeline": round(d2h_ms / t, 4)}
+            continue
         fl = op_flops(op)
         next_rep[op] = {"ms": round(t, 4), "TFLOPs": round(fl / t / 1e9, 1),
                         "frac_mfma_peak": round(fl / t / 1e9 / MFMA_PEAK_TFLOPS, 4),
@@ -399,9 +440,11 @@ def main():
                                "C=64, alpha=255: encode + decode_anchor + decode_full) + anchor-only decode "
                                "attention (16 seq x 64 q / 8 kv heads x 128, 32768-token context)",
                    "ops": per_op, "hbm_peak_GBs": HBM_PEAK_GBS, "hbm_measured": hbm,
-                   "beyond_step": {"workload": f"verification pass over full codes ({AB} seq x {AM} draft tokens "
-                                               f"x {AHQ} q / {AHKV} kv heads x {D}, {AT}-token context); "
-                                               "bound: mfma", "ops": next_rep},
+                   "beyond_step": {"workload": f"attn_verify: verification pass over full codes ({AB} seq x {AM} "
+                                               f"draft tokens x {AHQ} q / {AHKV} kv heads x {D}, {AT}-token "
+                                               "context), bound: mfma; encode_to_host: the request encoded "
+                                               f"in groups of {PIPE_GROUP} pages and copied to pinned host "
+                                               "memory, bound: the device-to-host link", "ops": next_rep},
                    "arith": "float32 codec (float64 statistics and boundary cases), float16 MFMA attention "
                             "with float32 accumulation"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

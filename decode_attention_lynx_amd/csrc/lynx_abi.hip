@@ -134,6 +134,65 @@ int lynx_encode(const void* kv_dev, int n_pages, int page_tokens, int kv_heads, 
   return launch(fn, grid, &a, static_cast<hipStream_t>(hip_stream));
 }
 
+size_t lynx_encode_to_host_staging_bytes(int group_pages, int page_tokens, int kv_heads, int head_dim, int chunk) {
+  Geometry g;
+  if (group_pages <= 0 || check_geometry(group_pages, page_tokens, kv_heads, head_dim, chunk, 1.0f, &g) != LYNX_OK)
+    return 0;
+  return 2 * (size_t)group_pages * (size_t)(g.anc_seg + g.res_seg);
+}
+
+int lynx_encode_to_host(const void* kv_dev, int n_pages, int page_tokens, int kv_heads, int head_dim, int chunk,
+                        float alpha, int group_pages, void* staging_dev, size_t staging_bytes, void* anchor_host,
+                        void* residual_host, void* compute_stream, void* copy_stream) {
+  Geometry g;
+  int st = check_geometry(n_pages, page_tokens, kv_heads, head_dim, chunk, alpha, &g);
+  if (st != LYNX_OK) return st;
+  if (group_pages <= 0) return LYNX_EINVAL;
+  if (n_pages == 0) return LYNX_OK;
+  if (anchor_host == nullptr || residual_host == nullptr) return LYNX_EINVAL;
+  if (!aligned16(kv_dev) || !aligned16(staging_dev)) return LYNX_EALIGN;
+  const int gp = group_pages < n_pages ? group_pages : n_pages;
+  const size_t a_sz = (size_t)g.anc_seg, r_sz = (size_t)g.res_seg;
+  if (staging_bytes < 2 * (size_t)gp * (a_sz + r_sz)) return LYNX_ENOSPACE;
+  hipStream_t cs = static_cast<hipStream_t>(compute_stream), xs = static_cast<hipStream_t>(copy_stream);
+  // enc[b]: group in staging buffer b encoded; cpy[b]: its copies done, buffer b free again
+  hipEvent_t enc[2] = {nullptr, nullptr}, cpy[2] = {nullptr, nullptr};
+  int rc = LYNX_OK;
+  for (int b = 0; b < 2 && rc == LYNX_OK; ++b)
+    if (hipEventCreateWithFlags(&enc[b], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&cpy[b], hipEventDisableTiming) != hipSuccess)
+      rc = LYNX_ELAUNCH;
+  // copies still queued on copy_stream (an earlier call's) may read the staging buffers:
+  // the first encodes wait for them
+  for (int b = 0; b < 2 && rc == LYNX_OK; ++b)
+    if (hipEventRecord(cpy[b], xs) != hipSuccess) rc = LYNX_ELAUNCH;
+  const size_t kv_page_elems = (size_t)page_tokens * g.H;
+  uint8_t* stage = static_cast<uint8_t*>(staging_dev);
+  for (int g0 = 0, grp = 0; g0 < n_pages && rc == LYNX_OK; g0 += gp, ++grp) {
+    const int n = n_pages - g0 < gp ? n_pages - g0 : gp;
+    const int b = grp & 1;
+    uint8_t* anc = stage + (size_t)b * gp * (a_sz + r_sz);
+    uint8_t* res = anc + (size_t)gp * a_sz;
+    if (hipStreamWaitEvent(cs, cpy[b], 0) != hipSuccess) { rc = LYNX_ELAUNCH; break; }
+    rc = lynx_encode(static_cast<const uint16_t*>(kv_dev) + (size_t)g0 * kv_page_elems, n, page_tokens, kv_heads,
+                     head_dim, chunk, alpha, LYNX_SEL_ANCHOR | LYNX_SEL_RESIDUAL, anc, res, cs);
+    if (rc != LYNX_OK) break;
+    // the anchor segments leave first, then the residual ones
+    if (hipEventRecord(enc[b], cs) != hipSuccess || hipStreamWaitEvent(xs, enc[b], 0) != hipSuccess ||
+        hipMemcpyAsync(static_cast<uint8_t*>(anchor_host) + (size_t)g0 * a_sz, anc, (size_t)n * a_sz,
+                       hipMemcpyDeviceToHost, xs) != hipSuccess ||
+        hipMemcpyAsync(static_cast<uint8_t*>(residual_host) + (size_t)g0 * r_sz, res, (size_t)n * r_sz,
+                       hipMemcpyDeviceToHost, xs) != hipSuccess ||
+        hipEventRecord(cpy[b], xs) != hipSuccess)
+      rc = LYNX_ELAUNCH;
+  }
+  for (int b = 0; b < 2; ++b) {          // released by the runtime once the recorded work is done
+    if (enc[b]) (void)hipEventDestroy(enc[b]);
+    if (cpy[b]) (void)hipEventDestroy(cpy[b]);
+  }
+  return rc;
+}
+
 static int decode_common(bool full, const void* anchor_dev, const void* residual_dev, int n_pages,
                          int page_tokens, int kv_heads, int head_dim, int chunk, float alpha, int out_dtype,
                          void* out_dev, void* hip_stream) {

@@ -23,7 +23,7 @@ OUT_F32 = 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblynx.so")
 EXPORTS = ("lynx_strerror", "lynx_stream_sizes", "lynx_encode", "lynx_decode_anchor", "lynx_decode_full",
            "lynx_attn_workspace_bytes", "lynx_attn_anchor", "lynx_attn_verify_workspace_bytes", "lynx_attn_verify",
-           "lynx_attn_anchor_paged")
+           "lynx_attn_anchor_paged", "lynx_encode_to_host_staging_bytes", "lynx_encode_to_host")
 
 _lib = None
 
@@ -59,6 +59,11 @@ def lib() -> ctypes.CDLL:
         L.lynx_attn_anchor.restype = c_int
         L.lynx_attn_anchor.argtypes = [c_void, c_void, c_void, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                        c_float, c_float, c_void, c_size, c_int, c_void, c_void]
+        L.lynx_encode_to_host_staging_bytes.restype = c_size
+        L.lynx_encode_to_host_staging_bytes.argtypes = [c_int] * 5
+        L.lynx_encode_to_host.restype = c_int
+        L.lynx_encode_to_host.argtypes = [c_void] + [c_int] * 5 + [c_float, c_int, c_void, c_size, c_void, c_void,
+                                                                 c_void, c_void]
         L.lynx_attn_anchor_paged.restype = c_int
         L.lynx_attn_anchor_paged.argtypes = [c_void, c_void, c_void, c_int, c_void, c_void] + [c_int] * 7 + [
             c_float, c_float, c_void, c_size, c_int, c_void, c_void]
@@ -113,6 +118,32 @@ def encode(kv, page_tokens: int, chunk: int, alpha: float, residual: bool = True
     _check(lib().lynx_encode(_ptr(kv), n_pages, page_tokens, Hkv, D, chunk, alpha, sel, _ptr(anchor_out),
                              _ptr(residual_out) if residual else None, _stream(stream)), "lynx_encode")
     return anchor_out, (residual_out if residual else None)
+
+
+def encode_to_host(kv, page_tokens: int, chunk: int, alpha: float, group_pages: int, anchor_host=None,
+                   residual_host=None, staging=None, compute_stream=None, copy_stream=None):
+    """Encode kv (CUDA bfloat16 [n_pages*P, Hkv, D]) group by group into pinned host tensors
+    (uint8 [n_pages, a_seg] and [n_pages, r_seg]), each group's copy overlapping the next group's
+    encode.  Asynchronous: the host tensors are complete once copy_stream has drained.  copy_stream
+    defaults to the compute stream (no overlap); pass a second stream to overlap."""
+    import torch
+    T, Hkv, D = kv.shape
+    n_pages = T // page_tokens
+    a_sz, r_sz = stream_sizes(page_tokens, Hkv, D, chunk)
+    if anchor_host is None:
+        anchor_host = torch.empty((n_pages, a_sz), dtype=torch.uint8, pin_memory=True)
+    if residual_host is None:
+        residual_host = torch.empty((n_pages, r_sz), dtype=torch.uint8, pin_memory=True)
+    gp = max(1, min(group_pages, n_pages))
+    need = int(lib().lynx_encode_to_host_staging_bytes(gp, page_tokens, Hkv, D, chunk))
+    if staging is None:
+        staging = torch.empty(max(need, 16), dtype=torch.uint8, device=kv.device)
+    cs = _stream(compute_stream)
+    xs = _stream(copy_stream) if copy_stream is not None else cs
+    _check(lib().lynx_encode_to_host(_ptr(kv), n_pages, page_tokens, Hkv, D, chunk, alpha, group_pages,
+                                     _ptr(staging), staging.numel(), ctypes.c_void_p(anchor_host.data_ptr()),
+                                     ctypes.c_void_p(residual_host.data_ptr()), cs, xs), "lynx_encode_to_host")
+    return anchor_host, residual_host
 
 
 def decode_anchor(anchor, n_pages: int, page_tokens: int, kv_heads: int, head_dim: int, chunk: int, alpha: float,

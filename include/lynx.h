@@ -166,6 +166,39 @@ int lynx_attn_anchor(const void* q_dev, const void* k_anchor_dev, const void* v_
                      void* hip_stream);
 
 /*
+ * Staging bytes lynx_encode_to_host needs for groups of group_pages pages: two groups'
+ * anchor + residual segments.  0 for an invalid geometry.
+ */
+size_t lynx_encode_to_host_staging_bytes(int group_pages, int page_tokens, int kv_heads, int head_dim, int chunk);
+
+/*
+ * Encode a request page group by page group and copy each group's streams to host memory
+ * while the next group is encoded ([Review] Implementation Notes: ping-pong double
+ * buffering, quantisation of one buffer while the other is transferred; Mechanism 2:
+ * the anchor stream is sent ahead of the residual stream).
+ *   kv_dev        : BF16 [n_pages * page_tokens][kv_heads][head_dim], as for lynx_encode.
+ *   group_pages   : pages per group (> 0); the last group may be shorter.
+ *   staging_dev   : device buffer of at least lynx_encode_to_host_staging_bytes(min(group_pages,
+ *                   n_pages), ...) bytes, 16-byte aligned; the two group buffers alternate.
+ *   anchor_host   : n_pages anchor segments, written in page order; residual_host likewise.
+ *                   Page-locked (pinned) host memory makes the copies asynchronous.
+ *   compute_stream: encodes run here; copy_stream: the copies (anchor segments of a group,
+ *                   then its residual segments) run here, each group after its encode.
+ *                   The two may be the same stream (no overlap).
+ * Asynchronous: the host buffers are complete once copy_stream's work so far has finished.
+ * The first encodes wait for the work already queued on copy_stream, so back-to-back calls
+ * may share one staging buffer.  Measured on ROCm 7 with 16 groups per call: queueing
+ * several calls ahead without waiting for copy_stream slowed the copies down up to ~4x;
+ * waiting between requests keeps them at the copy engine's rate.
+ * Errors: those of lynx_encode (checked once for the whole request); LYNX_EINVAL for
+ * group_pages <= 0 or a null host pointer; LYNX_EALIGN; LYNX_ENOSPACE for a small staging
+ * buffer; LYNX_ELAUNCH if a HIP call fails (work already enqueued stays enqueued).
+ */
+int lynx_encode_to_host(const void* kv_dev, int n_pages, int page_tokens, int kv_heads, int head_dim, int chunk,
+                        float alpha, int group_pages, void* staging_dev, size_t staging_bytes, void* anchor_host,
+                        void* residual_host, void* compute_stream, void* copy_stream);
+
+/*
  * lynx_attn_anchor over a paged cache with per-sequence lengths (the paged-attention
  * block layout of the serving engines the pages integrate with, [Review] Implementation
  * Notes: KV page granularity of 256 tokens as in paged attention).

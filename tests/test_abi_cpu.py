@@ -210,3 +210,22 @@ def test_attention_paged_validation():
     assert paged(maxp=1 << 24) == lynx.LYNX_EUNSUPPORTED          # max_pages * P overflows int
     assert paged() == lynx.LYNX_ENOSPACE
     assert paged(B=0) == lynx.LYNX_OK
+
+
+def test_encode_to_host_validation_and_staging():
+    L = lynx.lib()
+    a, r = lynx.stream_sizes(256, 2, 128, 64)
+    assert L.lynx_encode_to_host_staging_bytes(4, 256, 2, 128, 64) == 2 * 4 * (a + r)
+    assert L.lynx_encode_to_host_staging_bytes(0, 256, 2, 128, 64) == 0
+    assert L.lynx_encode_to_host_staging_bytes(4, 256, 2, 64, 64) == 0
+
+    def call(n=4, gp=2, staging=GOOD, sbytes=1 << 40, ah=GOOD, rh=GOOD, C=64, kv=GOOD):
+        return L.lynx_encode_to_host(kv, n, 256, 2, 128, C, 255.0, gp, staging, sbytes, ah, rh, None, None)
+    assert call(gp=0) == lynx.LYNX_EINVAL
+    assert call(ah=None) == lynx.LYNX_EINVAL
+    assert call(C=48) == lynx.LYNX_EINVAL                    # P % C
+    assert call(C=12) == lynx.LYNX_EINVAL                    # 256 % 12 != 0
+    assert call(staging=ODD) == lynx.LYNX_EALIGN
+    assert call(kv=ODD) == lynx.LYNX_EALIGN
+    assert call(sbytes=2 * 2 * (a + r) - 1) == lynx.LYNX_ENOSPACE
+    assert call(n=0) == lynx.LYNX_OK
