@@ -290,4 +290,16 @@ int lynx_attn_verify(const void* q_dev, const void* k_anchor_dev, const void* k_
                        ws_bytes, out_dtype, out_dev, lse_dev, static_cast<hipStream_t>(hip_stream));
 }
 
+int lynx_attn_verify_paged(const void* q_dev, const void* k_anchor_pool_dev, const void* k_residual_pool_dev,
+                           const void* v_anchor_pool_dev, const void* v_residual_pool_dev, int n_pool_pages,
+                           const int32_t* block_table_dev, const int32_t* seq_lens_dev, int batch, int n_query,
+                           int max_pages_per_seq, int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk,
+                           float alpha, float sm_scale, void* workspace_dev, size_t ws_bytes, int out_dtype,
+                           void* out_dev, float* lse_dev, void* hip_stream) {
+  return verify_paged_launch(q_dev, k_anchor_pool_dev, k_residual_pool_dev, v_anchor_pool_dev, v_residual_pool_dev,
+                             n_pool_pages, block_table_dev, seq_lens_dev, batch, n_query, max_pages_per_seq, q_heads,
+                             kv_heads, head_dim, page_tokens, chunk, alpha, sm_scale, workspace_dev, ws_bytes,
+                             out_dtype, out_dev, lse_dev, static_cast<hipStream_t>(hip_stream));
+}
+
 }  // extern "C"

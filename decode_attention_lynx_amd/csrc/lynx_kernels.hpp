@@ -33,5 +33,10 @@ int verify_launch(const void* q_dev, const void* k_anchor_dev, const void* k_res
                   const void* v_residual_dev, int batch, int n_query, int ctx_tokens, int q_heads, int kv_heads,
                   int head_dim, int page_tokens, int chunk, float alpha, float sm_scale, void* workspace_dev,
                   size_t ws_bytes, int out_dtype, void* out_dev, float* lse_dev, hipStream_t stream);
+int verify_paged_launch(const void* q_dev, const void* k_anchor_pool, const void* k_residual_pool,
+                        const void* v_anchor_pool, const void* v_residual_pool, int n_pool, const int32_t* block_table,
+                        const int32_t* seq_lens, int batch, int n_query, int max_pages, int q_heads, int kv_heads,
+                        int head_dim, int page_tokens, int chunk, float alpha, float sm_scale, void* workspace_dev,
+                        size_t ws_bytes, int out_dtype, void* out_dev, float* lse_dev, hipStream_t stream);
 
 }  // namespace lynx

@@ -78,6 +78,12 @@ struct VerifyArgs {
   int splits, tiles_per_split, ntiles;
   float qscale;                            // sm_scale * log2(e): scores kept in base 2
   int out_f32;
+  // paged form: sequence b's page p is pool segment block_table[b * max_pages + p] (clamped
+  // into [0, n_pool)) of both streams, and only its first seq_lens[b] tokens (clamped into
+  // [0, npages * P]) count.  Contiguous form: both null, segment b * npages + p.
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int max_pages, n_pool;
   float lut32[256];                        // S|x| of the full code n = anchor | residual << 4
 };
 
@@ -119,7 +125,12 @@ __device__ __forceinline__ TileAddr tile_addr(const VerifyArgs& a, int b, int kv
   const int page = tok / a.P;
   const int tin = tok - page * a.P;
   TileAddr t;
-  t.seg = (size_t)b * a.npages + page;
+  if (a.block_table == nullptr) {
+    t.seg = (size_t)b * a.npages + page;
+  } else {
+    const int sg = a.block_table[(size_t)b * a.max_pages + page];
+    t.seg = (size_t)min(max(sg, 0), a.n_pool - 1);
+  }
   t.row0 = ((size_t)kvh * a.P + tin) * (kHeadDim / 2);
   t.kc = tin / a.C;
   return t;
@@ -342,10 +353,13 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
   }
   int E_acc = 0;
 
+  // this sequence's context: all tiles, or its own length in the paged form
+  const int seq_len = a.seq_lens == nullptr ? a.ntiles * kVTile : min(max(a.seq_lens[b], 0), a.ntiles * kVTile);
   const int t_begin = split * a.tiles_per_split;
-  const int t_end = min(a.ntiles, t_begin + a.tiles_per_split);
+  const int t_end = min((seq_len + kVTile - 1) / kVTile, t_begin + a.tiles_per_split);
   const int t_last = t_end - 1;         // loads past the split's end re-read its last tile (unused)
-  const int nt = t_end - t_begin;
+  const int nt = t_end - t_begin;       // workgroup-uniform; <= 0 past a short sequence: no tiles
+  if (nt > 0) {
 
   // prologue: maps of tiles 0 and 1, codes of tiles 0 and 1, tile 0 decoded into buffer 0
   const bool mapper = wave < 2;          // wave-uniform
@@ -396,6 +410,14 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[gq][4 * mb + e] = acc[gq][e];
         __builtin_amdgcn_sched_barrier(0);   // bound the key fragments held in registers
+      }
+      if ((t_begin + i + 1) * kVTile > seq_len) {   // the sequence ends inside this tile: mask the tail
+        const int tok0 = (t_begin + i) * kVTile;
+#pragma unroll
+        for (int gq = 0; gq < kVGroups; ++gq)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (tok0 + 16 * (e >> 2) + 4 * g + (e & 3) >= seq_len) s[gq][e] = -INFINITY;
       }
 
       // ---- online softmax: p = 2^(s - m_run), the maximum moved (and o, l rescaled) only
@@ -469,6 +491,7 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
     step(i, 0);
     if (i + 1 < nt) step(i + 1, 1);
   }
+  }   // nt > 0
 
   // ---- this split's partial records for the lane's rows: (m, l, o[d]) with d = 16j + 4g + e
   const float oscale = ldexpf(1.0f, E_acc);
@@ -503,14 +526,14 @@ __global__ __launch_bounds__(kHeadDim) void k_verify_combine(VerifyArgs a) {
     o = fmaf(r[4 + d], f, o);
     l = fmaf(r[1], f, l);
   }
-  const float res = o / l;
+  const float res = l > 0.0f ? o / l : 0.0f;   // an empty context gives 0 (and LSE -inf)
   if (a.out_f32) static_cast<float*>(a.out)[(size_t)row * kHeadDim + d] = res;
   else {
     const uint32_t u = __float_as_uint(res);
     static_cast<uint16_t*>(a.out)[(size_t)row * kHeadDim + d] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
   }
   // natural-log LSE of the scaled scores: the partials are in base 2
-  if (a.lse && d == 0) a.lse[row] = (M2 + __log2f(l)) * 0.69314718055994531f;
+  if (a.lse && d == 0) a.lse[row] = l > 0.0f ? (M2 + __log2f(l)) * 0.69314718055994531f : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -553,10 +576,14 @@ size_t verify_workspace_bytes(int batch, int n_query, int ctx, int Hq, int Hkv, 
   return (size_t)batch * n_query * Hq * pl.splits * kRec * sizeof(float);
 }
 
-int verify_launch(const void* q_dev, const void* k_anchor_dev, const void* k_residual_dev, const void* v_anchor_dev,
-                  const void* v_residual_dev, int batch, int n_query, int ctx_tokens, int q_heads, int kv_heads,
-                  int head_dim, int page_tokens, int chunk, float alpha, float sm_scale, void* workspace_dev,
-                  size_t ws_bytes, int out_dtype, void* out_dev, float* lse_dev, hipStream_t stream) {
+namespace {
+
+int verify_launch_common(const void* q_dev, const void* k_anchor_dev, const void* k_residual_dev,
+                         const void* v_anchor_dev, const void* v_residual_dev, int batch, int n_query, int ctx_tokens,
+                         int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk, float alpha,
+                         float sm_scale, void* workspace_dev, size_t ws_bytes, int out_dtype, void* out_dev,
+                         float* lse_dev, const int32_t* block_table, const int32_t* seq_lens, int max_pages,
+                         int n_pool, hipStream_t stream) {
   if (batch < 0 || n_query <= 0 || ctx_tokens <= 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 ||
       page_tokens <= 0 || chunk <= 0)
     return LYNX_EINVAL;
@@ -582,6 +609,10 @@ int verify_launch(const void* q_dev, const void* k_anchor_dev, const void* k_res
   VerifyArgs a;
   std::memset(&a, 0, sizeof(a));
   a.q = static_cast<const uint16_t*>(q_dev);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.max_pages = max_pages;
+  a.n_pool = n_pool;
   a.kanc = static_cast<const uint8_t*>(k_anchor_dev);
   a.kres = static_cast<const uint8_t*>(k_residual_dev);
   a.vanc = static_cast<const uint8_t*>(v_anchor_dev);
@@ -631,6 +662,32 @@ int verify_launch(const void* q_dev, const void* k_anchor_dev, const void* k_res
   e = hipLaunchKernel(reinterpret_cast<const void*>(&k_verify_combine), dim3((unsigned)(batch * n_query * q_heads)),
                       dim3(kHeadDim), kargs, 0, stream);
   return e == hipSuccess ? LYNX_OK : LYNX_ELAUNCH;
+}
+
+}  // namespace
+
+int verify_launch(const void* q_dev, const void* k_anchor_dev, const void* k_residual_dev, const void* v_anchor_dev,
+                  const void* v_residual_dev, int batch, int n_query, int ctx_tokens, int q_heads, int kv_heads,
+                  int head_dim, int page_tokens, int chunk, float alpha, float sm_scale, void* workspace_dev,
+                  size_t ws_bytes, int out_dtype, void* out_dev, float* lse_dev, hipStream_t stream) {
+  return verify_launch_common(q_dev, k_anchor_dev, k_residual_dev, v_anchor_dev, v_residual_dev, batch, n_query,
+                              ctx_tokens, q_heads, kv_heads, head_dim, page_tokens, chunk, alpha, sm_scale,
+                              workspace_dev, ws_bytes, out_dtype, out_dev, lse_dev, nullptr, nullptr, 0, 0, stream);
+}
+
+int verify_paged_launch(const void* q_dev, const void* k_anchor_pool, const void* k_residual_pool,
+                        const void* v_anchor_pool, const void* v_residual_pool, int n_pool, const int32_t* block_table,
+                        const int32_t* seq_lens, int batch, int n_query, int max_pages, int q_heads, int kv_heads,
+                        int head_dim, int page_tokens, int chunk, float alpha, float sm_scale, void* workspace_dev,
+                        size_t ws_bytes, int out_dtype, void* out_dev, float* lse_dev, hipStream_t stream) {
+  if (n_pool <= 0 || max_pages <= 0 || page_tokens <= 0) return LYNX_EINVAL;
+  if ((long long)max_pages * page_tokens > 0x7fffffffll) return LYNX_EUNSUPPORTED;
+  auto al4 = [](const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+  if (!al4(block_table) || !al4(seq_lens)) return LYNX_EALIGN;
+  return verify_launch_common(q_dev, k_anchor_pool, k_residual_pool, v_anchor_pool, v_residual_pool, batch, n_query,
+                              max_pages * page_tokens, q_heads, kv_heads, head_dim, page_tokens, chunk, alpha,
+                              sm_scale, workspace_dev, ws_bytes, out_dtype, out_dev, lse_dev, block_table, seq_lens,
+                              max_pages, n_pool, stream);
 }
 
 }  // namespace lynx

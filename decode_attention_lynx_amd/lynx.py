@@ -23,7 +23,8 @@ OUT_F32 = 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblynx.so")
 EXPORTS = ("lynx_strerror", "lynx_stream_sizes", "lynx_encode", "lynx_decode_anchor", "lynx_decode_full",
            "lynx_attn_workspace_bytes", "lynx_attn_anchor", "lynx_attn_verify_workspace_bytes", "lynx_attn_verify",
-           "lynx_attn_anchor_paged", "lynx_encode_to_host_staging_bytes", "lynx_encode_to_host")
+           "lynx_attn_anchor_paged", "lynx_encode_to_host_staging_bytes", "lynx_encode_to_host",
+           "lynx_attn_verify_paged")
 
 _lib = None
 
@@ -67,6 +68,9 @@ def lib() -> ctypes.CDLL:
         L.lynx_attn_anchor_paged.restype = c_int
         L.lynx_attn_anchor_paged.argtypes = [c_void, c_void, c_void, c_int, c_void, c_void] + [c_int] * 7 + [
             c_float, c_float, c_void, c_size, c_int, c_void, c_void]
+        L.lynx_attn_verify_paged.restype = c_int
+        L.lynx_attn_verify_paged.argtypes = [c_void] * 5 + [c_int, c_void, c_void] + [c_int] * 8 + [
+            c_float, c_float, c_void, c_size, c_int, c_void, c_void, c_void]
         L.lynx_attn_verify_workspace_bytes.restype = c_size
         L.lynx_attn_verify_workspace_bytes.argtypes = [c_int] * 8
         L.lynx_attn_verify.restype = c_int
@@ -246,4 +250,32 @@ def attn_verify(q, k_anchor, k_residual, v_anchor, v_residual, ctx_tokens: int, 
                                   ctx_tokens, Hq, kv_heads, D, page_tokens, chunk, alpha, sm_scale, _ptr(workspace),
                                   workspace.numel(), code, _ptr(out), _ptr(lse), _stream(stream)),
            "lynx_attn_verify")
+    return out, lse
+
+
+def attn_verify_paged(q, k_anchor_pool, k_residual_pool, v_anchor_pool, v_residual_pool, block_table, seq_lens,
+                      kv_heads: int, page_tokens: int, chunk: int, alpha: float, sm_scale: float = 0.0,
+                      out_dtype=None, want_lse: bool = True, workspace=None, out=None, lse=None, stream=None):
+    """q: CUDA bfloat16 [B, M, Hq, D]; pools: [n_pool, seg] uint8 each; block_table: CUDA int32 [B, max_pages];
+    seq_lens: CUDA int32 [B].  Returns (O [B, M, Hq, D], lse [B, M, Hq] or None)."""
+    import torch
+    B, M, Hq, D = q.shape
+    n_pool = k_anchor_pool.shape[0]
+    max_pages = block_table.shape[1]
+    ws = attn_verify_workspace_bytes(B, M, max_pages * page_tokens, Hq, kv_heads, D, page_tokens, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
+    dt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, M, Hq, D), dtype=dt, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((B, M, Hq), dtype=torch.float32, device=q.device)
+    if not want_lse:
+        lse = None
+    code = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
+    _check(lib().lynx_attn_verify_paged(_ptr(q), _ptr(k_anchor_pool), _ptr(k_residual_pool), _ptr(v_anchor_pool),
+                                        _ptr(v_residual_pool), n_pool, _ptr(block_table), _ptr(seq_lens), B, M,
+                                        max_pages, Hq, kv_heads, D, page_tokens, chunk, alpha, sm_scale,
+                                        _ptr(workspace), workspace.numel(), code, _ptr(out), _ptr(lse),
+                                        _stream(stream)), "lynx_attn_verify_paged")
     return out, lse

@@ -259,6 +259,23 @@ int lynx_attn_verify(const void* q_dev, const void* k_anchor_dev, const void* k_
                      int chunk, float alpha, float sm_scale, void* workspace_dev, size_t ws_bytes,
                      int out_dtype, void* out_dev, float* lse_dev, void* hip_stream);
 
+/*
+ * lynx_attn_verify over a paged cache with per-sequence lengths (as lynx_attn_anchor_paged):
+ * the anchor and residual pools hold n_pool_pages segments each, and pool segment s of both
+ * streams is the same page.  block_table_dev int32 [batch][max_pages_per_seq] and seq_lens_dev
+ * int32 [batch] as for lynx_attn_anchor_paged (clamped entries; a sequence's tail is masked;
+ * an empty context gives O = 0 and LSE = -inf).  Workspace:
+ * lynx_attn_verify_workspace_bytes(batch, n_query, max_pages_per_seq * page_tokens, ...).
+ * Errors: those of lynx_attn_verify; LYNX_EINVAL for n_pool_pages or max_pages_per_seq <= 0;
+ * LYNX_EALIGN for a null or misaligned block table or length array.
+ */
+int lynx_attn_verify_paged(const void* q_dev, const void* k_anchor_pool_dev, const void* k_residual_pool_dev,
+                           const void* v_anchor_pool_dev, const void* v_residual_pool_dev, int n_pool_pages,
+                           const int32_t* block_table_dev, const int32_t* seq_lens_dev, int batch, int n_query,
+                           int max_pages_per_seq, int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk,
+                           float alpha, float sm_scale, void* workspace_dev, size_t ws_bytes, int out_dtype,
+                           void* out_dev, float* lse_dev, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -474,3 +474,28 @@ def attention_verify(q_bits: np.ndarray, k_anchor: np.ndarray, k_residual: np.nd
         Vh = decode_full(va[b], vr[b], n_pages, P, Hkv, D, C, alpha)
         O[b], lse[b] = attention_lse(q[b], Kh, Vh, sm_scale)
     return O, lse
+
+
+def attention_verify_paged(q_bits: np.ndarray, ka_pool: np.ndarray, kr_pool: np.ndarray, va_pool: np.ndarray,
+                           vr_pool: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray, Hq: int, Hkv: int,
+                           D: int, P: int, C: int, alpha: float, sm_scale: float | None = None):
+    """The verification pass over a paged cache with per-sequence lengths.
+
+    q_bits [B, M, Hq, D]; pools of anchor / residual segments ([n_pool, seg], pool segment s of both
+    streams is one page); block_table [B, max_pages]; seq_lens [B].  Sequence b's context is the
+    first seq_lens[b] tokens of its pages in order.  Returns (O, lse); an empty context gives O = 0
+    and lse = -inf.
+    """
+    q = bf16_bits_to_f64(q_bits)
+    B, M = q.shape[:2]
+    O = np.zeros((B, M, Hq, D), dtype=np.float64)
+    lse = np.full((B, M, Hq), -np.inf)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n <= 0:
+            continue
+        pages = [int(x) for x in block_table[b, :(n + P - 1) // P]]
+        Kh = decode_full(np.asarray(ka_pool)[pages], np.asarray(kr_pool)[pages], len(pages), P, Hkv, D, C, alpha)
+        Vh = decode_full(np.asarray(va_pool)[pages], np.asarray(vr_pool)[pages], len(pages), P, Hkv, D, C, alpha)
+        O[b], lse[b] = attention_lse(q[b], Kh[:n], Vh[:n], sm_scale)
+    return O, lse

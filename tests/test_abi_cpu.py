@@ -229,3 +229,17 @@ def test_encode_to_host_validation_and_staging():
     assert call(kv=ODD) == lynx.LYNX_EALIGN
     assert call(sbytes=2 * 2 * (a + r) - 1) == lynx.LYNX_ENOSPACE
     assert call(n=0) == lynx.LYNX_OK
+
+
+def test_verify_paged_validation():
+    def call(B=2, M=4, maxp=4, n_pool=8, bt=GOOD, sl=GOOD, P=256, C=64, D=128):
+        return lynx.lib().lynx_attn_verify_paged(GOOD, GOOD, GOOD, GOOD, GOOD, n_pool, bt, sl, B, M, maxp, 16, 2, D,
+                                                 P, C, 255.0, 0.0, GOOD, 0, lynx.OUT_F32, GOOD, None, None)
+    assert call(n_pool=0) == lynx.LYNX_EINVAL
+    assert call(maxp=0) == lynx.LYNX_EINVAL
+    assert call(bt=None) == lynx.LYNX_EALIGN
+    assert call(sl=ctypes.c_void_p(GOOD.value + 2)) == lynx.LYNX_EALIGN
+    assert call(C=16) == lynx.LYNX_EUNSUPPORTED
+    assert call(maxp=1 << 24) == lynx.LYNX_EUNSUPPORTED
+    assert call() == lynx.LYNX_ENOSPACE
+    assert call(B=0) == lynx.LYNX_OK

@@ -189,3 +189,38 @@ def test_verify_full_size_sampled(gpu):
                                             C, alpha)
         bound = lse_bound(qb[b:b + 1], KA[sl], KR[sl], 1, M, T, Hq, Hkv, P, C, alpha)
         check(got[b:b + 1], got_lse[b:b + 1], ref_o, ref_lse, bound, f"seq {b}")
+
+
+@pytest.mark.parametrize("C", [64, 32])
+def test_verify_paged_variable_lengths(gpu, C):
+    """A shuffled pool of pages behind a block table, with lengths ending inside a tile, on a tile
+    edge, inside a page, at one token and at zero (O = 0, LSE = -inf)."""
+    B, M, Hq, Hkv, P, maxp, alpha = 6, 3, 16, 2, 256, 4, 255.0
+    lens = np.array([1, 63, 64, 300, maxp * P, 0], dtype=np.int32)
+    print(f"[verify-paged] C={C} lens={lens.tolist()}", flush=True)
+    T = maxp * P
+    qb, ka, kr, va, vr = make_case(B, M, Hq, Hkv, T, P, C, alpha, seed=41)
+    perm = np.random.default_rng(C + 1).permutation(B * maxp)
+    bt = np.argsort(perm)[np.arange(B * maxp).reshape(B, maxp)].astype(np.int32)
+    bt[0, 1:] = -1                                   # pages past a sequence's end are not read
+    ref_o, ref_l = o.attention_verify_paged(qb, ka[perm], kr[perm], va[perm], vr[perm], bt, lens, Hq, Hkv, 128, P,
+                                            C, alpha)
+    out, lse = lynx.attn_verify_paged(bf16_tensor(qb), upload(ka[perm]), upload(kr[perm]), upload(va[perm]),
+                                      upload(vr[perm]), torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(),
+                                      Hkv, P, C, alpha, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got_o, got_l = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            assert np.all(got_o[b] == 0.0) and np.all(got_l[b] == -np.inf)
+            continue
+        npg = (n + P - 1) // P
+        # the LSE bound of lse_bound, on this sequence's first n tokens
+        idx = np.arange(b * maxp, b * maxp + npg)
+        K = np.abs(o.decode_full(ka[idx], kr[idx], npg, P, Hkv, 128, C, alpha)[:n])
+        q = np.abs(o.bf16_bits_to_f64(qb[b]))
+        G = Hq // Hkv
+        bound = np.stack([(q[:, h * G:(h + 1) * G].reshape(-1, 128) @ K[:, h, :].T).max(axis=1).reshape(M, G)
+                          for h in range(Hkv)], axis=1).reshape(M, Hq) * 2.0 ** -15 / np.sqrt(128)
+        check(got_o[b:b + 1], got_l[b:b + 1], ref_o[b:b + 1], ref_l[b:b + 1], bound[None], f"seq {b} len {n}")

@@ -474,3 +474,27 @@ def test_attention_anchor_paged_matches_contiguous():
     got = o.attention_anchor_paged(qb, ka, va, ident, np.array([2 * P, 0, T]), Hq, Hkv, 128, P, C, alpha)
     assert np.allclose(got[0], two[0], rtol=0, atol=1e-12)
     assert np.all(got[1] == 0.0)
+
+
+def test_attention_verify_paged_matches_contiguous():
+    """A shuffled pool behind a block table with full lengths reduces to the contiguous verification
+    pass; a length at a page boundary equals the pass over those pages; an empty context is (0, -inf)."""
+    from decode_attention_lynx_amd import synth
+    B, M, Hq, Hkv, T, P, C, alpha = 2, 3, 8, 2, 512, 128, 64, 255.0
+    kb = np.concatenate([synth.make_kv_np(T, Hkv, 128, seed=6, layer=b, kv_idx=0) for b in range(B)])
+    vb = np.concatenate([synth.make_kv_np(T, Hkv, 128, seed=6, layer=b, kv_idx=1) for b in range(B)])
+    ka, kr, _ = o.encode(kb, P, C, alpha)
+    va, vr, _ = o.encode(vb, P, C, alpha)
+    qb = synth.make_q_np(B * M, Hq, 128, seed=6).reshape(B, M, Hq, 128)
+    npg = T // P
+    ref_o, ref_l = o.attention_verify(qb, ka, kr, va, vr, B, M, T, Hq, Hkv, 128, P, C, alpha)
+    perm = np.random.default_rng(1).permutation(B * npg)
+    bt = np.argsort(perm)[np.arange(B * npg).reshape(B, npg)]
+    got_o, got_l = o.attention_verify_paged(qb, ka[perm], kr[perm], va[perm], vr[perm], bt, np.full(B, T), Hq, Hkv,
+                                            128, P, C, alpha)
+    assert np.allclose(got_o, ref_o, rtol=0, atol=1e-12) and np.allclose(got_l, ref_l, rtol=0, atol=1e-12)
+    one_o, one_l = o.attention_verify(qb[:1], ka[:1], kr[:1], va[:1], vr[:1], 1, M, P, Hq, Hkv, 128, P, C, alpha)
+    got_o, got_l = o.attention_verify_paged(qb, ka, kr, va, vr, np.arange(B * npg).reshape(B, npg),
+                                            np.array([P, 0]), Hq, Hkv, 128, P, C, alpha)
+    assert np.allclose(got_o[0], one_o[0], rtol=0, atol=1e-12) and np.allclose(got_l[0], one_l[0], rtol=0, atol=1e-12)
+    assert np.all(got_o[1] == 0.0) and np.all(got_l[1] == -np.inf)
