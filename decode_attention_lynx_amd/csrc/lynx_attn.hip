@@ -16,9 +16,9 @@
 // a dense contraction over the raw nibble table values, which runs on MFMA.
 // Likewise sum_t p_t v_hat[t,d] = A_V[c,d] sum_t p_t L[n_td] + B_V[c,d] sum_t p_t.
 //
-// Decomposition: one workgroup (8 waves) per (sequence, kv head, context split);
+// Decomposition: one workgroup (12 waves) per (sequence, kv head, context split);
 // each wave walks 64-token tiles (one tile lies inside one chunk because the
-// chunk is a multiple of 64) with an online softmax, the 8 waves merge in LDS
+// chunk is a multiple of 64) with an online softmax, the 12 waves merge in LDS
 // and write one partial (m, l, o[128]) per query head; k_attn_combine merges the
 // splits with the log-sum-exp rule.
 //
@@ -42,7 +42,7 @@ namespace lynx {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kAttnWaves = 8;
+constexpr int kAttnWaves = 12;          // three per SIMD
 constexpr int kAttnWorkgroups = 256;   // workgroups the context splits aim for
 constexpr int kMaxGroup = 8;         // query heads per kv head handled by one workgroup
 
@@ -179,7 +179,7 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int
 }
 
 template <int TILE>
-__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_anchor(AttnArgs a) {
+__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void k_attn_anchor(AttnArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile addressing stays scalar
@@ -200,7 +200,6 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   __shared__ float4 s_vab[kAttnWaves][kHeadDim / 2];
   uint32_t* s_pair = s_big;
 
-  static_assert(kPairWords % (kAttnWaves * 64) == 0, "the table fill covers the table exactly");
 #pragma unroll 8
   for (int w = tid; w < kPairWords; w += kAttnWaves * 64) s_pair[w] = a.pair[w >> 6];   // word 64e + r: entry e, copy r
   const uint32_t lane4 = 4u * (uint32_t)lane;
@@ -366,22 +365,12 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
     __builtin_amdgcn_wave_barrier();   // the next tile rewrites this wave's (A, B) tables
   };
 
-  // tiles t_begin + wave, + kAttnWaves, ...: two buffers in turn, the next tile's loads in
-  // flight while the current one is processed
-  TileIn<TILE> tb[2];
-  int tile = t_begin + wave;
-  const int t_last = t_end - 1;    // loads past the wave's last tile re-read that tile (in bounds, unused)
-  if (t_begin < t_end) {           // workgroup-uniform: a split past a short sequence loads nothing
-    load_tile(a, b, kvh, min(tile, t_last), toff, tb[0]);
-    load_tile(a, b, kvh, min(tile + kAttnWaves, t_last), toff, tb[1]);
-  }
-  while (tile < t_end) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (tile < t_end) process(tb[i], tile);
-      load_tile(a, b, kvh, min(tile + 2 * kAttnWaves, t_last), toff, tb[i]);
-      tile += kAttnWaves;
-    }
+  // tiles t_begin + wave, + kAttnWaves, ...: one tile buffer per wave; three waves per SIMD
+  // hide each other's load latency (a second buffer would cost the third wave's registers)
+  TileIn<TILE> cur;
+  for (int tile = t_begin + wave; tile < t_end; tile += kAttnWaves) {
+    load_tile(a, b, kvh, tile, toff, cur);
+    process(cur, tile);
   }
 
   // ---- merge the waves (columns 0..G-1 hold the result; 8..15 duplicate them)
@@ -458,7 +447,7 @@ bool attn_plan(int batch, int ctx, int Hq, int Hkv, int D, int P, int C, AttnPla
   pl->tile = attn_tile(C);
   if (D != kHeadDim || pl->tile == 0 || Hq / Hkv > kMaxGroup) return false;
   pl->ntiles = ctx / pl->tile;
-  // One workgroup per compute unit of the 256-CU gfx950 parts (8 waves fill a CU at this
+  // One workgroup per compute unit of the 256-CU gfx950 parts (12 waves fill a CU at this
   // kernel's register use): long-lived workgroups, one table fill and one merge each.
   const long long units = (long long)batch * Hkv;
   int want = (int)((kAttnWorkgroups + units - 1) / units);
