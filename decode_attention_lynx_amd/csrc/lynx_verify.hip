@@ -57,6 +57,7 @@ constexpr int kVWaves = 8;                 // waves per workgroup
 constexpr int kVThreads = kVWaves * 64;
 constexpr int kVGroups = 2;                // MFMA column groups (16 rows each) per wave
 constexpr int kVRows = 16 * kVGroups * kVWaves;   // query rows per workgroup (256)
+static_assert(kVThreads == 512, "the tile decode maps 512 threads onto 64 tokens x 128 channels");
 constexpr int kVTile = 64;                 // context tokens per step
 constexpr int kLutCopies = 16;             // copies of each table entry (lane l reads copy l % 16)
 constexpr int kRec = kHeadDim + 4;         // floats per partial record (o 16-byte aligned)
@@ -560,11 +561,21 @@ bool verify_plan(int batch, int n_query, int ctx, int Hq, int Hkv, int D, int P,
   const long long R = (long long)n_query * (Hq / Hkv);
   pl->rowblocks = (int)((R + kVRows - 1) / kVRows);
   pl->ntiles = ctx / kVTile;
+  // Split the context so that rounds of kVWorkgroups workgroups x tiles per split is least
+  // (ties: fewer splits, less merging).
   const long long units = (long long)batch * Hkv * pl->rowblocks;
-  int want = (int)((kVWorkgroups + units - 1) / units);
-  want = std::max(1, std::min(want, pl->ntiles));
-  pl->tiles_per_split = (pl->ntiles + want - 1) / want;
-  pl->splits = (pl->ntiles + pl->tiles_per_split - 1) / pl->tiles_per_split;
+  long long best_cost = -1;
+  for (int want = 1; want <= pl->ntiles && want <= 4096; ++want) {
+    const int tps = (pl->ntiles + want - 1) / want;
+    const int splits = (pl->ntiles + tps - 1) / tps;
+    const long long rounds = (units * splits + kVWorkgroups - 1) / kVWorkgroups;
+    const long long cost = rounds * tps;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      pl->tiles_per_split = tps;
+      pl->splits = splits;
+    }
+  }
   return true;
 }
 
