@@ -449,11 +449,20 @@ bool attn_plan(int batch, int ctx, int Hq, int Hkv, int D, int P, int C, AttnPla
   pl->ntiles = ctx / pl->tile;
   // One workgroup per compute unit of the 256-CU gfx950 parts (12 waves fill a CU at this
   // kernel's register use): long-lived workgroups, one table fill and one merge each.
+  // The split count minimises rounds of workgroups x tiles per split (ties: fewer splits).
   const long long units = (long long)batch * Hkv;
-  int want = (int)((kAttnWorkgroups + units - 1) / units);
-  want = std::max(1, std::min(want, pl->ntiles));
-  pl->tiles_per_split = (pl->ntiles + want - 1) / want;
-  pl->splits = (pl->ntiles + pl->tiles_per_split - 1) / pl->tiles_per_split;   // no empty split
+  long long best_cost = -1;
+  for (int want = 1; want <= pl->ntiles && want <= 4096; ++want) {
+    const int tps = (pl->ntiles + want - 1) / want;
+    const int splits = (pl->ntiles + tps - 1) / tps;            // no empty split
+    const long long rounds = (units * splits + kAttnWorkgroups - 1) / kAttnWorkgroups;
+    const long long cost = rounds * tps;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      pl->tiles_per_split = tps;
+      pl->splits = splits;
+    }
+  }
   return true;
 }
 
