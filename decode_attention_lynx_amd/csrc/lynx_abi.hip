@@ -35,6 +35,7 @@ int check_geometry(int n_pages, int P, int Hkv, int D, int C, float alpha, Geome
   if (!std::isfinite(alpha) || !(alpha > 0.0f)) return LYNX_EINVAL;
   if (D != kHeadDim) return LYNX_EUNSUPPORTED;
   if (!pow2_chunk(C)) return LYNX_EUNSUPPORTED;
+  if ((long long)P * Hkv * kHeadDim / 2 > 0x7fffffffll) return LYNX_EUNSUPPORTED;   // page byte counts in int
   if ((long long)n_pages * Hkv * ((P + kDecTile - 1) / kDecTile) > 0x7fffffffll ||
       (long long)n_pages * Hkv * (kHeadDim / kSlab) > 0x7fffffffll)
     return LYNX_EUNSUPPORTED;
@@ -76,7 +77,7 @@ const char* lynx_strerror(int status) {
   switch (status) {
     case LYNX_OK: return "ok";
     case LYNX_EINVAL: return "invalid argument (size, count, chunk, alpha, selector or dtype)";
-    case LYNX_EALIGN: return "null or misaligned pointer (16-byte alignment required)";
+    case LYNX_EALIGN: return "null or misaligned pointer (16-byte for data, 4-byte for index tables)";
     case LYNX_EUNSUPPORTED: return "shape not supported by this build";
     case LYNX_ENOSPACE: return "workspace too small";
     case LYNX_ELAUNCH: return "kernel launch failed";

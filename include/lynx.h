@@ -65,9 +65,10 @@ extern "C" {
 /* ---- status codes ------------------------------------------------------- */
 #define LYNX_OK            0
 #define LYNX_EINVAL       -1   /* bad size, count, chunk, alpha, selector or dtype */
-#define LYNX_EALIGN       -2   /* a pointer is NULL where data is required, or not 16-byte aligned */
+#define LYNX_EALIGN       -2   /* a pointer is NULL where data is required, or misaligned (16 bytes for
+                                   data buffers, 4 bytes for block tables and length arrays) */
 #define LYNX_EUNSUPPORTED -3   /* a valid shape this build does not implement (e.g. head_dim != 128) */
-#define LYNX_ENOSPACE     -4   /* workspace smaller than lynx_attn_workspace_bytes() */
+#define LYNX_ENOSPACE     -4   /* workspace or staging buffer smaller than its *_bytes() query */
 #define LYNX_ELAUNCH      -5   /* the HIP runtime rejected a kernel launch */
 
 /* ---- selectors ---------------------------------------------------------- */

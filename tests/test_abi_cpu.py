@@ -243,3 +243,11 @@ def test_verify_paged_validation():
     assert call(maxp=1 << 24) == lynx.LYNX_EUNSUPPORTED
     assert call() == lynx.LYNX_ENOSPACE
     assert call(B=0) == lynx.LYNX_OK
+
+
+def test_geometry_too_large_for_int_sizes():
+    """A page whose byte count does not fit an int is refused before any launch."""
+    L = lynx.lib()
+    assert L.lynx_encode(GOOD, 1, 1 << 16, 1 << 12, 128, 64, 255.0, 3, GOOD, GOOD, None) == lynx.LYNX_EUNSUPPORTED
+    assert L.lynx_decode_full(GOOD, GOOD, 1, 1 << 16, 1 << 12, 128, 64, 255.0, lynx.OUT_BF16, GOOD, None) == \
+        lynx.LYNX_EUNSUPPORTED
