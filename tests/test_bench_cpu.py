@@ -78,3 +78,12 @@ def test_load_traffic_rejects_a_stale_source_hash(tmp_path, monkeypatch):
     assert bench.load_traffic("encode") is None
     assert bench.load_traffic("decode_full") == 7
     assert bench.load_traffic("attn_anchor") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and says why, before touching a GPU."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
