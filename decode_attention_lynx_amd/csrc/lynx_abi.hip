@@ -22,8 +22,11 @@ namespace {
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// decode workgroups in flight: 8 per compute unit of the 256-CU MI355X; each walks a
-// contiguous range of 128-token tiles
+// decode workgroups: 8 per compute unit of the 256-CU MI355X, each walking a contiguous
+// range of 128-token tiles.  Registers (anchor decode) and the replicated table (full
+// decode) hold residency to 6 and 5 per CU, so the last ranges start late; a grid sized
+// to the residency, and prefetching the next tile's codes, measured no faster (the
+// decoders are bound by HBM writes)
 constexpr long long kDecodeWorkgroups = 2048;
 
 bool pow2_chunk(int c) { return c == 8 || c == 16 || c == 32 || c == 64 || c == 128 || c == 256; }

@@ -153,15 +153,17 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int
   const size_t row0 = ((size_t)kvh * a.P + tin) * (kHeadDim / 2);
   const uint8_t* kcb = a.kanc + seg + row0;
   const uint8_t* vcb = a.vanc + seg + row0;
+  // every code byte is read once: streaming loads, which keep the caches for the metadata
+  // (the page statistics are shared by all tiles of a page)
 #pragma unroll
-  for (int mb = 0; mb < TILE / 16; ++mb)
-    t.kw[mb] = *reinterpret_cast<const uint4*>(kcb + lo.kcode + 16 * mb * (kHeadDim / 2));
+  for (int mb = 0; mb < TILE / 16; ++mb) t.kw[mb] = ld_stream(kcb + lo.kcode + 16 * mb * (kHeadDim / 2));
 #pragma unroll
   for (int ks = 0; ks < TILE / 32; ++ks)
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int row = 32 * ks + (r < 4 ? r : 12 + r);     // + 4g (in the lane offset)
-      t.vw[8 * ks + r] = *reinterpret_cast<const uint32_t*>(vcb + lo.vcode + row * (kHeadDim / 2));
+      t.vw[8 * ks + r] =
+          __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vcb + lo.vcode + row * (kHeadDim / 2)));
     }
   const uint8_t* kmb = a.kanc + seg + a.codes + (size_t)kvh * kHeadDim * 4;
   const uint8_t* vmb = a.vanc + seg + a.codes + (size_t)kvh * kHeadDim * 4;
