@@ -81,7 +81,7 @@ const char* lynx_strerror(int status) {
     case LYNX_OK: return "ok";
     case LYNX_EINVAL: return "invalid argument (size, count, chunk, alpha, selector or dtype)";
     case LYNX_EALIGN: return "null or misaligned pointer (16-byte for data, 4-byte for index tables)";
-    case LYNX_EUNSUPPORTED: return "shape not supported by this build";
+    case LYNX_EUNSUPPORTED: return "shape not supported by this library";
     case LYNX_ENOSPACE: return "workspace too small";
     case LYNX_ELAUNCH: return "kernel launch failed";
     default: return "unknown status";

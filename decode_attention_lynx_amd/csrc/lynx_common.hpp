@@ -11,7 +11,7 @@
 
 namespace lynx {
 
-constexpr int kHeadDim = 128;        // head_dim supported by this build
+constexpr int kHeadDim = 128;        // head_dim supported by this library
 constexpr int kThreads = 256;        // workgroup size of the codec kernels
 constexpr int kSlab = 64;            // channels of one kv head handled by one codec workgroup
 constexpr int kDG = kSlab / 8;       // channel groups of 8 per slab (8)

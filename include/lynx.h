@@ -67,7 +67,7 @@ extern "C" {
 #define LYNX_EINVAL       -1   /* bad size, count, chunk, alpha, selector or dtype */
 #define LYNX_EALIGN       -2   /* a pointer is NULL where data is required, or misaligned (16 bytes for
                                    data buffers, 4 bytes for block tables and length arrays) */
-#define LYNX_EUNSUPPORTED -3   /* a valid shape this build does not implement (e.g. head_dim != 128) */
+#define LYNX_EUNSUPPORTED -3   /* a valid shape this library does not implement (e.g. head_dim != 128) */
 #define LYNX_ENOSPACE     -4   /* workspace or staging buffer smaller than its *_bytes() query */
 #define LYNX_ELAUNCH      -5   /* the HIP runtime rejected a kernel launch */
 
@@ -102,7 +102,7 @@ int lynx_stream_sizes(int page_tokens, int kv_heads, int head_dim, int chunk,
  * Per element: X_n = (X - gamma_min)/(gamma_scale + eps);
  * X_f = (X_n - mu)/(sigma + eps); Y = 127*ln(1 + alpha|X_f|)/ln(1 + alpha);
  * I = Round(Y); S = sign(X_f); then the split above.
- * Supported in this build: head_dim == 128 (else LYNX_EUNSUPPORTED).
+ * Supported by this library: head_dim == 128 (else LYNX_EUNSUPPORTED).
  */
 int lynx_encode(const void* kv_dev, int n_pages, int page_tokens, int kv_heads, int head_dim,
                 int chunk, float alpha, unsigned sel, void* anchor_dev, void* residual_dev,
@@ -152,13 +152,13 @@ size_t lynx_attn_workspace_bytes(int batch, int ctx_tokens, int q_heads, int kv_
  *   q_heads      : a multiple of kv_heads; query head hq reads kv head
  *                  hq / (q_heads/kv_heads).  Group size q_heads/kv_heads <= 8.
  *   ctx_tokens   : a positive multiple of page_tokens.
- *   chunk        : a multiple of 32 in this build (else LYNX_EUNSUPPORTED): each
+ *   chunk        : a multiple of 32 in this library (else LYNX_EUNSUPPORTED): each
  *                  wave step covers 64 tokens, or 32 when chunk == 32, inside one chunk.
  *   sm_scale     : > 0, or <= 0 to use 1/sqrt(head_dim).
  *   workspace_dev, ws_bytes : at least lynx_attn_workspace_bytes(...) bytes.
  *   out_dtype    : LYNX_OUT_BF16 or LYNX_OUT_F32.
  *   out_dev      : [batch][q_heads][head_dim] of out_dtype, written.
- * Supported in this build: head_dim == 128.
+ * Supported by this library: head_dim == 128.
  */
 int lynx_attn_anchor(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev,
                      int batch, int ctx_tokens, int q_heads, int kv_heads, int head_dim,
@@ -244,7 +244,7 @@ size_t lynx_attn_verify_workspace_bytes(int batch, int n_query, int ctx_tokens, 
  *                  segments; sequence b's context is the ctx_tokens/page_tokens
  *                  consecutive segments starting at segment b*(ctx_tokens/page_tokens).
  *   q_heads      : a multiple of kv_heads (query head hq reads kv head hq / (q_heads/kv_heads)).
- *   chunk        : a multiple of 64, or 32 with page_tokens a multiple of 64, in this build
+ *   chunk        : a multiple of 64, or 32 with page_tokens a multiple of 64, in this library
  *                  (else LYNX_EUNSUPPORTED).
  *   sm_scale     : > 0, or <= 0 to use 1/sqrt(head_dim).
  *   workspace_dev, ws_bytes : at least lynx_attn_verify_workspace_bytes(...) bytes.
@@ -252,7 +252,7 @@ size_t lynx_attn_verify_workspace_bytes(int batch, int n_query, int ctx_tokens, 
  *   lse_dev      : float32 [batch][n_query][q_heads], written; may be NULL.
  * Keys are formed in float32 and carried as BF16 high + low parts (~16 significant
  * bits); values as float16 table values with the affine map applied in float32.
- * Supported in this build: head_dim == 128.  Asynchronous on hip_stream.
+ * Supported by this library: head_dim == 128.  Asynchronous on hip_stream.
  */
 int lynx_attn_verify(const void* q_dev, const void* k_anchor_dev, const void* k_residual_dev,
                      const void* v_anchor_dev, const void* v_residual_dev, int batch, int n_query,
