@@ -27,6 +27,18 @@ def test_library_loads_and_exports_declared_symbols():
         assert hasattr(L, s), s
 
 
+def test_missing_library_fails_loudly(monkeypatch):
+    """No fallback: without the built library every entry point raises instead of computing."""
+    monkeypatch.setattr(lynx, "_lib", None)
+    monkeypatch.setattr(lynx, "LIB_PATH", os.path.join(ROOT, "no-such-dir", "liblynx.so"))
+    with pytest.raises(RuntimeError, match="not found"):
+        lynx.lib()
+    with pytest.raises(RuntimeError, match="not found"):
+        lynx.stream_sizes(256, 8, 128, 64)
+    with pytest.raises(RuntimeError, match="not found"):
+        lynx.attn_workspace_bytes(16, 32768, 64, 8, 128, 256, 64)
+
+
 def test_strerror():
     for st in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(lynx.strerror(st), str) and lynx.strerror(st)
