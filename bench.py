@@ -232,6 +232,91 @@ def cpu_baseline(budget_s: float = 15.0):
                       f"{T}-token prefix; {t_codec + t_attn:.1f} s of CPU time"}
 
 
+# The codec on the other request shapes (parity cases of the test suite), reported by
+# --codec-workloads: (name, layers, tokens per tensor, kv heads, page tokens, seed,
+# [(chunk, alpha)], one call per layer tensor)
+CODEC_WORKLOADS = [
+    ("single KV page pair: K and V of 4096 tokens x 8 kv heads x 128 (16.8 MB, cache-resident)",
+     1, 4096, 8, 4096, 0, [(64, 255.0)], False),
+    ("qwen-32b request: 64 layers x K,V x 16384 tokens x 8 kv heads x 128 (4.3 GB)",
+     64, 16384, 8, 256, 2, [(c, al) for c in (32, 64, 128) for al in (15.0, 63.0, 255.0)], False),
+    ("qwen3-235b long context: 94 layers x K,V x 131072 tokens x 4 kv heads x 128 (25.2 GB), "
+     "one call per layer tensor", 94, 131072, 4, 256, 3, [(64, 255.0)], True),
+]
+
+
+def codec_workloads(reps: int, warmup: int) -> dict:
+    """Encode and both decoders (BF16 out) on each workload of CODEC_WORKLOADS: median launch
+    time over `reps` event-timed repetitions (a repetition of a per-tensor workload covers all
+    its layer tensors), algorithmic GB/s and fraction of HBM peak."""
+    import torch
+    from decode_attention_lynx_amd import lynx, synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    rows = []
+    for name, layers, tokens, kvh, pt, seed, settings, per_tensor in CODEC_WORKLOADS:
+        print(f"[bench] codec workload: {name}", file=sys.stderr, flush=True)
+        n_t = 2 * layers
+        kv = torch.empty((n_t * tokens, kvh, D), dtype=torch.bfloat16, device=dev)
+        for layer in range(layers):
+            for kv_idx in (0, 1):
+                t0 = (layer * 2 + kv_idx) * tokens
+                synth.make_kv_torch(tokens, kvh, D, seed=seed, layer=layer, kv_idx=kv_idx, out=kv[t0:t0 + tokens])
+        n_pages = n_t * tokens // pt
+        ppt = tokens // pt                       # pages per layer tensor
+        elems = n_t * tokens * kvh * D
+        out = torch.empty((tokens if per_tensor else n_t * tokens, kvh, D), dtype=torch.bfloat16, device=dev)
+        for c_, al in settings:
+            a_sz, r_sz = lynx.stream_sizes(pt, kvh, D, c_)
+            anc = torch.empty((n_pages, a_sz), dtype=torch.uint8, device=dev)
+            res = torch.empty((n_pages, r_sz), dtype=torch.uint8, device=dev)
+            parts = [(t * tokens, t * ppt) for t in range(n_t)] if per_tensor else [(0, 0)]
+            span_t = tokens if per_tensor else n_t * tokens
+            span_p = ppt if per_tensor else n_pages
+
+            def enc():
+                for t0, p0 in parts:
+                    lynx.encode(kv[t0:t0 + span_t], pt, c_, al, anchor_out=anc[p0:p0 + span_p],
+                                residual_out=res[p0:p0 + span_p])
+
+            def dec_a():
+                for _, p0 in parts:
+                    lynx.decode_anchor(anc[p0:p0 + span_p], span_p, pt, kvh, D, c_, al, out=out)
+
+            def dec_f():
+                for _, p0 in parts:
+                    lynx.decode_full(anc[p0:p0 + span_p], res[p0:p0 + span_p], span_p, pt, kvh, D, c_, al, out=out)
+
+            meta = 8.0 / c_ + 8.0 / pt
+            per = {}
+            for op, fn, bpe in (("encode", enc, 3.0 + meta), ("decode_anchor", dec_a, 2.5 + meta),
+                                ("decode_full", dec_f, 3.0 + meta)):
+                for _ in range(warmup):
+                    fn()
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(reps)]
+                for e0, e1 in evs:
+                    e0.record(stream)
+                    fn()
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                t_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)[reps // 2]
+                per[op] = {"ms": round(t_ms, 4), "alg_GBs": round(bpe * elems / t_ms / 1e6, 1),
+                           "frac_hbm_peak": round(bpe * elems / t_ms / 1e6 / HBM_PEAK_GBS, 4),
+                           "bf16_equiv_GBs": round(2.0 * elems / t_ms / 1e6, 1)}
+            rows.append({"workload": name, "page_tokens": pt, "chunk": c_, "alpha": al, "elements": elems,
+                         "calls_per_op": len(parts), "ops": per})
+            print(f"[bench]   C={c_} alpha={al:g}: " + ", ".join(
+                f"{op} {v['ms']:.4f} ms {v['frac_hbm_peak'] * 100:.1f}%" for op, v in per.items()),
+                file=sys.stderr, flush=True)
+            del anc, res
+        del kv, out
+        torch.cuda.empty_cache()
+    return {"codec_workloads": rows, "hbm_peak_GBs": HBM_PEAK_GBS, "reps": reps, "warmup": warmup,
+            "timing": "median of the event-timed repetitions; BF16 decode output; inputs resident in HBM"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +330,8 @@ def main():
                     help="summarise two rocprofv3 --pmc runs of this benchmark into per-op HBM bytes")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="summarise a rocprofv3 --kernel-trace run of this benchmark per kernel and grid")
+    ap.add_argument("--codec-workloads", action="store_true",
+                    help="instead of the step: time the codec on the other request shapes (one JSON line)")
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
@@ -256,6 +343,9 @@ def main():
         print("bench.py measures one GPU only: the Lynx hot path here is single-GPU (the codec and the "
               "attention shard by page / sequence with no exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.codec_workloads:
+        print(json.dumps(codec_workloads(reps=max(args.steps, 5), warmup=max(args.warmup, 1))), flush=True)
+        return
 
     import torch
     from decode_attention_lynx_amd import lynx, synth

@@ -87,3 +87,15 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_codec_workloads_are_valid_shapes():
+    """Every shape the codec-workloads report times is one the library accepts: whole pages,
+    chunks that divide the page, and a segment size the oracle agrees with."""
+    from decode_attention_lynx_amd import lynx
+    from oracle import lynx_oracle as o
+    for name, layers, tokens, kvh, pt, seed, settings, per_tensor in bench.CODEC_WORKLOADS:
+        assert tokens % pt == 0 and layers > 0 and kvh > 0, name
+        for c_, al in settings:
+            assert pt % c_ == 0 and c_ in (8, 16, 32, 64, 128, 256) and al > 0, (name, c_)
+            assert lynx.stream_sizes(pt, kvh, 128, c_) == o.segment_bytes(pt, kvh, 128, c_)
