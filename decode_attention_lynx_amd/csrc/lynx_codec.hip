@@ -426,42 +426,43 @@ template __global__ void k_encode<256>(EncodeArgs);
 // ---------------------------------------------------------------------------
 template <bool FULL, bool F32OUT>
 __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
-  // A unit is one 128-token tile of one kv head of one page; thread t owns channels
-  // 8*(t % 16) .. +7 and tokens 8*(t / 16) .. +7 of the tile, so the 64-byte code row
-  // of a (head, token) is read whole by 16 neighbouring threads.  Each workgroup walks
-  // a contiguous range of units (contiguous per XCD), so the lookup table it builds is
-  // reused across many tiles.
+  // One workgroup per unit: one 128-token tile of one kv head of one page (units
+  // numbered contiguously per XCD).  Thread t owns channels 8*(t % 16) .. +7 and tokens
+  // 8*(t / 16) .. +7 of the tile, so the 64-byte code row of a (head, token) is read
+  // whole by 16 neighbouring threads.  A workgroup that walked a range of tiles would
+  // wait, before each tile's loads return, for its previous tile's stores too (loads
+  // and stores share one in-order counter); short workgroups keep the stores of
+  // finished tiles out of the critical path.
   const Geometry& g = a.g;
   const int ntiles = (g.P + kDecTile - 1) / kDecTile;
-  const int n_units = g.n_pages * g.Hkv * ntiles;
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int upw = (n_units + gridDim.x - 1) / gridDim.x;
-  const int u_begin = wg * upw, u_end = min(n_units, u_begin + upw);
+  const int unit = xcd_remap(blockIdx.x, gridDim.x);
   const int tid = threadIdx.x, dg = tid & (kDecDG - 1), tg = tid / kDecDG;
   const int H = g.H;
 
   // Lookup tables in LDS.  Full decode indexes 256 entries at random, so each entry is
-  // kept in 32 copies, one per bank: lane l reads copy l % 32 and no two lanes of a
-  // half-wave meet in a bank.  The anchor table has 16 entries, which sit in 16 banks
-  // and are read conflict-free as they are.
+  // kept in 32 adjacent copies, one per bank: lane l reads copy l % 32 and no two lanes
+  // of a half-wave meet in a bank.  The anchor table has 16 entries, which sit in 16
+  // banks and are read conflict-free as they are.
   __shared__ float s_lut[FULL ? 256 * 32 : 16];
   if (FULL) {
-#pragma unroll 8
-    for (int k = 0; k < 32; ++k) s_lut[k * 256 + tid] = a.lut[8 * k + (tid >> 5)];   // entry 8k + tid/32, copy tid%32
+    const float e = a.lut[tid];                                       // entry tid, all 32 copies
+    float4* dst = reinterpret_cast<float4*>(s_lut + tid * 32);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dst[k] = make_float4(e, e, e, e);
   } else if (tid < 16) {
     s_lut[tid] = a.lut[tid];
   }
   __syncthreads();
   const float* lut_l = FULL ? s_lut + (tid & 31) : s_lut;   // this lane's copy
 
-  for (int unit = u_begin; unit < u_end; ++unit) {
+  {
     const int tile = unit % ntiles;
     const int ph = unit / ntiles;
     const int page = ph / g.Hkv;
     const int h = ph - page * g.Hkv;
     const int cbase = h * kHeadDim;
     const int tok0 = tile * kDecTile + tg * kTokPerThread;
-    if (tok0 >= g.P) continue;
+    if (tok0 >= g.P) return;
     const uint8_t* anc = a.anchor + (size_t)page * g.anc_seg;
     const float* meta = reinterpret_cast<const float*>(anc + g.codes);
     const size_t code_off = (size_t)h * g.P * (kHeadDim / 2) + dg * 4;
