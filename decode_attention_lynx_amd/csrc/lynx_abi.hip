@@ -34,7 +34,7 @@ int check_geometry(int n_pages, int P, int Hkv, int D, int C, float alpha, Geome
   if (!pow2_chunk(C)) return LYNX_EUNSUPPORTED;
   if ((long long)P * Hkv * kHeadDim / 2 > 0x7fffffffll) return LYNX_EUNSUPPORTED;   // page byte counts in int
   if ((long long)n_pages * Hkv * ((P + kDecTile - 1) / kDecTile) > 0x7fffffffll ||
-      (long long)n_pages * Hkv * (kHeadDim / kSlab) > 0x7fffffffll)
+      (long long)n_pages * Hkv * (kHeadDim / kSlab) * ((P + kTileTokens - 1) / kTileTokens) > 0x7fffffffll)
     return LYNX_EUNSUPPORTED;
   g->n_pages = n_pages;
   g->P = P;
@@ -58,6 +58,14 @@ void anchor_fields(int nib, int* S, int* vmag) {
   const int q = nib >= 8 ? nib - 16 : nib;
   *S = q < 0 ? -1 : 1;
   *vmag = q < 0 ? -q - 1 : q;
+}
+
+// The encoder for chunk C: pages of one tile take Stage 1 in the same kernel, longer
+// pages read the gamma stored by the two Stage 1 kernels.
+template <int C>
+const void* encode_kernel(bool page_stored) {
+  return page_stored ? reinterpret_cast<const void*>(&k_encode<C, true>)
+                     : reinterpret_cast<const void*>(&k_encode<C, false>);
 }
 
 int launch(const void* fn, dim3 grid, void* args_struct, hipStream_t stream) {
@@ -118,18 +126,30 @@ int lynx_encode(const void* kv_dev, int n_pages, int page_tokens, int kv_heads, 
   a.bnd[0] = 0.0;
   for (int j = 1; j <= kCodeMax; ++j) a.bnd[j] = std::expm1(((double)j - 0.5) * L / kCodeMax) / al;
   a.bnd[128] = INFINITY;
-  const long long n_units = (long long)n_pages * kv_heads * (kHeadDim / kSlab);   // (page, head, slab)
+  // one workgroup per (page, head, 64-channel slab, 256-token tile)
+  const long long ntiles = (page_tokens + kTileTokens - 1) / kTileTokens;
+  const long long n_wg = (long long)n_pages * kv_heads * (kHeadDim / kSlab) * ntiles;
+  const bool stored = ntiles > 1;
   const void* fn = nullptr;
   switch (chunk) {
-    case 8: fn = reinterpret_cast<const void*>(&k_encode<8>); break;
-    case 16: fn = reinterpret_cast<const void*>(&k_encode<16>); break;
-    case 32: fn = reinterpret_cast<const void*>(&k_encode<32>); break;
-    case 64: fn = reinterpret_cast<const void*>(&k_encode<64>); break;
-    case 128: fn = reinterpret_cast<const void*>(&k_encode<128>); break;
-    default: fn = reinterpret_cast<const void*>(&k_encode<256>); break;
+    case 8: fn = encode_kernel<8>(stored); break;
+    case 16: fn = encode_kernel<16>(stored); break;
+    case 32: fn = encode_kernel<32>(stored); break;
+    case 64: fn = encode_kernel<64>(stored); break;
+    case 128: fn = encode_kernel<128>(stored); break;
+    default: fn = encode_kernel<256>(stored); break;
   }
-  const dim3 grid((unsigned)n_units);
-  return launch(fn, grid, &a, static_cast<hipStream_t>(hip_stream));
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  if (ntiles > 1) {
+    // Stage 1 of a page longer than one tile: per-tile extremes, then gamma per (page, channel)
+    st = launch(reinterpret_cast<const void*>(&k_page_extremes), dim3((unsigned)n_wg), &a, stream);
+    if (st != LYNX_OK) return st;
+    const long long n_ch = (long long)n_pages * a.g.H;
+    st = launch(reinterpret_cast<const void*>(&k_page_finish), dim3((unsigned)((n_ch + kThreads - 1) / kThreads)), &a,
+                stream);
+    if (st != LYNX_OK) return st;
+  }
+  return launch(fn, dim3((unsigned)n_wg), &a, stream);
 }
 
 size_t lynx_encode_to_host_staging_bytes(int group_pages, int page_tokens, int kv_heads, int head_dim, int chunk) {

@@ -194,16 +194,17 @@ __device__ __forceinline__ void page_stats(EncodeShared<C>& sh, int tid) {
 }
 
 // Stage 1, second half, and Stage 2 ([Review] Mechanism 1, Stages 1-2) of the chunks in
-// the tile at t0.  Each (chunk, channel) thread combines the four partial page extremes
-// of its channel: gamma_min and gamma_scale are stored as float32 (by the chunk-0
-// threads of the first tile), D1 = gamma_scale + eps is used in float64.  Then
-// mu = mean(X_n), sigma = max |X_n - mu|, both stored as float32 and used in their stored
-// form from here on.  The mean comes from the float64 sum of the chunk's BF16 values;
-// sigma from the chunk's extreme values (X_n is monotone in X).  One (chunk, channel)
-// pair per thread and step.
+// the tile at t0.  On a one-tile page each (chunk, channel) thread combines the four
+// partial page extremes of its channel, and the chunk-0 threads store gamma_min and
+// gamma_scale as float32; on a longer page both were stored by k_page_finish and are
+// read back.  D1 = gamma_scale + eps is used in float64.  Then mu = mean(X_n),
+// sigma = max |X_n - mu|, both stored as float32 and used in their stored form from
+// here on.  The mean comes from the float64 sum of the chunk's BF16 values; sigma from
+// the chunk's extreme values (X_n is monotone in X).  One (chunk, channel) pair per
+// thread and step.
 template <int C>
 __device__ __forceinline__ void chunk_stats(EncodeShared<C>& sh, float* meta, int cbase, int t0, int tid,
-                                            const Geometry& g) {
+                                            const Geometry& g, bool page_stored) {
   constexpr int G = C / kTokPerThread;               // token groups (threads) per chunk
   constexpr int NCT = kTileTokens / C;               // chunks per tile
   float* meta_mu = meta + 2 * g.H + cbase;
@@ -220,22 +221,30 @@ __device__ __forceinline__ void chunk_stats(EncodeShared<C>& sh, float* meta, in
       lo = fminf(lo, sh.pmin[row][pc]);
       hi = fmaxf(hi, sh.pmax[row][pc]);
     }
-    float plo = INFINITY, phi = -INFINITY;
+    float gmin32, gscale;
+    if (page_stored) {
+      gmin32 = meta[cbase + c];
+      gscale = meta[g.H + cbase + c];
+    } else {
+      float plo = INFINITY, phi = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < kThreads / kSlab; ++q) {
-      const uint32_t w = sh.gpart[q][col];
-      plo = fminf(plo, __uint_as_float(w << 16));
-      phi = fmaxf(phi, __uint_as_float(w & 0xffff0000u));
+      for (int q = 0; q < kThreads / kSlab; ++q) {
+        const uint32_t w = sh.gpart[q][col];
+        plo = fminf(plo, __uint_as_float(w << 16));
+        phi = fmaxf(phi, __uint_as_float(w & 0xffff0000u));
+      }
+      // + 0: a zero minimum / range is stored as +0 whatever the signs of the zeros
+      gmin32 = plo + 0.0f;
+      gscale = (float)(((double)phi - (double)gmin32) + 0.0);   // exact difference, one rounding
     }
-    // + 0: a zero minimum / range is stored as +0 whatever the signs of the zeros
-    const float gmin32 = plo + 0.0f;
-    const float gscale = (float)(((double)phi - (double)gmin32) + 0.0);   // exact difference, one rounding
     const double gmin = (double)gmin32, D1 = (double)gscale + kEps, r1 = 1.0 / D1;
-    if (ck == 0 && t0 == 0) {
+    if (ck == 0) {
       sh.gmin[col] = gmin32;
       sh.D1[col] = D1;
-      meta[cbase + c] = gmin32;
-      meta[g.H + cbase + c] = gscale;
+      if (!page_stored) {
+        meta[cbase + c] = gmin32;
+        meta[g.H + cbase + c] = gscale;
+      }
     }
     const double mean = (s - (double)C * gmin) * r1 * (1.0 / C);     // 1/C exact (C a power of two)
     const float mu32 = (float)mean;
@@ -345,77 +354,121 @@ __device__ __forceinline__ void encode_tokens(const EncodeShared<C>& sh, const E
   }
 }
 
-// General encoder: one workgroup per unit, pages of any length.  Pages longer than
-// one 256-token tile take Stage 1 in a first pass over the page and Stages 2-4 tile
-// by tile in a second.
-template <int C>
+// Stage 1 of pages longer than one 256-token tile, first part: the extremes of every
+// channel of the slab over one tile, one workgroup per (unit, tile).  The partial
+// minimum of tile t is parked in row t of the page's mu array and the partial maximum
+// in row t of its sigma array (P/C >= P/256 rows each); k_page_finish reduces them,
+// and k_encode then overwrites those rows with the chunk statistics.
+__global__ __launch_bounds__(kThreads) void k_page_extremes(EncodeArgs a) {
+  __shared__ float s_mn[kTG][kSlab];
+  __shared__ float s_mx[kTG][kSlab];
+  const Geometry& g = a.g;
+  const int ntiles = (g.P + kTileTokens - 1) / kTileTokens;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int t = w % ntiles;
+  const int tid = threadIdx.x, dg = tid & (kDG - 1), tg = tid / kDG;
+  const EncodeUnit u = encode_unit(a, w / ntiles, dg);
+  const int t0 = t * kTileTokens;
+  uint4 v[kTokPerThread];
+  load_tile(v, u.X, t0, tg, g);
+  float mn[8], mx[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { mn[j] = INFINITY; mx[j] = -INFINITY; }
+  if (t0 + tg * kTokPerThread < g.P) {
+#pragma unroll
+    for (int i = 0; i < kTokPerThread; ++i) {
+      const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lo = bf16_lo(q[k]), hi = bf16_hi(q[k]);
+        mn[2 * k] = fminf(mn[2 * k], lo);
+        mx[2 * k] = fmaxf(mx[2 * k], lo);
+        mn[2 * k + 1] = fminf(mn[2 * k + 1], hi);
+        mx[2 * k + 1] = fmaxf(mx[2 * k + 1], hi);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    s_mn[tg][lds_swz(tg, j * 8 + dg)] = mn[j];
+    s_mx[tg][lds_swz(tg, j * 8 + dg)] = mx[j];
+  }
+  __syncthreads();
+  if (tid < kSlab) {
+    const int col = tid, c = lds_chan(col);
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll 8
+    for (int r = 0; r < kTG; ++r) {
+      lo = fminf(lo, s_mn[r][lds_swz(r, col)]);
+      hi = fmaxf(hi, s_mx[r][lds_swz(r, col)]);
+    }
+    u.meta[2 * g.H + (size_t)t * g.H + u.cbase + c] = lo;
+    u.meta[2 * g.H + (size_t)(g.nck + t) * g.H + u.cbase + c] = hi;
+  }
+}
+
+// Stage 1 of pages longer than one tile, second part ([Review] Mechanism 1, Stage 1):
+// gamma_min = min over the tiles' partial minima, gamma_scale = float32(max - min) with
+// the difference exact in float64, one thread per (page, channel).
+__global__ __launch_bounds__(kThreads) void k_page_finish(EncodeArgs a) {
+  const Geometry& g = a.g;
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (long long)g.n_pages * g.H) return;
+  const int page = (int)(i / g.H), c = (int)(i - (long long)page * g.H);
+  float* meta = reinterpret_cast<float*>(a.anchor + (size_t)page * g.anc_seg + g.codes);
+  const int ntiles = (g.P + kTileTokens - 1) / kTileTokens;
+  float lo = INFINITY, hi = -INFINITY;
+  for (int t = 0; t < ntiles; ++t) {
+    lo = fminf(lo, meta[2 * g.H + (size_t)t * g.H + c]);
+    hi = fmaxf(hi, meta[2 * g.H + (size_t)(g.nck + t) * g.H + c]);
+  }
+  // + 0: a zero minimum / range is stored as +0 whatever the signs of the zeros
+  const float gmin32 = lo + 0.0f;
+  meta[c] = gmin32;
+  meta[g.H + c] = (float)(((double)hi - (double)gmin32) + 0.0);
+}
+
+// Stages 1-4 of one 256-token tile of one unit per workgroup.  A one-tile page
+// (PAGE_STORED false) takes Stage 1 from the same partials Stage 2 uses; a longer page
+// (PAGE_STORED true) reads the gamma that k_page_extremes and k_page_finish stored.
+template <int C, bool PAGE_STORED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C >= 64 ? 4 : 2))) void k_encode(EncodeArgs a) {
   __shared__ EncodeShared<C> sh;
   const Geometry& g = a.g;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int ntiles = PAGE_STORED ? (g.P + kTileTokens - 1) / kTileTokens : 1;
+  const int t = PAGE_STORED ? w % ntiles : 0;
   const int tid = threadIdx.x, dg = tid & (kDG - 1), tg = tid / kDG;
-  const EncodeUnit u = encode_unit(a, xcd_remap(blockIdx.x, gridDim.x), dg);
-  const int ntiles = (g.P + kTileTokens - 1) / kTileTokens;
+  const EncodeUnit u = encode_unit(a, PAGE_STORED ? w / ntiles : w, dg);
+  const int t0 = t * kTileTokens;
 
   for (int i = tid; i < 129; i += kThreads) sh.bnd[i] = a.bnd[i];
 
   uint4 v[kTokPerThread];
-  // ---- Stage 1: per-channel page min / max over all tokens.  A page of one tile takes
-  // them from the same partials Stage 2 uses; longer pages make a pass.
-  if (ntiles == 1) {
-    load_tile(v, u.X, 0, tg, g);
-    store_partials(sh, v, tg * kTokPerThread < g.P, tg, dg);
-  } else {
-    float mn[8], mx[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) { mn[j] = INFINITY; mx[j] = -INFINITY; }
-    for (int t = 0; t < ntiles; ++t) {
-      load_tile(v, u.X, t * kTileTokens, tg, g);
-      if (t * kTileTokens + tg * kTokPerThread < g.P) {
-#pragma unroll
-        for (int i = 0; i < kTokPerThread; ++i) {
-          const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float lo = bf16_lo(q[k]), hi = bf16_hi(q[k]);
-            mn[2 * k] = fminf(mn[2 * k], lo);
-            mx[2 * k] = fmaxf(mx[2 * k], lo);
-            mn[2 * k + 1] = fminf(mn[2 * k + 1], hi);
-            mx[2 * k + 1] = fmaxf(mx[2 * k + 1], hi);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      sh.pmin[tg][lds_swz(tg, j * 8 + dg)] = mn[j];
-      sh.pmax[tg][lds_swz(tg, j * 8 + dg)] = mx[j];
-    }
-  }
+  load_tile(v, u.X, t0, tg, g);
+  store_partials(sh, v, t0 + tg * kTokPerThread < g.P, tg, dg);
   __syncthreads();
-  page_stats(sh, tid);
-  __syncthreads();
-
-  // ---- per tile: Stage 2 chunk statistics, then Stages 3-4 per element
-  for (int t = 0; t < ntiles; ++t) {
-    const int t0 = t * kTileTokens;
-    if (ntiles > 1) {
-      load_tile(v, u.X, t0, tg, g);
-      store_partials(sh, v, t0 + tg * kTokPerThread < g.P, tg, dg);
-      __syncthreads();
-    }
-    chunk_stats(sh, u.meta, u.cbase, t0, tid, g);
+  if (!PAGE_STORED) {
+    page_stats(sh, tid);
     __syncthreads();
-    encode_tokens(sh, a, u, v, t0, tg, dg);
-    if (ntiles > 1) __syncthreads();   // the LDS partials and chunk tables are reused by the next tile
   }
+  chunk_stats(sh, u.meta, u.cbase, t0, tid, g, PAGE_STORED);
+  __syncthreads();
+  encode_tokens(sh, a, u, v, t0, tg, dg);
 }
 
-template __global__ void k_encode<8>(EncodeArgs);
-template __global__ void k_encode<16>(EncodeArgs);
-template __global__ void k_encode<32>(EncodeArgs);
-template __global__ void k_encode<64>(EncodeArgs);
-template __global__ void k_encode<128>(EncodeArgs);
-template __global__ void k_encode<256>(EncodeArgs);
+template __global__ void k_encode<8, false>(EncodeArgs);
+template __global__ void k_encode<8, true>(EncodeArgs);
+template __global__ void k_encode<16, false>(EncodeArgs);
+template __global__ void k_encode<16, true>(EncodeArgs);
+template __global__ void k_encode<32, false>(EncodeArgs);
+template __global__ void k_encode<32, true>(EncodeArgs);
+template __global__ void k_encode<64, false>(EncodeArgs);
+template __global__ void k_encode<64, true>(EncodeArgs);
+template __global__ void k_encode<128, false>(EncodeArgs);
+template __global__ void k_encode<128, true>(EncodeArgs);
+template __global__ void k_encode<256, false>(EncodeArgs);
+template __global__ void k_encode<256, true>(EncodeArgs);
 
 // ---------------------------------------------------------------------------
 // Decode ([Review] Mechanism 2: Q_approx = dequant(Q_anc, gamma, mu, sigma) and

@@ -8,8 +8,10 @@
 
 namespace lynx {
 
-template <int C>
+template <int C, bool PAGE_STORED>
 __global__ void k_encode(EncodeArgs a);
+__global__ void k_page_extremes(EncodeArgs a);
+__global__ void k_page_finish(EncodeArgs a);
 template <bool FULL, bool F32OUT>
 __global__ void k_decode(DecodeArgs a);
 
