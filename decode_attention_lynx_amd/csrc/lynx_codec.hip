@@ -7,11 +7,12 @@
 //            (decode-side anchor / residual phases), Worked Example (Eq. 14-15),
 //            Implementation Notes (two 4-bit codes per byte, 256-token pages).
 //
-// Work decomposition.  A workgroup of 256 threads owns a 64-channel slab of one
-// kv head of one page (encode) or of one 256-token tile of a page (decode).
-// Thread t owns channels 8*(t % 8) .. +7 of the slab and the 8 consecutive
-// tokens 8*(t / 8) .. +7 of the tile.  A token row of the slab is 128 B of BF16
-// (8 threads x 16 B loads) and 32 B of nibbles per stream (8 threads x 4 B).
+// Work decomposition.  An encode workgroup of 256 threads owns one 256-token tile
+// of a 64-channel slab of one kv head of one page: thread t owns channels
+// 8*(t % 8) .. +7 of the slab and the 8 consecutive tokens 8*(t / 8) .. +7 of the
+// tile.  A token row of the slab is 128 B of BF16 (8 threads x 16 B loads) and 32 B
+// of nibbles per stream (8 threads x 4 B).  A decode workgroup owns one 128-token
+// tile of one kv head (see k_decode).
 // Chunk sizes are powers of two in [8, 256], so a thread's tokens always lie in
 // one chunk, a chunk is a power-of-two run of threads, and chunks never straddle
 // 256-token tiles.

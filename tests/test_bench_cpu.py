@@ -1,6 +1,7 @@
 """Host logic of bench.py: the rocprofv3 counter and trace summaries (CPU only)."""
 import csv
 import json
+import os
 
 import bench
 
@@ -26,8 +27,8 @@ def test_counter_summary_calibrates_against_the_copy(tmp_path):
     enc_grid = bench.OP_KERNELS["encode"][0][1]
     gib_kib = (1 << 30) / 1024
     fetch = {("hbm_probe::k_probe_copy(unsigned int const*)", 2097152): [gib_kib / 2] * 3,
-             (f"void lynx::k_encode<{bench.C}>(lynx::EncodeArgs)", enc_grid): [1000.0, 1002.0],
-             (f"void lynx::k_encode<{bench.C}>(lynx::EncodeArgs)", enc_grid // 2): [7.0],   # setup encode, ignored
+             (f"void lynx::k_encode<{bench.C}, false>(lynx::EncodeArgs)", enc_grid): [1000.0, 1002.0],
+             (f"void lynx::k_encode<{bench.C}, false>(lynx::EncodeArgs)", enc_grid // 2): [7.0],   # setup encode, ignored
              ("void lynx::k_decode<false, false>(lynx::DecodeArgs)", 524288): [10.0],
              ("void lynx::k_decode<true, false>(lynx::DecodeArgs)", 524288): [20.0],
              ("void lynx::k_attn_anchor<64>(lynx::AttnArgs)", 4096): [30.0],
@@ -99,3 +100,19 @@ def test_codec_workloads_are_valid_shapes():
         for c_, al in settings:
             assert pt % c_ == 0 and c_ in (8, 16, 32, 64, 128, 256) and al > 0, (name, c_)
             assert lynx.stream_sizes(pt, kvh, 128, c_) == o.segment_bytes(pt, kvh, 128, c_)
+
+
+def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    """The counters' source hash survives a comment-only edit and changes with the code."""
+    import shutil
+    for s in bench.KERNEL_SOURCES:
+        (tmp_path / s).parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(bench.ROOT, s), tmp_path / s)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_hash()
+    src = tmp_path / bench.KERNEL_SOURCES[0]
+    text = src.read_text()
+    src.write_text("// a comment line\n\n" + text.replace("\n", "   // trailing note\n", 1))
+    assert bench.kernel_hash() == h0
+    src.write_text(text.replace("kTileTokens", "kTileTokens + 0", 1))
+    assert bench.kernel_hash() != h0

@@ -87,10 +87,12 @@ def test_codec_shapes(gpu, P, C, alpha, Hkv, n_pages):
     run_codec(bits, P, C, alpha, label=f"shape P{P} C{C}")
 
 
-def test_degenerate_pages(gpu):
+@pytest.mark.parametrize("P", [256, 512])
+def test_degenerate_pages(gpu, P):
     """Constant channels (at zero, negative, with -0.0), a constant chunk inside a live
-    channel, huge and tiny magnitudes, and an all-constant page."""
-    P, C, Hkv, D = 256, 32, 1, 128
+    channel, huge and tiny magnitudes, and an all-constant page; P = 512 takes the
+    two-tile path, whose page extremes are reduced across workgroups."""
+    C, Hkv, D = 32, 1, 128
     rng = np.random.default_rng(7)
     X = rng.laplace(0, 0.5, size=(2 * P, Hkv, D)).astype(np.float32)
     X[:, 0, 0] = 0.0
@@ -104,7 +106,7 @@ def test_degenerate_pages(gpu):
     X[P:, 0, 7:] = 2.0                             # second page: constant except channels 0..6
     X[:, 0, 8] = rng.choice([-1.0, 1.0], size=2 * P) * 2.0 ** rng.integers(-20, 20, size=2 * P)
     bits = o.f64_to_bf16_bits(X.astype(np.float64))
-    run_codec(bits, P, C, 255.0, label="degenerate", bf16_share=None)
+    run_codec(bits, P, C, 255.0, label=f"degenerate P{P}", bf16_share=None)
 
 
 def test_zero_pages_is_a_noop(gpu):
