@@ -268,17 +268,20 @@ __device__ __forceinline__ void chunk_stats(EncodeShared<C>& sh, float* meta, in
   }
 }
 
-// Eq. 7 in float32 for X_f = f, returned as the bits of 128 + Y + 1/2 (Y < 127.5, so
-// the float lies in [128, 256) with an ulp of 2^-16): byte 2 is floor(Y + 1/2) =
-// Round(Y) and the low 16 bits are the fraction of Y + 1/2 in units of 2^-16.
-__device__ __forceinline__ uint32_t y_bits(float f, float alpha, float ylog2k) {
+// Eq. 7 in float32 for X_f = f, returned as the bits of 128 + Y + 1/2 + z*2^-16, z the
+// half-width of the band in units of 2^-16 (ybias = 128.5 + z*2^-16, exact in float32;
+// Y < 127.5, so the float lies in [128, 256) with an ulp of 2^-16).  Byte 2 is
+// floor(Y + 1/2 + z*2^-16), which is Round(Y) except in the band, and the low 16 bits
+// are the fraction of Y + 1/2 moved up by z.
+__device__ __forceinline__ uint32_t y_bits(float f, float alpha, float ylog2k, float ybias) {
   const float tt = fmaf(alpha, fabsf(f), 1.0f);
-  return __float_as_uint(fmaf(__builtin_amdgcn_logf(tt), ylog2k, 128.5f));
+  return __float_as_uint(fmaf(__builtin_amdgcn_logf(tt), ylog2k, ybias));
 }
 
-// Y within `zband` units of 2^-16 of a rounding boundary (fraction of Y + 1/2 near 0 or 1).
+// Y within z units of 2^-16 of a rounding boundary: the fraction of Y + 1/2 lies in
+// [0, z) or (1 - z, 1), so the moved fraction lies in [0, 2z) (one 16-bit compare).
 __device__ __forceinline__ bool in_band(uint32_t yb, uint32_t zband) {
-  return ((yb + zband) << 16) < (2u * zband << 16);
+  return static_cast<uint16_t>(yb) < static_cast<uint16_t>(2u * zband);
 }
 
 // Stages 3-4 ([Review] Mechanism 1, Stages 3-4, Eq. 7 and Eq. 9) for this thread's 8
@@ -295,6 +298,7 @@ __device__ __forceinline__ void encode_tokens(const EncodeShared<C>& sh, const E
   const int kc = tg / G;                             // chunk within tile
   const float alpha = a.alpha, ylog2k = a.ylog2k;
   const uint32_t zband = a.zband;
+  const float ybias = 128.5f + (float)zband * (1.0f / 65536.0f);
   // this thread's columns j*8 + dg of the chunk tables: one base each, j an offset
   const float4* cst_t = &sh.cst[kc][dg];
   const float* sig_t = &sh.sig[kc][dg];
@@ -320,7 +324,7 @@ __device__ __forceinline__ void encode_tokens(const EncodeShared<C>& sh, const E
     for (int j = 0; j < 8; ++j) {
       const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
       const float f = fmaf(x - ch[j], kk[j], ckn[j]);
-      mb[j] = y_bits(f, alpha, ylog2k);
+      mb[j] = y_bits(f, alpha, ylog2k, ybias);
       near[j] = in_band(mb[j], zband);
       xf[j] = f;
     }
@@ -340,9 +344,9 @@ __device__ __forceinline__ void encode_tokens(const EncodeShared<C>& sh, const E
         const float x = (j & 1) ? bf16_hi_p(w) : bf16_lo_p(w);
         const float4 cs = cst_t[j * 8];
         // the fast path's Y again (same operations), to find the boundary it lies near:
-        // a fraction of Y + 1/2 near 0 is the boundary below code I, near 1 the one above
-        const uint32_t yb = y_bits(fmaf(x - cs.x, cs.y, cs.z), alpha, ylog2k);
-        const int jb = (int)((yb >> 16) & 0xFFu) + ((yb & 0xFFFFu) >= 0x8000u ? 1 : 0);   // in [1, 128]
+        // the moved fraction is below 2z, so byte 2 is the code just above that boundary
+        const uint32_t yb = y_bits(fmaf(x - cs.x, cs.y, cs.z), alpha, ylog2k, ybias);
+        const int jb = (int)((yb >> 16) & 0xFFu);     // in [1, 128]: Y + 1/2 lies just around jb
         const float2 e = encode_exact(x, gmin_t[j * 8], D1_t[j * 8], cs.w, (double)sig_t[j * 8] + kEps, jb, sh.bnd);
         const uint32_t byte = (uint32_t)e.x ^ (e.y < 0.0f ? 0xF7u : 0x07u);   // anchor nibble high, residual low
         const uint32_t m = 0xFu << (4 * j);
