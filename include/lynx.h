@@ -102,6 +102,9 @@ int lynx_stream_sizes(int page_tokens, int kv_heads, int head_dim, int chunk,
  * Per element: X_n = (X - gamma_min)/(gamma_scale + eps);
  * X_f = (X_n - mu)/(sigma + eps); Y = 127*ln(1 + alpha|X_f|)/ln(1 + alpha);
  * I = Round(Y); S = sign(X_f); then the split above.
+ * Pages longer than 256 tokens are encoded by three launches on the stream (the
+ * page extremes per 256-token tile, gamma, then the tiles); until they have run,
+ * the anchor segments' mu / sigma rows hold intermediate values.
  * Supported by this library: head_dim == 128 (else LYNX_EUNSUPPORTED).
  */
 int lynx_encode(const void* kv_dev, int n_pages, int page_tokens, int kv_heads, int head_dim,
