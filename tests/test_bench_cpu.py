@@ -116,3 +116,12 @@ def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.kernel_hash() == h0
     src.write_text(text.replace("kTileTokens", "kTileTokens + 0", 1))
     assert bench.kernel_hash() != h0
+
+
+def test_cpu_baseline_reports_its_workers():
+    """The oracle baseline runs one single-threaded worker per host core (at most 16) and
+    states the core count and the sample it timed."""
+    rec = bench.cpu_baseline(cpu_seconds=0.1)
+    n = max(1, min(16, len(os.sched_getaffinity(0))))
+    assert rec["cores"] == n and rec["kind"] == "oracle" and rec["unit"] == "GB/s"
+    assert rec["value"] > 0 and f"{n} single-threaded worker processes" in rec["sample"]
