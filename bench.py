@@ -274,6 +274,7 @@ def codec_workloads(reps: int, warmup: int) -> dict:
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()           # default priority, like every stream here
     rows = []
     for name, layers, tokens, kvh, pt, seed, settings, per_tensor in CODEC_WORKLOADS:
         print(f"[bench] codec workload: {name}", file=sys.stderr, flush=True)
@@ -287,6 +288,7 @@ def codec_workloads(reps: int, warmup: int) -> dict:
         ppt = tokens // pt                       # pages per layer tensor
         elems = n_t * tokens * kvh * D
         out = torch.empty((tokens if per_tensor else n_t * tokens, kvh, D), dtype=torch.bfloat16, device=dev)
+        outs = [out, torch.empty_like(out)] if per_tensor else [out]
         for c_, al in settings:
             a_sz, r_sz = lynx.stream_sizes(pt, kvh, D, c_)
             anc = torch.empty((n_pages, a_sz), dtype=torch.uint8, device=dev)
@@ -295,47 +297,71 @@ def codec_workloads(reps: int, warmup: int) -> dict:
             span_t = tokens if per_tensor else n_t * tokens
             span_p = ppt if per_tensor else n_pages
 
-            def enc():
-                for t0, p0 in parts:
-                    lynx.encode(kv[t0:t0 + span_t], pt, c_, al, anchor_out=anc[p0:p0 + span_p],
-                                residual_out=res[p0:p0 + span_p])
+            # per-tensor calls go round-robin over `streams` (one output buffer each), the
+            # extra streams joined to the timing stream around each repetition
+            def over_streams(call, streams):
+                if len(streams) > 1:
+                    fork = torch.cuda.Event()
+                    fork.record(stream)
+                    for st in streams[1:]:
+                        st.wait_event(fork)
+                for i, (t0, p0) in enumerate(parts):
+                    k = i % len(streams)
+                    call(t0, p0, streams[k], outs[k])
+                for st in streams[1:]:
+                    join = torch.cuda.Event()
+                    join.record(st)
+                    stream.wait_event(join)
 
-            def dec_a():
-                for _, p0 in parts:
-                    lynx.decode_anchor(anc[p0:p0 + span_p], span_p, pt, kvh, D, c_, al, out=out)
+            def enc(streams):
+                over_streams(lambda t0, p0, st, o: lynx.encode(
+                    kv[t0:t0 + span_t], pt, c_, al, anchor_out=anc[p0:p0 + span_p],
+                    residual_out=res[p0:p0 + span_p], stream=st), streams)
 
-            def dec_f():
-                for _, p0 in parts:
-                    lynx.decode_full(anc[p0:p0 + span_p], res[p0:p0 + span_p], span_p, pt, kvh, D, c_, al, out=out)
+            def dec_a(streams):
+                over_streams(lambda t0, p0, st, o: lynx.decode_anchor(
+                    anc[p0:p0 + span_p], span_p, pt, kvh, D, c_, al, out=o, stream=st), streams)
+
+            def dec_f(streams):
+                over_streams(lambda t0, p0, st, o: lynx.decode_full(
+                    anc[p0:p0 + span_p], res[p0:p0 + span_p], span_p, pt, kvh, D, c_, al, out=o, stream=st),
+                    streams)
 
             meta = 8.0 / c_ + 8.0 / pt
             # a workload of a few microseconds is timed over back-to-back calls, so that the
             # binding's host time between the two events is hidden behind queued launches
             inner = 20 if elems < (1 << 26) else 1
-            per = {}
-            for op, fn, bpe in (("encode", enc, 3.0 + meta), ("decode_anchor", dec_a, 2.5 + meta),
-                                ("decode_full", dec_f, 3.0 + meta)):
-                for _ in range(warmup):
-                    fn()
-                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                       for _ in range(reps)]
-                for e0, e1 in evs:
-                    e0.record(stream)
-                    for _ in range(inner):
-                        fn()
-                    e1.record(stream)
-                torch.cuda.synchronize()
-                t_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)[reps // 2] / inner
-                per[op] = {"ms": round(t_ms, 4), "alg_GBs": round(bpe * elems / t_ms / 1e6, 1),
-                           "frac_hbm_peak": round(bpe * elems / t_ms / 1e6 / HBM_PEAK_GBS, 4),
-                           "bf16_equiv_GBs": round(2.0 * elems / t_ms / 1e6, 1)}
-            rows.append({"workload": name, "page_tokens": pt, "chunk": c_, "alpha": al, "elements": elems,
-                         "calls_per_op": len(parts), "back_to_back": inner, "ops": per})
+            layouts = [("ops", [stream])]
+            if per_tensor:
+                layouts.append(("ops_two_streams", [stream, side]))
+            row = {"workload": name, "page_tokens": pt, "chunk": c_, "alpha": al, "elements": elems,
+                   "calls_per_op": len(parts), "back_to_back": inner}
+            for key, streams in layouts:
+                per = {}
+                for op, fn, bpe in (("encode", enc, 3.0 + meta), ("decode_anchor", dec_a, 2.5 + meta),
+                                    ("decode_full", dec_f, 3.0 + meta)):
+                    for _ in range(warmup):
+                        fn(streams)
+                    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                           for _ in range(reps)]
+                    for e0, e1 in evs:
+                        e0.record(stream)
+                        for _ in range(inner):
+                            fn(streams)
+                        e1.record(stream)
+                    torch.cuda.synchronize()
+                    t_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)[reps // 2] / inner
+                    per[op] = {"ms": round(t_ms, 4), "alg_GBs": round(bpe * elems / t_ms / 1e6, 1),
+                               "frac_hbm_peak": round(bpe * elems / t_ms / 1e6 / HBM_PEAK_GBS, 4),
+                               "bf16_equiv_GBs": round(2.0 * elems / t_ms / 1e6, 1)}
+                row[key] = per
+            per = row["ops"]
+            rows.append(row)
             print(f"[bench]   C={c_} alpha={al:g}: " + ", ".join(
                 f"{op} {v['ms']:.4f} ms {v['frac_hbm_peak'] * 100:.1f}%" for op, v in per.items()),
                 file=sys.stderr, flush=True)
             del anc, res
-        del kv, out
+        del kv, out, outs
         torch.cuda.empty_cache()
     return {"codec_workloads": rows, "hbm_peak_GBs": HBM_PEAK_GBS, "reps": reps, "warmup": warmup,
             "timing": "median of the event-timed repetitions; BF16 decode output; inputs resident in HBM"}
