@@ -129,3 +129,36 @@ def test_anchor_only_encode_matches_full_encode(gpu):
     a2, r2 = lynx.encode(kv, 256, 64, 255.0, residual=False)
     torch.cuda.synchronize()
     assert r2 is None and torch.equal(a1, a2)
+
+
+def test_calls_on_two_streams_match_one_stream(gpu):
+    """The library keeps no state between calls: per-tensor encodes and decodes alternating
+    over two streams (running concurrently) give the bytes of the same calls on one stream."""
+    P, C, alpha, Hkv, D = 256, 64, 255.0, 4, 128
+    n_t, tokens = 6, 1024
+    kv = torch.cat([to_dev(synth.make_kv_np(tokens, Hkv, D, seed=9, layer=t)) for t in range(n_t)])
+    ppt = tokens // P
+    a_sz, r_sz = lynx.stream_sizes(P, Hkv, D, C)
+
+    def run(streams):
+        anc = torch.zeros((n_t * ppt, a_sz), dtype=torch.uint8, device="cuda")
+        res = torch.zeros((n_t * ppt, r_sz), dtype=torch.uint8, device="cuda")
+        outs = [torch.zeros((tokens, Hkv, D), dtype=torch.bfloat16, device="cuda") for _ in range(n_t)]
+        main = torch.cuda.current_stream()
+        for st in streams:
+            st.wait_stream(main)
+        for t in range(n_t):
+            st = streams[t % len(streams)]
+            sl = slice(t * ppt, (t + 1) * ppt)
+            lynx.encode(kv[t * tokens:(t + 1) * tokens], P, C, alpha, anchor_out=anc[sl], residual_out=res[sl],
+                        stream=st)
+            lynx.decode_full(anc[sl], res[sl], ppt, P, Hkv, D, C, alpha, out=outs[t], stream=st)
+        for st in streams:
+            main.wait_stream(st)
+        torch.cuda.synchronize()
+        return anc, res, torch.stack(outs)
+
+    one = run([torch.cuda.current_stream()])
+    two = run([torch.cuda.Stream(), torch.cuda.Stream()])
+    for x, y in zip(one, two):
+        assert torch.equal(x, y)
