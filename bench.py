@@ -126,6 +126,29 @@ def counter_summary(fetch_csv: str, write_csv: str, out_json: str) -> str:
     return "\n".join(lines)
 
 
+def util_summary(counter_csv: str) -> str:
+    """Per (kernel, grid) averages of every counter in a rocprofv3 --pmc CSV of this benchmark
+    (for instance the derived MfmaUtil and VALUBusy percentages and raw instruction counts)."""
+    import csv
+    from collections import defaultdict
+    acc = defaultdict(lambda: defaultdict(list))
+    names = []
+    with open(counter_csv) as f:
+        for r in csv.DictReader(f):
+            kern = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+            if not kern.startswith(("lynx::", "hbm_probe::")):
+                continue
+            c = r["Counter_Name"]
+            if c not in names:
+                names.append(c)
+            acc[(kern, int(r["Grid_Size"]))][c].append(float(r["Counter_Value"]))
+    lines = [f"{'kernel':40s} {'grid':>10s} " + " ".join(f"{n:>14s}" for n in names)]
+    for (kern, grid), cs in sorted(acc.items()):
+        vals = [sum(cs[n]) / len(cs[n]) if cs.get(n) else float("nan") for n in names]
+        lines.append(f"{kern:40s} {grid:10d} " + " ".join(f"{v:14.4g}" for v in vals))
+    return "\n".join(lines)
+
+
 def trace_summary(trace_csv: str) -> str:
     """Per (kernel, grid) dispatch durations from a rocprofv3 --kernel-trace CSV of this benchmark."""
     import csv
@@ -380,11 +403,16 @@ def main():
                     help="summarise two rocprofv3 --pmc runs of this benchmark into per-op HBM bytes")
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="summarise a rocprofv3 --kernel-trace run of this benchmark per kernel and grid")
+    ap.add_argument("--util-summary", metavar="COUNTER_CSV",
+                    help="summarise a rocprofv3 --pmc run of this benchmark: every counter per kernel and grid")
     ap.add_argument("--codec-workloads", action="store_true",
                     help="instead of the step: time the codec on the other request shapes (one JSON line)")
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
+        return
+    if args.util_summary:
+        print(util_summary(args.util_summary))
         return
     if args.counter_summary:
         print(counter_summary(*args.counter_summary))
