@@ -48,6 +48,7 @@ def make_case(B, Hq, Hkv, T, P, C, alpha, seed):
     (1, 64, 8, 2048, 256, 64, 255.0),    # the full head geometry, short context
     (2, 16, 2, 1024, 256, 32, 255.0),    # chunk of 32 (the pages' own setting): 32-token tiles
     (1, 8, 1, 96, 32, 32, 63.0),         # chunk 32, three pages of one chunk each
+    (1, 16, 2, 8192, 4096, 256, 255.0),  # two 4096-token pages, chunks of 256 (four tiles each)
 ])
 def test_attention_small(gpu, B, Hq, Hkv, T, P, C, alpha):
     print(f"[attn] B={B} Hq={Hq} Hkv={Hkv} T={T} P={P} C={C} alpha={alpha}", flush=True)

@@ -84,6 +84,7 @@ def check(got_o, got_lse, ref_o, ref_lse, bound, tag):
     (1, 3, 2, 2, 64, 64, 64, 15.0),         # one tile, group of 1
     (2, 4, 16, 2, 1024, 256, 32, 255.0),    # chunk of 32 (the pages' own setting): two chunks per tile
     (1, 9, 24, 4, 384, 64, 32, 63.0),       # chunk 32 in one-tile pages, group of 6, 54 rows
+    (1, 4, 16, 2, 8192, 4096, 256, 63.0),   # two 4096-token pages, chunks of 256 (four tiles each)
 ])
 def test_verify_small(gpu, B, M, Hq, Hkv, T, P, C, alpha):
     print(f"[verify] B={B} M={M} Hq={Hq} Hkv={Hkv} T={T} P={P} C={C} alpha={alpha}", flush=True)
