@@ -81,6 +81,9 @@ def test_encode_validation():
     assert enc(P=96, C=48) == lynx.LYNX_EUNSUPPORTED           # chunk not a power of two in [8, 256]
     assert enc(P=1024, C=512) == lynx.LYNX_EUNSUPPORTED
     assert enc(P=4, C=4) == lynx.LYNX_EUNSUPPORTED
+    # encoder workgroups beyond int: (page, head, slab, 256-token tile) units of long pages
+    # (8388608 pages x 80 heads x 2 slabs x 2 tiles; the decoders' 3 tiles of 128 still fit)
+    assert enc(n_pages=1 << 23, P=264, Hkv=80, C=8) == lynx.LYNX_EUNSUPPORTED
     assert enc(kv=None) == lynx.LYNX_EALIGN
     assert enc(anc=ODD) == lynx.LYNX_EALIGN
     assert enc(res=None) == lynx.LYNX_EALIGN                   # residual selected but missing
