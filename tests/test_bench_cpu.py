@@ -125,3 +125,19 @@ def test_cpu_baseline_reports_its_workers():
     n = max(1, min(16, len(os.sched_getaffinity(0))))
     assert rec["cores"] == n and rec["kind"] == "oracle" and rec["unit"] == "GB/s"
     assert rec["value"] > 0 and f"{n} single-threaded worker processes" in rec["sample"]
+
+
+def test_util_summary_averages_every_counter_per_kernel(tmp_path):
+    rows = kernel_rows("MfmaUtil", {("void lynx::k_verify<1>(lynx::VerifyArgs)", 131072): [30.0, 40.0]})
+    rows += kernel_rows("VALUBusy", {("void lynx::k_verify<1>(lynx::VerifyArgs)", 131072): [50.0, 54.0],
+                                     ("void lynx::k_decode<false, false>(lynx::DecodeArgs)", 16777216): [49.0]})
+    rows += kernel_rows("VALUBusy", {("at::native::foo(int)", 64): [1.0]})
+    p = tmp_path / "u.csv"
+    write_rows(p, rows, ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+    text = bench.util_summary(str(p)).splitlines()
+    assert text[0].split()[2:] == ["MfmaUtil", "VALUBusy"]
+    assert not any("at::native" in ln for ln in text)
+    ver = [ln for ln in text if "k_verify" in ln][0].split()
+    assert ver[-3:] == ["131072", "35", "52"]
+    dec = [ln for ln in text if "k_decode" in ln][0].split()
+    assert dec[-2:] == ["nan", "49"]
