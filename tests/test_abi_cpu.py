@@ -266,3 +266,24 @@ def test_geometry_too_large_for_int_sizes():
     assert L.lynx_encode(GOOD, 1, 1 << 16, 1 << 12, 128, 64, 255.0, 3, GOOD, GOOD, None) == lynx.LYNX_EUNSUPPORTED
     assert L.lynx_decode_full(GOOD, GOOD, 1, 1 << 16, 1 << 12, 128, 64, 255.0, lynx.OUT_BF16, GOOD, None) == \
         lynx.LYNX_EUNSUPPORTED
+
+
+def test_binding_refuses_buffers_before_any_launch():
+    """The binding checks device, dtype, contiguity and sizes of the tensors it passes as
+    pointers; these cases raise on the host without touching a GPU."""
+    import torch
+    kv_host = torch.zeros((256, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="CUDA"):
+        lynx.encode(kv_host, 256, 64, 255.0)
+    with pytest.raises(ValueError, match="whole number"):
+        lynx.encode(torch.zeros((300, 2, 128), dtype=torch.bfloat16), 256, 64, 255.0)
+    a_sz, _ = lynx.stream_sizes(256, 2, 128, 64)
+    with pytest.raises(ValueError, match="CUDA"):
+        lynx.decode_anchor(torch.zeros((1, a_sz), dtype=torch.uint8), 1, 256, 2, 128, 64, 255.0)
+    with pytest.raises(ValueError, match="dtype"):
+        lynx._need(torch.zeros(4, dtype=torch.float16), "out", 0, (torch.bfloat16, torch.float32), device="cpu")
+    with pytest.raises(ValueError, match="contiguous"):
+        lynx._need(torch.zeros((4, 4)).t(), "x", 0, device="cpu")
+    with pytest.raises(ValueError, match="bytes"):
+        lynx._need(torch.zeros(4, dtype=torch.uint8), "x", 5, device="cpu")
+    assert lynx._need(torch.zeros(5, dtype=torch.uint8), "x", 5, device="cpu") is not None

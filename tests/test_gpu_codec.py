@@ -162,3 +162,29 @@ def test_calls_on_two_streams_match_one_stream(gpu):
     two = run([torch.cuda.Stream(), torch.cuda.Stream()])
     for x, y in zip(one, two):
         assert torch.equal(x, y)
+
+
+def test_binding_refuses_undersized_or_mistyped_device_buffers(gpu):
+    """A buffer the kernels would overrun, or read in the wrong format, is refused on the host."""
+    P, C, alpha, Hkv, D = 256, 64, 255.0, 2, 128
+    kv = to_dev(synth.make_kv_np(2 * P, Hkv, D, seed=4))
+    a_sz, r_sz = lynx.stream_sizes(P, Hkv, D, C)
+    small = torch.empty((1, a_sz), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="anchor_out"):
+        lynx.encode(kv, P, C, alpha, anchor_out=small)
+    anc, res = lynx.encode(kv, P, C, alpha)
+    with pytest.raises(ValueError, match="residual"):
+        lynx.decode_full(anc, res[:1], 2, P, Hkv, D, C, alpha)
+    with pytest.raises(ValueError, match="dtype"):
+        lynx.decode_anchor(anc, 2, P, Hkv, D, C, alpha, out=torch.empty((2 * P, Hkv, D), dtype=torch.float16,
+                                                                        device="cuda"))
+    with pytest.raises(ValueError, match="out"):
+        lynx.decode_anchor(anc, 2, P, Hkv, D, C, alpha, out=torch.empty((P, Hkv, D), dtype=torch.bfloat16,
+                                                                        device="cuda"))
+    q32 = torch.zeros((1, 4, D), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="q"):
+        lynx.attn_anchor(q32, anc, anc, 2 * P, Hkv, P, C, alpha)
+    q = q32.to(torch.bfloat16)
+    with pytest.raises(ValueError, match="k_anchor"):
+        lynx.attn_anchor(q, anc[:1], anc, 2 * P, Hkv, P, C, alpha)
+    torch.cuda.synchronize()
