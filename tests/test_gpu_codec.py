@@ -84,6 +84,8 @@ def test_single_page_4096_tokens_k_and_v(gpu):
     (264, 8, 255.0, 1, 2),      # long page: a full tile plus an 8-token tile, the smallest chunk
     (1024, 256, 63.0, 2, 1),    # four tiles of one 256-token chunk each
     (2048, 32, 15.0, 1, 2),     # eight tiles, two pages
+    (256, 64, 1.0, 2, 2),       # alpha 1: the compander close to linear
+    (256, 32, 4096.0, 1, 2),    # a very large alpha
 ])
 def test_codec_shapes(gpu, P, C, alpha, Hkv, n_pages):
     bits = synth.make_kv_np(P * n_pages, Hkv, 128, seed=P + C, layer=Hkv)
