@@ -83,7 +83,11 @@ __device__ __forceinline__ void pack8(const uint32_t* mb, const float* xf, uint3
 // store one j (4 token groups x 8 channel groups) then hit 32 different banks,
 // and the column walk of the reducing threads stays a permutation of one row.
 // Rows are not padded, so the tables of a 64-token chunk fit four workgroups
-// in the 160 KB of LDS of a compute unit.
+// in the 160 KB of LDS of a compute unit.  Chunks of 32 tokens or fewer need larger
+// chunk tables; there the extremes of a row are kept as one word of two BF16 halves
+// (the values are BF16, so nothing is lost), which lets four workgroups fit at C = 32.
+// Four is also the count that serves longer chunks best: five, at the packed size,
+// measured ~3% slower at C = 128.
 __device__ __forceinline__ int lds_col(int c) { return (c & 7) * 8 + (c >> 3); }   // channel -> column
 __device__ __forceinline__ int lds_chan(int col) { return (col & 7) * 8 + (col >> 3); }  // column -> channel
 __device__ __forceinline__ int lds_swz(int row, int col) { return col ^ ((row & 3) << 3); }
@@ -92,8 +96,8 @@ template <int C>
 struct EncodeShared {
   static constexpr int kChunksPerTile = kTileTokens / C;
   double bnd[130];
-  float pmin[kTG][kSlab];
-  float pmax[kTG][kSlab];
+  static constexpr bool kPacked = C <= 32;   // extremes as two BF16 halves of one word
+  uint32_t pext[kTG][kSlab][kPacked ? 1 : 2];  // [0]: min (packed: min low, max high), [1]: max
   double psum[kTG][kSlab];
   uint32_t gpart[kThreads / kSlab][kSlab];  // page min / max of 8 partial rows, two BF16 per word
   float gmin[kSlab];                     // by column
@@ -101,6 +105,28 @@ struct EncodeShared {
   float4 cst[kChunksPerTile][kSlab];     // by column: c_hi, k, -c_lo*k, mu (float32 fast path + stored mu)
   float sig[kChunksPerTile][kSlab];      // stored sigma, by column
 };
+
+// Store / combine the extremes of one partial row entry (BF16 values held as floats).
+template <int C>
+__device__ __forceinline__ void put_extremes(EncodeShared<C>& sh, int row, int col, float mn, float mx) {
+  if constexpr (EncodeShared<C>::kPacked) {
+    sh.pext[row][col][0] = (__float_as_uint(mx) & 0xffff0000u) | (__float_as_uint(mn) >> 16);
+  } else {
+    sh.pext[row][col][0] = __float_as_uint(mn);
+    sh.pext[row][col][1] = __float_as_uint(mx);
+  }
+}
+template <int C>
+__device__ __forceinline__ void merge_extremes(const EncodeShared<C>& sh, int row, int col, float& lo, float& hi) {
+  if constexpr (EncodeShared<C>::kPacked) {
+    const uint32_t w = sh.pext[row][col][0];
+    lo = fminf(lo, __uint_as_float(w << 16));
+    hi = fmaxf(hi, __uint_as_float(w & 0xffff0000u));
+  } else {
+    lo = fminf(lo, __uint_as_float(sh.pext[row][col][0]));
+    hi = fmaxf(hi, __uint_as_float(sh.pext[row][col][1]));
+  }
+}
 
 // Addresses of one encode unit: a 64-channel slab of one kv head of one page.
 struct EncodeUnit {
@@ -173,8 +199,7 @@ __device__ __forceinline__ void store_partials(EncodeShared<C>& sh, const uint4 
   for (int j = 0; j < 8; ++j) {
     const int col = lds_swz(tg, j * 8 + dg);
     sh.psum[tg][col] = sm[j];
-    sh.pmin[tg][col] = cmn[j];
-    sh.pmax[tg][col] = cmx[j];
+    put_extremes(sh, tg, col, cmn[j], cmx[j]);
   }
 }
 
@@ -188,8 +213,7 @@ __device__ __forceinline__ void page_stats(EncodeShared<C>& sh, int tid) {
   float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
   for (int r = part * kRows; r < (part + 1) * kRows; ++r) {
-    lo = fminf(lo, sh.pmin[r][lds_swz(r, col)]);
-    hi = fmaxf(hi, sh.pmax[r][lds_swz(r, col)]);
+    merge_extremes(sh, r, lds_swz(r, col), lo, hi);
   }
   sh.gpart[part][col] = (__float_as_uint(hi) & 0xffff0000u) | (__float_as_uint(lo) >> 16);
 }
@@ -219,8 +243,7 @@ __device__ __forceinline__ void chunk_stats(EncodeShared<C>& sh, float* meta, in
     for (int r = 0; r < G; ++r) {
       const int row = ck * G + r, pc = lds_swz(row, col);
       s += sh.psum[row][pc];
-      lo = fminf(lo, sh.pmin[row][pc]);
-      hi = fmaxf(hi, sh.pmax[row][pc]);
+      merge_extremes(sh, row, pc, lo, hi);
     }
     float gmin32, gscale;
     if (page_stored) {
@@ -437,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void k_page_finish(EncodeArgs a) {
 // (PAGE_STORED false) takes Stage 1 from the same partials Stage 2 uses; a longer page
 // (PAGE_STORED true) reads the gamma that k_page_extremes and k_page_finish stored.
 template <int C, bool PAGE_STORED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C >= 64 ? 4 : 2))) void k_encode(EncodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C >= 32 ? 4 : 2))) void k_encode(EncodeArgs a) {
   __shared__ EncodeShared<C> sh;
   const Geometry& g = a.g;
   const int w = xcd_remap(blockIdx.x, gridDim.x);
