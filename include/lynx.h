@@ -13,7 +13,10 @@
  *     tensors), owned by the caller, 16-byte aligned.  The library allocates
  *     nothing, keeps no global state, and is re-entrant.
  *   - `hip_stream` is a hipStream_t (NULL = the legacy default stream).  Work is
- *     enqueued asynchronously on it; the host is never synchronised.
+ *     enqueued asynchronously on it; the host is never synchronised.  Calls on
+ *     different streams may run at once (give each its own output buffers): many
+ *     small calls, such as one per layer tensor, keep the GPU fuller when they
+ *     alternate over two streams than when they queue on one.
  *   - Argument errors are detected on the host and returned BEFORE anything
  *     is launched; nothing is written in that case.  A failed launch returns
  *     LYNX_ELAUNCH.  No C++ exception crosses this boundary.
