@@ -71,7 +71,8 @@ OP_KERNELS = {
     "encode": [("lynx::k_encode<%d, false>" % C, LAYERS * 2 * TOKENS // P * KVH * 2 * 256)],
     "decode_anchor": [("lynx::k_decode<false, false>", None)],
     "decode_full": [("lynx::k_decode<true, false>", None)],
-    "attn_anchor": [("lynx::k_attn_anchor<%d>" % (64 if C % 64 == 0 else 32), None), ("lynx::k_attn_combine", None)],
+    "attn_anchor": [("lynx::k_attn_anchor<%s>" % ("64, 1" if C % 64 == 0 else "64, 2" if P % 64 == 0 else "32, 1"), None),
+                    ("lynx::k_attn_combine", None)],
     "attn_verify": [("lynx::k_verify<%d>" % (1 if C % 64 == 0 else 2), None), ("lynx::k_verify_combine", None)],
     "copy": [("hbm_probe::k_probe_copy", None)],
 }

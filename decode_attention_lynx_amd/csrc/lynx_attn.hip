@@ -117,11 +117,14 @@ __device__ __forceinline__ h8 lookup_row(uint32_t w, const uint32_t* s_pair, uin
 }
 
 // one wave's raw inputs for one 64-token tile
-template <int TILE>
+// CPT: chunks per tile (1, or 2 for a chunk of 32 in a 64-token tile)
+template <int TILE, int CPT>
 struct TileIn {
   uint4 kw[TILE / 16];      // K code rows tin + 16mb + n, bytes 16g .. 16g+15
   uint32_t vw[TILE / 4];    // V code dword n of the rows this lane feeds to the value MFMAs
-  float km[8], vm[8];   // gamma_min, gamma_scale, mu, sigma of channels 2*lane, 2*lane+1
+  // gamma_min, gamma_scale, then mu and sigma of each chunk of the tile, for channels
+  // 2*lane, 2*lane+1: [0..1] gamma_min, [2..3] gamma_scale, [4+4k..5+4k] mu, [6+4k..7+4k] sigma
+  float km[4 + 4 * CPT], vm[4 + 4 * CPT];
 };
 
 // Per-lane byte offsets of one wave's tile loads; they do not depend on the tile, whose
@@ -142,9 +145,9 @@ __device__ __forceinline__ TileOffsets tile_offsets(int lane) {
 }
 
 // `tile` is wave-uniform: the page, chunk and segment addresses are scalar arithmetic.
-template <int TILE>
+template <int TILE, int CPT>
 __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int tile, const TileOffsets& lo,
-                                          TileIn<TILE>& t) {
+                                          TileIn<TILE, CPT>& t) {
   const int tok = tile * TILE;
   const int page = tok / a.P;
   const int tin = tok - page * a.P;
@@ -167,10 +170,16 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int
     }
   const uint8_t* kmb = a.kanc + seg + a.codes + (size_t)kvh * kHeadDim * 4;
   const uint8_t* vmb = a.vanc + seg + a.codes + (size_t)kvh * kHeadDim * 4;
-  const size_t offs[4] = {0, (size_t)a.H, 2 * (size_t)a.H + (size_t)kc * a.H,
-                          2 * (size_t)a.H + (size_t)(a.nck + kc) * a.H};
+  size_t offs[2 + 2 * CPT];
+  offs[0] = 0;
+  offs[1] = (size_t)a.H;
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
+  for (int k = 0; k < CPT; ++k) {
+    offs[2 + 2 * k] = 2 * (size_t)a.H + (size_t)(kc + k) * a.H;
+    offs[3 + 2 * k] = 2 * (size_t)a.H + (size_t)(a.nck + kc + k) * a.H;
+  }
+#pragma unroll
+  for (int f = 0; f < 2 + 2 * CPT; ++f) {
     const float2 k2 = *reinterpret_cast<const float2*>(kmb + offs[f] * 4 + lo.meta);
     const float2 v2 = *reinterpret_cast<const float2*>(vmb + offs[f] * 4 + lo.meta);
     t.km[2 * f] = k2.x;
@@ -180,7 +189,7 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int
   }
 }
 
-template <int TILE>
+template <int TILE, int CPT>
 __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void k_attn_anchor(AttnArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -198,8 +207,8 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   __shared__ uint32_t s_big[kPairWords > kMergeWords ? kPairWords : kMergeWords];
   // per wave: (A_K, B_K) and (A_V, B_V) of channels 2i, 2i+1 at slot swz(i), where
   // swz(16g + t) = 4t + g puts the 4 lane groups' simultaneous reads in different banks
-  __shared__ float4 s_kab[kAttnWaves][kHeadDim / 2];
-  __shared__ float4 s_vab[kAttnWaves][kHeadDim / 2];
+  __shared__ float4 s_kab[kAttnWaves][CPT][kHeadDim / 2];
+  __shared__ float4 s_vab[kAttnWaves][CPT][kHeadDim / 2];
   uint32_t* s_pair = s_big;
 
 #pragma unroll 8
@@ -233,72 +242,77 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int seq_len = a.seq_lens == nullptr ? a.T : min(max(a.seq_lens[b], 0), a.T);
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min((seq_len + TILE - 1) / TILE, t_begin + a.tiles_per_split);   // may be empty
-  float4* kab = s_kab[wave];
-  float4* vab = s_vab[wave];
+  float4 (*kab)[kHeadDim / 2] = s_kab[wave];
+  float4 (*vab)[kHeadDim / 2] = s_vab[wave];
 
   const TileOffsets toff = tile_offsets(lane);
 
   // one 64-token tile of this wave: scores, online softmax, values
-  auto process = [&](const TileIn<TILE>& cur, int tile) {
+  auto process = [&](const TileIn<TILE, CPT>& cur, int tile) {
 
     // ---- the chunk's affine maps for channels 2*lane, 2*lane+1, shared through LDS:
     //      A = (gamma_scale+eps)(sigma+eps), B = gamma_min + mu (gamma_scale+eps);
     //      the key map carries the softmax scale (base 2).  One 16-byte record per
     //      channel pair, at slot swz(lane).
-    {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
       float ak[2], bk[2], av[2], bv[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const float d1k = cur.km[2 + e] + (float)kEps, d2k = cur.km[6 + e] + (float)kEps;
+        const float d1k = cur.km[2 + e] + (float)kEps, d2k = cur.km[6 + 4 * k + e] + (float)kEps;
         ak[e] = d1k * d2k * qscale;
-        bk[e] = fmaf(cur.km[4 + e], d1k, cur.km[e]) * qscale;
-        const float d1v = cur.vm[2 + e] + (float)kEps, d2v = cur.vm[6 + e] + (float)kEps;
+        bk[e] = fmaf(cur.km[4 + 4 * k + e], d1k, cur.km[e]) * qscale;
+        const float d1v = cur.vm[2 + e] + (float)kEps, d2v = cur.vm[6 + 4 * k + e] + (float)kEps;
         av[e] = d1v * d2v;
-        bv[e] = fmaf(cur.vm[4 + e], d1v, cur.vm[e]);
+        bv[e] = fmaf(cur.vm[4 + 4 * k + e], d1v, cur.vm[e]);
       }
       const int slot = 4 * (lane & 15) + (lane >> 4);
-      kab[slot] = make_float4(ak[0], ak[1], bk[0], bk[1]);
-      vab[slot] = make_float4(av[0], av[1], bv[0], bv[1]);
+      kab[k][slot] = make_float4(ak[0], ak[1], bk[0], bk[1]);
+      vab[k][slot] = make_float4(av[0], av[1], bv[0], bv[1]);
     }
     __builtin_amdgcn_wave_barrier();
 
-    // ---- fold the key map into the query: qt = q*A_K (float16 hi / lo by column), beta = q.B_K
-    h8 bq[4];
-    float beta = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      uint32_t bw[4];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const float4 ab = kab[4 * (4 * kk + e2) + g];      // channels 32g + 8kk + 2e2, +1
-        const uint32_t w = qw[4 * kk + e2];
-        const float x0 = bf16_lo(w), x1 = bf16_hi(w);
-        beta = fmaf(x0, ab.z, fmaf(x1, ab.w, beta));
-        const float q0 = x0 * ab.x, q1 = x1 * ab.y;
-        // float16 split of the folded query: columns 0..7 take hi = rtz(q), columns
-        // 8..15 take rtz(q - hi); hi + lo carries ~22 bits of q
-        const auto hi = __builtin_amdgcn_cvt_pkrtz(q0, q1);
-        const float r0 = fmaf(-(float)hi[0], lo_w, q0), r1 = fmaf(-(float)hi[1], lo_w, q1);
-        bw[e2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
-      }
-      const u32x4v bv4 = {bw[0], bw[1], bw[2], bw[3]};
-      bq[kk] = __builtin_bit_cast(h8, bv4);
-    }
-    beta = wave_sum_g(beta);
-
-    // ---- scores: S^T = L_K (64 tokens x 128) * qt (128 x 16 columns)
+    // ---- per chunk of the tile: fold its key map into the query, qt = q*A_K (float16
+    //      hi / lo by column) and beta = q.B_K, then the scores of its tokens:
+    //      S^T = L_K (tokens x 128) * qt (128 x 16 columns)
     constexpr int NS = TILE / 4;         // scores per lane: TILE/16 row blocks x 4
+    constexpr int MBC = TILE / 16 / CPT; // row blocks of 16 tokens per chunk
     float s[NS];
-    const float hb = 0.5f * beta;        // each of the two column halves carries half of beta
 #pragma unroll
-    for (int mb = 0; mb < TILE / 16; ++mb) {
-      f4 acc = f4{hb, hb, hb, hb};
-      const uint32_t w4[4] = {cur.kw[mb].x, cur.kw[mb].y, cur.kw[mb].z, cur.kw[mb].w};
+    for (int k = 0; k < CPT; ++k) {
+      h8 bq[4];
+      float beta = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lookup_row(w4[kk], s_pair, lane4), bq[kk], acc, 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk) {
+        uint32_t bw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[4 * mb + i] = acc[i] + dpp_row_ror8(acc[i]);
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float4 ab = kab[k][4 * (4 * kk + e2) + g];   // channels 32g + 8kk + 2e2, +1
+          const uint32_t w = qw[4 * kk + e2];
+          const float x0 = bf16_lo(w), x1 = bf16_hi(w);
+          beta = fmaf(x0, ab.z, fmaf(x1, ab.w, beta));
+          const float q0 = x0 * ab.x, q1 = x1 * ab.y;
+          // float16 split of the folded query: columns 0..7 take hi = rtz(q), columns
+          // 8..15 take rtz(q - hi); hi + lo carries ~22 bits of q
+          const auto hi = __builtin_amdgcn_cvt_pkrtz(q0, q1);
+          const float r0 = fmaf(-(float)hi[0], lo_w, q0), r1 = fmaf(-(float)hi[1], lo_w, q1);
+          bw[e2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+        }
+        const u32x4v bv4 = {bw[0], bw[1], bw[2], bw[3]};
+        bq[kk] = __builtin_bit_cast(h8, bv4);
+      }
+      beta = wave_sum_g(beta);
+      const float hb = 0.5f * beta;      // each of the two column halves carries half of beta
+#pragma unroll
+      for (int mb = MBC * k; mb < MBC * (k + 1); ++mb) {
+        f4 acc = f4{hb, hb, hb, hb};
+        const uint32_t w4[4] = {cur.kw[mb].x, cur.kw[mb].y, cur.kw[mb].z, cur.kw[mb].w};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lookup_row(w4[kk], s_pair, lane4), bq[kk], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[4 * mb + i] = acc[i] + dpp_row_ror8(acc[i]);
+      }
     }
     if ((tile + 1) * TILE > seq_len) {   // the sequence ends inside this tile: mask the tail
 #pragma unroll
@@ -315,53 +329,62 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
     mt = wave_max_g(mt);
     const float m_new = fmaxf(m_run, mt);
     const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-    float lsum = 0.0f;
+    float lsum[CPT];                     // per chunk: its tokens' p of this lane
     h8 pt[TILE / 32];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) lsum[k] = 0.0f;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const float p = __builtin_amdgcn_exp2f(s[i] - m_new);
-      lsum += p;
+      lsum[i / (NS / CPT)] += p;
       pt[i >> 3][i & 7] = (_Float16)p;
     }
-    l_run = fmaf(l_run, corr, lsum);
+    float lsum_all = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) lsum_all += lsum[k];
+    l_run = fmaf(l_run, corr, lsum_all);
     if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0) {   // the running max moved for some head
 #pragma unroll
       for (int j = 0; j < 8; ++j) o_acc[j] *= corr;
     }
     m_run = m_new;
-    const float lt = wave_sum_g(lsum);
 
-    // ---- values: T^T = L_V (128 x 64 tokens) * p (64 tokens x 16 columns), block j holds d = 8*row + j.
-    // Token pairs (2i, 2i+1) of a k-step are interleaved into pair-table indices per channel.
-    f4 tacc[8];
+    // ---- values, per chunk: T^T = L_V (128 x its tokens) * p (its tokens x 16 columns),
+    // block j holds d = 8*row + j.  Token pairs (2i, 2i+1) of a k-step are interleaved into
+    // pair-table indices per channel.  Then the chunk's value map is undone:
+    // o += A_V * T + B_V * sum(p), channel d = 32g + 8i + j.
+    constexpr int KSC = TILE / 32 / CPT;   // k-steps of 32 tokens per chunk
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tacc[j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < CPT; ++k) {
+      const float lt = wave_sum_g(lsum[k]);
+      f4 tacc[8];
 #pragma unroll
-    for (int ks = 0; ks < TILE / 32; ++ks) {
-      uint32_t ev[4], od[4];
+      for (int j = 0; j < 8; ++j) tacc[j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = KSC * k; ks < KSC * (k + 1); ++ks) {
+        uint32_t ev[4], od[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w0 = cur.vw[8 * ks + 2 * i], w1 = cur.vw[8 * ks + 2 * i + 1];
+          ev[i] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);   // byte k: channel 2k of tokens 2i, 2i+1
+          od[i] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);  // byte k: channel 2k+1
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t* src = (j & 1) ? od : ev;
+          const u32x4v r = {pair_at(s_pair, lane4, src[0], j >> 1), pair_at(s_pair, lane4, src[1], j >> 1),
+                            pair_at(s_pair, lane4, src[2], j >> 1), pair_at(s_pair, lane4, src[3], j >> 1)};
+          tacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, r), pt[ks], tacc[j], 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t w0 = cur.vw[8 * ks + 2 * i], w1 = cur.vw[8 * ks + 2 * i + 1];
-        ev[i] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);   // byte k: channel 2k of tokens 2i, 2i+1
-        od[i] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);  // byte k: channel 2k+1
-      }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t* src = (j & 1) ? od : ev;
-        const u32x4v r = {pair_at(s_pair, lane4, src[0], j >> 1), pair_at(s_pair, lane4, src[1], j >> 1),
-                          pair_at(s_pair, lane4, src[2], j >> 1), pair_at(s_pair, lane4, src[3], j >> 1)};
-        tacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, r), pt[ks], tacc[j], 0, 0, 0);
-      }
-    }
-
-    // ---- undo the value map: o += A_V * T + B_V * sum(p), channel d = 32g + 8i + j
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j2 = 0; j2 < 4; ++j2) {
-        const float4 ab = vab[4 * (4 * i + j2) + g];       // channels 32g + 8i + 2j2, +1
-        o_acc[2 * j2][i] = fmaf(ab.x, tacc[2 * j2][i], fmaf(ab.z, lt, o_acc[2 * j2][i]));
-        o_acc[2 * j2 + 1][i] = fmaf(ab.y, tacc[2 * j2 + 1][i], fmaf(ab.w, lt, o_acc[2 * j2 + 1][i]));
+        for (int j2 = 0; j2 < 4; ++j2) {
+          const float4 ab = vab[k][4 * (4 * i + j2) + g];   // channels 32g + 8i + 2j2, +1
+          o_acc[2 * j2][i] = fmaf(ab.x, tacc[2 * j2][i], fmaf(ab.z, lt, o_acc[2 * j2][i]));
+          o_acc[2 * j2 + 1][i] = fmaf(ab.y, tacc[2 * j2 + 1][i], fmaf(ab.w, lt, o_acc[2 * j2 + 1][i]));
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();   // the next tile rewrites this wave's (A, B) tables
@@ -369,7 +392,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
 
   // tiles t_begin + wave, + kAttnWaves, ...: one tile buffer per wave; three waves per SIMD
   // hide each other's load latency (a second buffer would cost the third wave's registers)
-  TileIn<TILE> cur;
+  TileIn<TILE, CPT> cur;
   for (int tile = t_begin + wave; tile < t_end; tile += kAttnWaves) {
     load_tile(a, b, kvh, tile, toff, cur);
     process(cur, tile);
@@ -437,16 +460,24 @@ __global__ __launch_bounds__(kHeadDim) void k_attn_combine(AttnArgs a) {
 namespace {
 
 struct AttnPlan {
-  int tile, splits, tiles_per_split, ntiles;
+  int tile, cpt, splits, tiles_per_split, ntiles;
 };
 
-// Tile of a chunk: 64 tokens, or 32 for a chunk of 32; 0 for chunks the kernel does not take.
-int attn_tile(int C) { return C % 64 == 0 ? 64 : (C % 32 == 0 ? 32 : 0); }
+// Tile of the context: 64 tokens inside one chunk of 64 or more, or two chunks of 32 when
+// the pages hold whole 64-token tiles; 32 tokens for a chunk of 32 in pages of an odd
+// number of chunks; 0 for chunks the kernel does not take.  *cpt = chunks per tile.
+int attn_tile(int C, int P, int* cpt) {
+  *cpt = 1;
+  if (C % 64 == 0) return 64;
+  if (C != 32) return 0;
+  if (P % 64 == 0) { *cpt = 2; return 64; }
+  return 32;
+}
 
 bool attn_plan(int batch, int ctx, int Hq, int Hkv, int D, int P, int C, AttnPlan* pl) {
   if (batch <= 0 || ctx <= 0 || Hq <= 0 || Hkv <= 0 || P <= 0 || C <= 0) return false;
   if (ctx % P != 0 || P % C != 0 || Hq % Hkv != 0) return false;
-  pl->tile = attn_tile(C);
+  pl->tile = attn_tile(C, P, &pl->cpt);
   if (D != kHeadDim || pl->tile == 0 || Hq / Hkv > kMaxGroup) return false;
   pl->ntiles = ctx / pl->tile;
   // One workgroup per compute unit of the 256-CU gfx950 parts (12 waves fill a CU at this
@@ -494,7 +525,9 @@ int attn_launch(const void* q_dev, const void* k_anchor_dev, const void* v_ancho
   if (ctx_tokens % page_tokens != 0 || page_tokens % chunk != 0 || q_heads % kv_heads != 0) return LYNX_EINVAL;
   if (!std::isfinite(alpha) || !(alpha > 0.0f) || !std::isfinite(sm_scale)) return LYNX_EINVAL;
   if (out_dtype != LYNX_OUT_BF16 && out_dtype != LYNX_OUT_F32) return LYNX_EINVAL;
-  if (head_dim != kHeadDim || attn_tile(chunk) == 0 || q_heads / kv_heads > kMaxGroup || batch > 65535 ||
+  int cpt_unused = 0;
+  if (head_dim != kHeadDim || attn_tile(chunk, page_tokens, &cpt_unused) == 0 || q_heads / kv_heads > kMaxGroup ||
+      batch > 65535 ||
       kv_heads > 65535)
     return LYNX_EUNSUPPORTED;
   if (batch == 0) return LYNX_OK;
@@ -545,8 +578,9 @@ int attn_launch(const void* q_dev, const void* k_anchor_dev, const void* v_ancho
   }
   for (int bt = 0; bt < 256; ++bt) a.pair[bt] = (uint32_t)lut[bt & 15] | ((uint32_t)lut[bt >> 4] << 16);
   void* kargs[] = {&a};
-  const void* fn = pl.tile == 64 ? reinterpret_cast<const void*>(&k_attn_anchor<64>)
-                                 : reinterpret_cast<const void*>(&k_attn_anchor<32>);
+  const void* fn = pl.tile == 32  ? reinterpret_cast<const void*>(&k_attn_anchor<32, 1>)
+                   : pl.cpt == 2 ? reinterpret_cast<const void*>(&k_attn_anchor<64, 2>)
+                                 : reinterpret_cast<const void*>(&k_attn_anchor<64, 1>);
   hipError_t e = hipLaunchKernel(fn,
                                  dim3((unsigned)pl.splits, (unsigned)kv_heads, (unsigned)batch),
                                  dim3(kAttnWaves * 64), kargs, 0, stream);
