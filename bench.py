@@ -50,7 +50,8 @@ def alg_bytes_per_elem(op: str) -> float:
     float32 metadata 8/C + 8/P B)."""
     meta = 8.0 / C + 8.0 / P
     return {"encode": 2.0 + 1.0 + meta, "decode_anchor": 0.5 + meta + 2.0, "decode_full": 1.0 + meta + 2.0,
-            "attn_anchor": 0.5 + meta, "attn_verify": 1.0 + meta, "copy": 4.0}[op]
+            "attn_anchor": 0.5 + meta, "attn_verify": 1.0 + meta, "copy": 4.0,
+            "attn_anchor_c32": 0.5 + 8.0 / 32 + 8.0 / P}[op]
 
 
 def op_flops(op: str) -> float:
@@ -62,7 +63,7 @@ def op_elems(op: str) -> int:
     """KV elements one launch of an op processes (the copy counts 2-byte elements of 1 GiB)."""
     return {"encode": LAYERS * 2 * TOKENS * KVH * D, "decode_anchor": LAYERS * 2 * TOKENS * KVH * D,
             "decode_full": LAYERS * 2 * TOKENS * KVH * D, "attn_anchor": 2 * AB * AT * AHKV * D,
-            "attn_verify": 2 * AB * AT * AHKV * D,
+            "attn_verify": 2 * AB * AT * AHKV * D, "attn_anchor_c32": 2 * AB * AT * AHKV * D,
             "copy": (1 << 30) // 2}[op]
 
 
@@ -398,7 +399,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ops", default="encode,decode_anchor,decode_full,attn_anchor")
-    ap.add_argument("--next-ops", default="attn_verify,encode_to_host",
+    ap.add_argument("--next-ops", default="attn_verify,encode_to_host,attn_anchor_c32",
                     help="ops timed after the step, on their own (empty: none)")
     ap.add_argument("--counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="summarise two rocprofv3 --pmc runs of this benchmark into per-op HBM bytes")
@@ -455,15 +456,18 @@ def main():
     # attention inputs: segments of 16 sequences x 32768 tokens, encoded once (the residual
     # stream only when the verification pass is timed)
     akv = torch.empty((AB * AT, AHKV, D), dtype=torch.bfloat16, device=dev)
-    att, att_res = {}, {}
+    att, att_res, att32 = {}, {}, {}
     for kv_idx in (0, 1):
         for b in range(AB):
             synth.make_kv_torch(AT, AHKV, D, seed=1, layer=b, kv_idx=kv_idx, out=akv[b * AT:(b + 1) * AT])
         att[kv_idx], att_res[kv_idx] = lynx.encode(akv, P, C, ALPHA, residual="attn_verify" in next_ops + ops)
+        if "attn_anchor_c32" in next_ops + ops:      # the same KV at the pages' chunk of 32 tokens
+            att32[kv_idx], _ = lynx.encode(akv, P, 32, ALPHA, residual=False)
     del akv
     q = synth.make_q_torch(AB, AHQ, D, seed=0)
     ws = torch.empty(lynx.attn_workspace_bytes(AB, AT, AHQ, AHKV, D, P, C), dtype=torch.uint8, device=dev)
     o_att = torch.empty((AB, AHQ, D), dtype=torch.bfloat16, device=dev)
+    ws32 = torch.empty(lynx.attn_workspace_bytes(AB, AT, AHQ, AHKV, D, P, 32), dtype=torch.uint8, device=dev)
     if "attn_verify" in next_ops + ops:
         qv = synth.make_q_torch(AB * AM, AHQ, D, seed=2).view(AB, AM, AHQ, D)
         ws_v = torch.empty(lynx.attn_verify_workspace_bytes(AB, AM, AT, AHQ, AHKV, D, P, C), dtype=torch.uint8,
@@ -507,6 +511,8 @@ def main():
         elif op == "d2h_copy":      # reference: the same bytes, already encoded, copied device -> host
             anchor_h.copy_(anchor, non_blocking=True)
             residual_h.copy_(residual, non_blocking=True)
+        elif op == "attn_anchor_c32":
+            lynx.attn_anchor(q, att32[0], att32[1], AT, AHKV, P, 32, ALPHA, workspace=ws32, out=o_att)
         elif op == "attn_verify":
             lynx.attn_verify(qv, att[0], att_res[0], att[1], att_res[1], AT, AHKV, P, C, ALPHA, workspace=ws_v,
                              out=o_ver, lse=lse_ver)
@@ -595,6 +601,12 @@ def main():
                             "d2h_copy_GBs": round(nbytes / d2h_ms / 1e6, 2),
                             "copy_over_pipeline": round(d2h_ms / t, 4)}
             continue
+        if op == "attn_anchor_c32":
+            ab = alg_bytes_per_elem(op) * op_elems(op)
+            next_rep[op] = {"ms": round(t, 4), "alg_GBs": round(ab / t / 1e6, 1),
+                            "frac_hbm_peak": round(ab / t / 1e6 / HBM_PEAK_GBS, 4), "chunk": 32,
+                            "alg_bytes_per_launch": int(ab)}
+            continue
         fl = op_flops(op)
         next_rep[op] = {"ms": round(t, 4), "TFLOPs": round(fl / t / 1e9, 1),
                         "frac_mfma_peak": round(fl / t / 1e9 / MFMA_PEAK_TFLOPS, 4),
@@ -619,7 +631,9 @@ def main():
                                                f"draft tokens x {AHQ} q / {AHKV} kv heads x {D}, {AT}-token "
                                                "context), bound: mfma; encode_to_host: the request encoded "
                                                f"in groups of {PIPE_GROUP} pages and copied to pinned host "
-                                               "memory, bound: the device-to-host link", "ops": next_rep},
+                                               "memory, bound: the device-to-host link; attn_anchor_c32: the "
+                                               "anchor attention of the step at a chunk of 32 tokens, bound: hbm",
+                                   "ops": next_rep},
                    "arith": "float32 codec (float64 statistics and boundary cases), float16 MFMA attention "
                             "with float32 accumulation"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
