@@ -159,7 +159,9 @@ size_t lynx_attn_workspace_bytes(int batch, int ctx_tokens, int q_heads, int kv_
  *                  hq / (q_heads/kv_heads).  Group size q_heads/kv_heads <= 8.
  *   ctx_tokens   : a positive multiple of page_tokens.
  *   chunk        : a multiple of 32 in this library (else LYNX_EUNSUPPORTED): each
- *                  wave step covers 64 tokens, or 32 when chunk == 32, inside one chunk.
+ *                  wave step covers 64 tokens of one chunk, or, when chunk == 32, 64
+ *                  tokens of two chunks if page_tokens is a multiple of 64 and 32
+ *                  tokens of one chunk otherwise.
  *   sm_scale     : > 0, or <= 0 to use 1/sqrt(head_dim).
  *   workspace_dev, ws_bytes : at least lynx_attn_workspace_bytes(...) bytes.
  *   out_dtype    : LYNX_OUT_BF16 or LYNX_OUT_F32.
