@@ -35,7 +35,6 @@ Readings (where the pages are silent, ambiguous or inconsistent):
             V_res = V_recon - I in [-8, 7], Q_anc = V_mag*S + min(S, 0)
             (Eq. 9 unchanged) in [-8, 7].  Decode recovers I = V_recon - V_res
             exactly, and anchor-only decode is full decode with V_res = 0.
-            The literal form is kept as `split_literal` for the worked example.
   R-nibble  a 4-bit code q is stored as the nibble q & 0xF (two's complement);
             two codes share a byte, the even element in the low nibble.
   R-layout  within a page, codes are ordered [kv_head][token][head_dim]; a
@@ -174,17 +173,6 @@ def split_streams(I: np.ndarray, S: np.ndarray):
     V_res = V_recon - I
     Q_anc = V_mag * S + np.minimum(S, 0)        # Eq. 9
     return Q_anc.astype(np.int32), V_res.astype(np.int32)
-
-
-def split_literal(I: int, S: int):
-    """Stage 4 exactly as printed (bias before the shift); used only to replay the worked example.
-    Returns (I_bias, V_mag, V_recon, V_res, Q_anc)."""
-    I_bias = I + 7
-    V_mag = I_bias >> 4
-    V_recon = V_mag << 4
-    V_res = V_recon - I
-    Q_anc = V_mag * S + min(S, 0)
-    return I_bias, V_mag, V_recon, V_res, Q_anc
 
 
 def anchor_sign_mag(Q_anc: np.ndarray):

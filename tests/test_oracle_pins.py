@@ -36,27 +36,31 @@ def test_worked_example_forward():
     assert int(I[0]) == int(g["I"][0]) and int(S[0]) == 1
 
 
-def test_worked_example_literal_split_and_recombination():
-    g = load("worked_example.txt")
-    I_bias, V_mag, V_recon, V_res, Q_anc = o.split_literal(int(g["I"][0]), +1)
-    assert (I_bias, V_mag, V_recon, V_res, Q_anc) == (
-        int(g["I_bias"][0]), int(g["V_mag"][0]), int(g["V_recon"][0]), int(g["V_res"][0]),
-        int(g["Q_anc"][0]))
-    assert V_res == int(g["Q_res"][0])
-    # the page's corrected decode: I = V_recon - V_res recovers the code exactly
-    assert V_recon - V_res == int(g["I_full"][0])
+def test_worked_example_through_r_split():
+    """The worked example's Stage 4 numbers through split_streams / code_anchor_only / code_full.
 
-
-def test_worked_example_reading_r_split():
-    """Under the repository's reading the anchor is the same (Q_anc = 7) and the
-    full code is recovered exactly, as on the page."""
+    Under the repository's +7-at-reconstruction reading the anchor is the page's (V_mag = 7,
+    Q_anc = 7) and the full code is recovered exactly (I = 118), as on the page.  The page's
+    printed V_recon / V_res (112 / -6) belong to its bias-before-shift form and differ here
+    (119 / 1); their own recombination 112 - (-6) = 118 is checked as page arithmetic."""
     g = load("worked_example.txt")
-    I = np.array([int(g["I"][0])])
-    q_anc, q_res = o.split_streams(I, np.array([1]))
-    assert int(q_anc[0]) == int(g["Q_anc"][0])
-    assert int(q_res[0]) == 16 * 7 + 7 - 118       # V_recon = 119 under the reading
-    S, I_full = o.code_full(q_anc, q_res)
-    assert int(I_full[0]) == 118 and int(S[0]) == 1
+    I = int(g["I"][0])
+    q_anc, q_res = o.split_streams(np.array([I]), np.array([1]))
+    assert int(q_anc[0]) == int(g["Q_anc"][0]) == 7
+    assert int(q_res[0]) == 1                       # V_recon 119 - I 118 under the reading
+    S_a, I_a = o.code_anchor_only(q_anc)
+    assert int(S_a[0]) == 1 and int(I_a[0]) == 16 * int(g["V_mag"][0]) + 7 == 119
+    S_f, I_f = o.code_full(q_anc, q_res)
+    assert int(S_f[0]) == 1 and int(I_f[0]) == int(g["I_full"][0]) == 118
+    assert int(g["V_recon"][0]) - int(g["V_res"][0]) == int(g["I_full"][0])
+    # anchor-only value: the page prints ~0.729 (after its 256^0.882 slip); the reading's
+    # anchor level 119 gives 0.704, within 4% of it and within 5% of x_final = 0.6727
+    alpha = g["alpha"][0]
+    anchor_val = o.alaw_inverse(I_a, alpha)[0]
+    assert abs(anchor_val - 0.704024) < 1e-6
+    assert abs(anchor_val - g["anchor_value"][0]) / g["anchor_value"][0] < 0.04
+    xf = g["x_final_num"][0] / g["x_final_den"][0]
+    assert abs(anchor_val - xf) / xf < 0.05
 
 
 def test_worked_example_reconstruction():
@@ -246,6 +250,65 @@ def test_two_token_chunks_brute_force():
     full = o.decode_page_full(enc["Q_anc"], enc["Q_res"], enc["mu"], enc["sigma"], enc["gmin"],
                               enc["gscale"], 2, 255.0)
     assert np.max(np.abs(full - X)) < 2e-6 * (8 + o.EPS)
+
+
+@pytest.mark.parametrize("alpha", [15.0, 63.0, 255.0])
+@pytest.mark.parametrize("C", [8, 64, 256])
+def test_codes_given_metadata_reproduces_encode(alpha, C):
+    """Stages 2-4 run on a page's own stored metadata give that page's codes bit for bit
+    (this is the checker every GPU code comparison runs on the GPU's metadata)."""
+    bits = synth.make_kv_np(256, 2, 8, seed=11 + C)
+    X = o.bf16_bits_to_f64(bits).reshape(256, 16)
+    enc = o.encode_page(X, C, alpha)
+    got = o.codes_given_metadata(X, enc["gmin"], enc["gscale"], enc["mu"], enc["sigma"], C, alpha)
+    for k in ("I", "S", "Q_anc", "Q_res"):
+        assert np.array_equal(got[k], enc[k]), k
+    assert np.array_equal(got["Y"], enc["Y"])
+
+
+def test_codes_given_metadata_hand_computed():
+    """Altered metadata on the two-token page, codes derived by hand from Eq. 7 and Eq. 9.
+
+    Page X (P = 4, H = 2, C = 2) with gamma_min = (-1, -3), gamma_scale = (8, 8), D1 = 8 + eps.
+    (a) sigma doubled: each live chunk {a, b} has X_n = mu -+ s with s = |a - b| / (2 D1), so
+        X_f = -+ s / (2 s32 + eps) ~ -+1/2 and Y = 127 ln(1 + alpha/2) / ln(1 + alpha) = 111.21 at
+        alpha = 255: I = 111, V_mag = 6, Q_anc = 6 (S = +1) or -7 (S = -1), Q_res = 103 - 111 = -8.
+    (b) mu moved to the chunk's lower X_n with sigma unchanged: the lower token gives X_f = 0
+        (I = 0, S = +1, codes (0, 7)); the upper one X_f = 2 s / (s + eps) ~ 2, clipped to I = 127.
+    Swapping gamma_min and gamma_scale, or mu and sigma, in the checker breaks both."""
+    X = np.array([[0.5, -3.0], [2.0, 5.0], [7.0, -3.0], [-1.0, -3.0]])
+    gmin = np.array([-1.0, -3.0], np.float32)
+    gscale = np.array([8.0, 8.0], np.float32)
+    D1 = 8.0 + o.EPS
+    # hand-derived chunk statistics (chunk 1 of channel 1 is constant at gamma_min: X_n = 0)
+    lo = np.array([[0.5, -3.0], [-1.0, -3.0]])     # lower value of each chunk, per channel
+    hi = np.array([[2.0, 5.0], [7.0, -3.0]])
+    s = (hi - lo) / (2 * D1)
+    mu = ((lo + hi) / 2 - gmin.astype(np.float64)) / D1
+    mu32, s32 = mu.astype(np.float32), s.astype(np.float32)
+    alpha = 255.0
+    Y_half = 127 * math.log(1 + alpha / 2) / math.log(1 + alpha)
+    assert 111.0 < Y_half < 111.5
+    live = np.array([[True, True], [True, False]])
+    # (a) sigma doubled
+    got = o.codes_given_metadata(X, gmin, gscale, mu32, (2 * s32).astype(np.float32), 2, alpha)
+    expect_S = np.array([[-1, -1], [1, 1], [1, 1], [-1, 1]])
+    expect_I = np.where(np.repeat(live, 2, axis=0), 111, 0)
+    assert np.array_equal(got["I"], expect_I)
+    assert np.array_equal(got["S"], expect_S)
+    assert np.array_equal(got["Q_anc"], np.where(expect_I == 111, np.where(expect_S < 0, -7, 6), 0))
+    assert np.array_equal(got["Q_res"], np.where(expect_I == 111, -8, 7))
+    # (b) mu at the chunk's lower X_n, sigma as encoded
+    mu_lo = ((lo - gmin.astype(np.float64)) / D1).astype(np.float32)
+    got = o.codes_given_metadata(X, gmin, gscale, mu_lo, s32, 2, alpha)
+    is_hi = np.array([[False, False], [True, True], [True, False], [False, False]])
+    expect_I = np.where(is_hi, 127, 0)
+    assert np.array_equal(got["I"], expect_I)
+    assert np.all(got["S"] == 1)
+    assert np.array_equal(got["Q_anc"], np.where(is_hi, 7, 0))
+    assert np.array_equal(got["Q_res"], np.where(is_hi, -8, 7))
+    # the upper tokens sit near X_f = 2 (clipped), not at 1
+    assert np.all(np.abs(got["Xf"][is_hi] - 2.0) < 1e-4)      # 2 s / (s + eps), s >= 0.09
 
 
 def test_constant_channel():
