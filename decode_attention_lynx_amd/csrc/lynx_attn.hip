@@ -128,18 +128,20 @@ struct TileIn {
 };
 
 // Per-lane byte offsets of one wave's tile loads; they do not depend on the tile, whose
-// (wave-uniform) base addresses are added to them.
+// (wave-uniform) base addresses are added to them.  Code rows are 32 bytes per token in
+// each of the head's two 64-channel code blocks (block b at b * P * 32 from the head's
+// first row).
 struct TileOffsets {
-  uint32_t kcode;   // K code rows: 16g + 64n (+ 1024 mb)
-  uint32_t vcode;   // V code rows: 4n + 256g (+ row constants)
+  uint32_t kcode;   // K code rows: channels 32g .. +31 of token n, i.e. block g/2, bytes 16(g%2) .. +15
+  uint32_t vcode;   // V code rows: channels 8(n%16) .. +7 (block n/8, dword n%8) of row 4g
   uint32_t meta;    // float32 metadata of channels 2*lane, 2*lane + 1: 8*lane
 };
 
-__device__ __forceinline__ TileOffsets tile_offsets(int lane) {
+__device__ __forceinline__ TileOffsets tile_offsets(int lane, int P) {
   const int n = lane & 15, g = lane >> 4;
   TileOffsets o;
-  o.kcode = (uint32_t)(16 * g + n * (kHeadDim / 2));
-  o.vcode = (uint32_t)(4 * n + 4 * g * (kHeadDim / 2));
+  o.kcode = (uint32_t)((g >> 1) * P * kCodeRow + n * kCodeRow + 16 * (g & 1));
+  o.vcode = (uint32_t)((n >> 3) * P * kCodeRow + 4 * (n & 7) + 4 * g * kCodeRow);
   o.meta = (uint32_t)(8 * lane);
   return o;
 }
@@ -153,20 +155,20 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int
   const int tin = tok - page * a.P;
   const int kc = tin / a.C;
   const size_t seg = segment_of(a, b, page) * (size_t)a.anc_seg;
-  const size_t row0 = ((size_t)kvh * a.P + tin) * (kHeadDim / 2);
+  const size_t row0 = code_offset(a.P, kvh, 0, tin);   // block 0 of the head, token tin
   const uint8_t* kcb = a.kanc + seg + row0;
   const uint8_t* vcb = a.vanc + seg + row0;
   // every code byte is read once: streaming loads, which keep the caches for the metadata
   // (the page statistics are shared by all tiles of a page)
 #pragma unroll
-  for (int mb = 0; mb < TILE / 16; ++mb) t.kw[mb] = ld_stream(kcb + lo.kcode + 16 * mb * (kHeadDim / 2));
+  for (int mb = 0; mb < TILE / 16; ++mb) t.kw[mb] = ld_stream(kcb + lo.kcode + 16 * mb * kCodeRow);
 #pragma unroll
   for (int ks = 0; ks < TILE / 32; ++ks)
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int row = 32 * ks + (r < 4 ? r : 12 + r);     // + 4g (in the lane offset)
       t.vw[8 * ks + r] =
-          __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vcb + lo.vcode + row * (kHeadDim / 2)));
+          __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vcb + lo.vcode + row * kCodeRow));
     }
   const uint8_t* kmb = a.kanc + seg + a.codes + (size_t)kvh * kHeadDim * 4;
   const uint8_t* vmb = a.vanc + seg + a.codes + (size_t)kvh * kHeadDim * 4;
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   float4 (*kab)[kHeadDim / 2] = s_kab[wave];
   float4 (*vab)[kHeadDim / 2] = s_vab[wave];
 
-  const TileOffsets toff = tile_offsets(lane);
+  const TileOffsets toff = tile_offsets(lane, a.P);
 
   // one 64-token tile of this wave: scores, online softmax, values
   auto process = [&](const TileIn<TILE, CPT>& cur, int tile) {

@@ -11,8 +11,10 @@
 // of a 64-channel slab of one kv head of one page: thread t owns channels
 // 8*(t % 8) .. +7 of the slab and the 8 consecutive tokens 8*(t / 8) .. +7 of the
 // tile.  A token row of the slab is 128 B of BF16 (8 threads x 16 B loads) and 32 B
-// of nibbles per stream (8 threads x 4 B).  A decode workgroup owns one 128-token
-// tile of one kv head (see k_decode).
+// of nibbles per stream.  The slab is one 64-channel code block, so the codes of a
+// wave's 64 tokens are 2 KB of contiguous memory per stream; each wave stages them in
+// LDS and writes them as 1 KB per store instruction.  A decode workgroup owns one
+// 128-token tile of one kv head (see k_decode).
 // Chunk sizes are powers of two in [8, 256], so a thread's tokens always lie in
 // one chunk, a chunk is a power-of-two run of threads, and chunks never straddle
 // 256-token tiles.
@@ -52,6 +54,11 @@ __device__ __forceinline__ float2 encode_exact(float x, float gmin, double D1, f
   const int I = fabs(xfe) >= bnd[jb] ? jb : jb - 1;
   return make_float2((float)I, (xfe < 0.0) ? -1.0f : 1.0f);
 }
+
+// Code stores of the encoder: 16-byte streaming stores, 1 KB contiguous per wave store.  With
+// plain stores the code lines stay dirty in the caches after the encode and the next
+// kernel pays for writing them back (the anchor decode right after it was ~6% slower).
+__device__ __forceinline__ void st_codes(void* p, uint4 v) { st_stream(p, v); }
 
 // Pack 8 codes (one token, 8 consecutive channels) into one anchor word and one
 // residual word ([Review] Mechanism 1, Stage 4 and Eq. 9, with the +7 bias at
@@ -98,7 +105,7 @@ struct EncodeShared {
   double bnd[130];
   static constexpr bool kPacked = C <= 32;   // extremes as two BF16 halves of one word
   uint32_t pext[kTG][kSlab][kPacked ? 1 : 2];  // [0]: min (packed: min low, max high), [1]: max
-  double psum[kTG][kSlab];
+  double psum[kTG][kSlab];                // after Stage 2: the waves' code staging (see stage_words)
   uint32_t gpart[kThreads / kSlab][kSlab];  // page min / max of 8 partial rows, two BF16 per word
   float gmin[kSlab];                     // by column
   double D1[kSlab];
@@ -132,8 +139,8 @@ __device__ __forceinline__ void merge_extremes(const EncodeShared<C>& sh, int ro
 struct EncodeUnit {
   const uint16_t* X;      // this thread's first BF16 value (token 0, channel cbase + 8*dg)
   float* meta;            // the page's float32 metadata
-  uint8_t* anc_codes;     // this thread's anchor word of token 0
-  uint8_t* res_codes;     // this thread's residual word of token 0, or nullptr
+  uint8_t* anc_codes;     // the slab's anchor code block (token 0)
+  uint8_t* res_codes;     // the slab's residual code block, or nullptr
   int cbase;              // first channel of the slab
 };
 
@@ -148,7 +155,8 @@ __device__ __forceinline__ EncodeUnit encode_unit(const EncodeArgs& a, int unit,
   u.X = a.kv + (size_t)page * g.P * g.H + u.cbase + dg * 8;
   uint8_t* anc = a.anchor + (size_t)page * g.anc_seg;
   u.meta = reinterpret_cast<float*>(anc + g.codes);
-  const size_t code_off = (size_t)h * g.P * (kHeadDim / 2) + slab * (kSlab / 2) + dg * 4;
+  static_assert(kSlab == kCodeBlock, "an encode slab is one code block");
+  const size_t code_off = code_offset(g.P, h, slab * kSlab, 0);
   u.anc_codes = anc + code_off;
   u.res_codes = a.residual ? a.residual + (size_t)page * g.res_seg + code_off : nullptr;
   return u;
@@ -307,78 +315,108 @@ __device__ __forceinline__ bool in_band(uint32_t yb, uint32_t zband) {
   return static_cast<uint16_t>(yb) < static_cast<uint16_t>(2u * zband);
 }
 
+// Code staging: wave w's 64 tokens of the slab (2 KB of code rows per stream) in words
+// 1024w .. 1024w + 511 (anchor) and the next 512 (residual) of the dead psum rows.  Word
+// (token group tgl of the wave, token i of the group, channel group dg) sits at
+// 64*tgl + 8*((i + tgl) & 7) + dg: the row of 8 words is rotated by the token group, so
+// the 32 lanes of a half-wave that write one i hit 32 different banks.
+__device__ __forceinline__ int stage_word(int tgl, int i, int dg) { return 64 * tgl + 8 * ((i + tgl) & 7) + dg; }
+
 // Stages 3-4 ([Review] Mechanism 1, Stages 3-4, Eq. 7 and Eq. 9) for this thread's 8
 // tokens of the tile at t0.  Every element takes the float32 fast path; the rare
 // elements whose float32 Y lies within the band of a rounding boundary are then re-decided
 // in float64 and their two nibbles patched into the packed words (the fast path's
 // per-element values are dead by then, which leaves room for four workgroups per CU).
+// The packed words go to the wave's LDS staging rows; the wave then writes its code rows
+// as 16 bytes per lane, 1 KB contiguous per store instruction.
 template <int C>
-__device__ __forceinline__ void encode_tokens(const EncodeShared<C>& sh, const EncodeArgs& a, const EncodeUnit& u,
-                                              const uint4 (&v)[kTokPerThread], int t0, int tg, int dg) {
+__device__ __forceinline__ void encode_tokens(EncodeShared<C>& sh, const EncodeArgs& a, const EncodeUnit& u,
+                                              const uint4 (&v)[kTokPerThread], int t0, int tid, int tg, int dg) {
   constexpr int G = C / kTokPerThread;
   const int tok0 = t0 + tg * kTokPerThread;
-  if (tok0 >= a.g.P) return;
-  const int kc = tg / G;                             // chunk within tile
-  const float alpha = a.alpha, ylog2k = a.ylog2k;
-  const uint32_t zband = a.zband;
-  const float ybias = 128.5f + (float)zband * (1.0f / 65536.0f);
-  // this thread's columns j*8 + dg of the chunk tables: one base each, j an offset
-  const float4* cst_t = &sh.cst[kc][dg];
-  const float* sig_t = &sh.sig[kc][dg];
-  const float* gmin_t = &sh.gmin[dg];
-  const double* D1_t = &sh.D1[dg];
-  float ch[8], kk[8], ckn[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float4 cs = cst_t[j * 8];
-    ch[j] = cs.x;
-    kk[j] = cs.y;
-    ckn[j] = cs.z;
-  }
-  uint32_t* anc_w = reinterpret_cast<uint32_t*>(u.anc_codes + (size_t)tok0 * (kHeadDim / 2));
-  uint32_t* res_w = u.res_codes ? reinterpret_cast<uint32_t*>(u.res_codes + (size_t)tok0 * (kHeadDim / 2)) : nullptr;
-#pragma unroll
-  for (int i = 0; i < kTokPerThread; ++i) {
-    const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-    uint32_t mb[8];
-    float xf[8];
-    bool near[8];                                    // element j lies in the band (a lane mask each)
+  const int wave = tid >> 6, lane = tid & 63, tgl = tg & 7;
+  uint32_t* st_a = reinterpret_cast<uint32_t*>(&sh.psum[0][0]) + wave * 1024;
+  uint32_t* st_r = st_a + 512;
+  static_assert(sizeof(sh.psum) >= (kThreads / 64) * 1024 * sizeof(uint32_t), "staging fits in psum");
+  if (tok0 < a.g.P) {
+    const int kc = tg / G;                           // chunk within tile
+    const float alpha = a.alpha, ylog2k = a.ylog2k;
+    const uint32_t zband = a.zband;
+    const float ybias = 128.5f + (float)zband * (1.0f / 65536.0f);
+    // this thread's columns j*8 + dg of the chunk tables: one base each, j an offset
+    const float4* cst_t = &sh.cst[kc][dg];
+    const float* sig_t = &sh.sig[kc][dg];
+    const float* gmin_t = &sh.gmin[dg];
+    const double* D1_t = &sh.D1[dg];
+    float ch[8], kk[8], ckn[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
-      const float f = fmaf(x - ch[j], kk[j], ckn[j]);
-      mb[j] = y_bits(f, alpha, ylog2k, ybias);
-      near[j] = in_band(mb[j], zband);
-      xf[j] = f;
+      const float4 cs = cst_t[j * 8];
+      ch[j] = cs.x;
+      kk[j] = cs.y;
+      ckn[j] = cs.z;
     }
-    uint32_t aw, rw;
-    pack8(mb, xf, &aw, &rw);
-    if (near[0] | near[1] | near[2] | near[3] | near[4] | near[5] | near[6] | near[7]) {
-      // the per-lane bit mask is formed here, on this rare path only: `one` comes out of an
-      // opaque step, so the compiler cannot move the mask's eight selects onto the fast path
-      uint32_t one = 1u, bits = 0;
-      asm volatile("" : "+v"(one));
 #pragma unroll
-      for (int j = 0; j < 8; ++j) bits |= (near[j] ? one : 0u) << j;
-      do {                                           // one element at a time, lowest first
-        const int j = __builtin_ctz(bits);
-        bits &= bits - 1;
-        const uint32_t w = (j >> 1) == 0 ? q[0] : (j >> 1) == 1 ? q[1] : (j >> 1) == 2 ? q[2] : q[3];
-        const float x = (j & 1) ? bf16_hi_p(w) : bf16_lo_p(w);
-        const float4 cs = cst_t[j * 8];
-        // the fast path's Y again (same operations), to find the boundary it lies near:
-        // the moved fraction is below 2z, so byte 2 is the code just above that boundary
-        const uint32_t yb = y_bits(fmaf(x - cs.x, cs.y, cs.z), alpha, ylog2k, ybias);
-        const int jb = (int)((yb >> 16) & 0xFFu);     // in [1, 128]: Y + 1/2 lies just around jb
-        const float2 e = encode_exact(x, gmin_t[j * 8], D1_t[j * 8], cs.w, (double)sig_t[j * 8] + kEps, jb, sh.bnd);
-        const uint32_t byte = (uint32_t)e.x ^ (e.y < 0.0f ? 0xF7u : 0x07u);   // anchor nibble high, residual low
-        const uint32_t m = 0xFu << (4 * j);
-        aw = (aw & ~m) | ((byte >> 4) << (4 * j));
-        rw = (rw & ~m) | ((byte & 0xFu) << (4 * j));
-      } while (bits);
+    for (int i = 0; i < kTokPerThread; ++i) {
+      const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      uint32_t mb[8];
+      float xf[8];
+      bool near[8];                                  // element j lies in the band (a lane mask each)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
+        const float f = fmaf(x - ch[j], kk[j], ckn[j]);
+        mb[j] = y_bits(f, alpha, ylog2k, ybias);
+        near[j] = in_band(mb[j], zband);
+        xf[j] = f;
+      }
+      uint32_t aw, rw;
+      pack8(mb, xf, &aw, &rw);
+      if (near[0] | near[1] | near[2] | near[3] | near[4] | near[5] | near[6] | near[7]) {
+        // the per-lane bit mask is formed here, on this rare path only: `one` comes out of an
+        // opaque step, so the compiler cannot move the mask's eight selects onto the fast path
+        uint32_t one = 1u, bits = 0;
+        asm volatile("" : "+v"(one));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bits |= (near[j] ? one : 0u) << j;
+        do {                                         // one element at a time, lowest first
+          const int j = __builtin_ctz(bits);
+          bits &= bits - 1;
+          const uint32_t w = (j >> 1) == 0 ? q[0] : (j >> 1) == 1 ? q[1] : (j >> 1) == 2 ? q[2] : q[3];
+          const float x = (j & 1) ? bf16_hi_p(w) : bf16_lo_p(w);
+          const float4 cs = cst_t[j * 8];
+          // the fast path's Y again (same operations), to find the boundary it lies near:
+          // the moved fraction is below 2z, so byte 2 is the code just above that boundary
+          const uint32_t yb = y_bits(fmaf(x - cs.x, cs.y, cs.z), alpha, ylog2k, ybias);
+          const int jb = (int)((yb >> 16) & 0xFFu);   // in [1, 128]: Y + 1/2 lies just around jb
+          const float2 e = encode_exact(x, gmin_t[j * 8], D1_t[j * 8], cs.w, (double)sig_t[j * 8] + kEps, jb, sh.bnd);
+          const uint32_t byte = (uint32_t)e.x ^ (e.y < 0.0f ? 0xF7u : 0x07u);   // anchor nibble high, residual low
+          const uint32_t m = 0xFu << (4 * j);
+          aw = (aw & ~m) | ((byte >> 4) << (4 * j));
+          rw = (rw & ~m) | ((byte & 0xFu) << (4 * j));
+        } while (bits);
+      }
+      st_a[stage_word(tgl, i, dg)] = aw;
+      st_r[stage_word(tgl, i, dg)] = rw;
     }
-    anc_w[i * (kHeadDim / 8)] = aw;                  // one 64-byte code row per token
-    if (res_w) res_w[i * (kHeadDim / 8)] = rw;
+  }
+  // the wave reads back what its own lanes staged: LDS operations of one wave complete in
+  // order, so a wavefront-scope fence (no workgroup barrier) orders the reads after the writes
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // lane l writes bytes 16l .. 16l+15 of each 1 KB half of the wave's 2 KB code block:
+  // token 32*half + l/2 of the wave, channels 32*(l&1) .. +31 of the slab
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int tl = 32 * half + (lane >> 1);          // token of the wave
+    const int tok = t0 + wave * 64 + tl;
+    if (tok < a.g.P) {
+      const int w = stage_word(tl >> 3, tl & 7, 4 * (lane & 1));
+      const size_t off = (size_t)tok * kCodeRow + 16 * (lane & 1);
+      st_codes(u.anc_codes + off, *reinterpret_cast<const uint4*>(st_a + w));
+      if (u.res_codes) st_codes(u.res_codes + off, *reinterpret_cast<const uint4*>(st_r + w));
+    }
   }
 }
 
@@ -482,7 +520,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C >= 3
   }
   chunk_stats(sh, u.meta, u.cbase, t0, tid, g, PAGE_STORED);
   __syncthreads();
-  encode_tokens(sh, a, u, v, t0, tg, dg);
+  encode_tokens(sh, a, u, v, t0, tid, tg, dg);
 }
 
 template __global__ void k_encode<8, false>(EncodeArgs);
@@ -546,15 +584,15 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     if (tok0 >= g.P) return;
     const uint8_t* anc = a.anchor + (size_t)page * g.anc_seg;
     const float* meta = reinterpret_cast<const float*>(anc + g.codes);
-    const size_t code_off = (size_t)h * g.P * (kHeadDim / 2) + dg * 4;
+    const size_t code_off = code_offset(g.P, h, dg * 8, 0);    // code block dg / 8, word dg % 8
     const uint8_t* anc_codes = anc + code_off;
     const uint8_t* res_codes = FULL ? a.residual + (size_t)page * g.res_seg + code_off : nullptr;
 
     uint32_t wa[kTokPerThread], wr[kTokPerThread];
 #pragma unroll
     for (int i = 0; i < kTokPerThread; ++i) {
-      wa[i] = *reinterpret_cast<const uint32_t*>(anc_codes + (size_t)(tok0 + i) * (kHeadDim / 2));
-      if (FULL) wr[i] = *reinterpret_cast<const uint32_t*>(res_codes + (size_t)(tok0 + i) * (kHeadDim / 2));
+      wa[i] = *reinterpret_cast<const uint32_t*>(anc_codes + (size_t)(tok0 + i) * kCodeRow);
+      if (FULL) wr[i] = *reinterpret_cast<const uint32_t*>(res_codes + (size_t)(tok0 + i) * kCodeRow);
     }
     float A[8], B[8];
     {

@@ -25,7 +25,14 @@ constexpr double kEps = 1e-6;        // epsilon of both normalisation stages (no
 constexpr int kCodeMax = 127;        // 2^7 - 1 ([Review] Mechanism 1, Stage 3, Eq. 7)
 
 // Geometry of one encode/decode call.  Channel c = h*128 + d; a page row (one token)
-// holds H = kv_heads*128 BF16 values; codes are [kv_head][token][head_dim] nibbles.
+// holds H = kv_heads*128 BF16 values.  Codes are nibbles ordered
+// [kv_head][channel block][token][channel in block], blocks of kCodeBlock channels: the
+// 32-byte code row of (head, block, token) lies at code_offset(P, h, d, t).
+constexpr int kCodeBlock = 64;                      // channels per code block
+constexpr int kCodeRow = kCodeBlock / 2;            // bytes of one token's code row in a block
+__host__ __device__ constexpr size_t code_offset(int P, int h, int d, int t) {
+  return ((size_t)(h * (kHeadDim / kCodeBlock) + d / kCodeBlock) * P + t) * kCodeRow + (d % kCodeBlock) / 2;
+}
 struct Geometry {
   int n_pages;
   int P;            // tokens per page

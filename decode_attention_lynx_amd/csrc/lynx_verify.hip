@@ -117,7 +117,7 @@ struct CodeIn {
 
 struct TileAddr {
   size_t seg;     // segment index of the tile's page
-  size_t row0;    // byte offset of the tile's first code row of this kv head
+  size_t row0;    // byte offset of the tile's first code row in block 0 of this kv head
   int kc;         // chunk of the tile within its page
 };
 
@@ -132,7 +132,7 @@ __device__ __forceinline__ TileAddr tile_addr(const VerifyArgs& a, int b, int kv
     const int sg = a.block_table[(size_t)b * a.max_pages + page];
     t.seg = (size_t)min(max(sg, 0), a.n_pool - 1);
   }
-  t.row0 = ((size_t)kvh * a.P + tin) * (kHeadDim / 2);
+  t.row0 = code_offset(a.P, kvh, 0, tin);
   t.kc = tin / a.C;
   return t;
 }
@@ -140,13 +140,17 @@ __device__ __forceinline__ TileAddr tile_addr(const VerifyArgs& a, int b, int kv
 __device__ __forceinline__ void load_codes(const VerifyArgs& a, int b, int kvh, int tile, int tid, CodeIn& in) {
   const TileAddr ta = tile_addr(a, b, kvh, tile);
   {
-    const size_t off = ta.row0 + (size_t)(tid >> 3) * (kHeadDim / 2) + 8 * (tid & 7);
+    // channels 16*(tid%8) .. +15: code block (tid%8)/4, bytes 8*(tid%4) .. +7 of its row
+    const size_t off = ta.row0 + (size_t)((tid & 7) >> 2) * a.P * kCodeRow + (size_t)(tid >> 3) * kCodeRow +
+                       8 * (tid & 3);
     in.ka = *reinterpret_cast<const uint2*>(a.kanc + ta.seg * a.anc_seg + off);
     in.kr = *reinterpret_cast<const uint2*>(a.kres + ta.seg * a.codes + off);
   }
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const size_t off = ta.row0 + (size_t)(2 * (tid & 31) + r) * (kHeadDim / 2) + 4 * (tid >> 5);
+    // channels 8*(tid/32) .. +7: code block tid/256, dword (tid/32)%8 of its row
+    const size_t off = ta.row0 + (size_t)(tid >> 8) * a.P * kCodeRow + (size_t)(2 * (tid & 31) + r) * kCodeRow +
+                       4 * ((tid >> 5) & 7);
     in.va[r] = *reinterpret_cast<const uint32_t*>(a.vanc + ta.seg * a.anc_seg + off);
     in.vr[r] = *reinterpret_cast<const uint32_t*>(a.vres + ta.seg * a.codes + off);
   }

@@ -40,8 +40,11 @@
  *   residual segment = [residual nibbles : P*H/2 bytes]
  *   Anchor codes and their metadata are contiguous so one copy moves the whole
  *   high-priority stream ([Review] Mechanism 2, prefill-side workflow).  Codes
- *   are ordered [kv_head][token][head_dim] inside a page; two 4-bit codes share
- *   a byte, the even element in the low nibble ([Review] Implementation Notes).
+ *   are ordered [kv_head][channel block][token][channel in block] inside a page,
+ *   the 128 channels of a head split into two blocks of 64 (so a code row is 32
+ *   bytes: element (t, h, d) is nibble ((h*2 + d/64)*P + t)*64 + d%64 of the
+ *   stream); two 4-bit codes share a byte, the even element in the low nibble
+ *   ([Review] Implementation Notes).
  *   A 4-bit code q in [-8, 7] is stored as the nibble q & 0xF.
  *   Metadata count = H*(2 + 2P/C) float32 scalars ([Review] Deep Dive).
  *

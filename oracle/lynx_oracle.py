@@ -37,7 +37,9 @@ Readings (where the pages are silent, ambiguous or inconsistent):
             exactly, and anchor-only decode is full decode with V_res = 0.
   R-nibble  a 4-bit code q is stored as the nibble q & 0xF (two's complement);
             two codes share a byte, the even element in the low nibble.
-  R-layout  within a page, codes are ordered [kv_head][token][head_dim]; a
+  R-layout  within a page, codes are ordered [kv_head][channel block][token][channel
+            in block], the head's channels split into blocks of 64 (a head of at
+            most 64 channels is one block, i.e. [kv_head][token][head_dim]); a
             page's anchor segment is the anchor nibbles followed by
             gamma_min f32[H], gamma_scale f32[H], mu f32[P/C][H],
             sigma f32[P/C][H] (H = kv_heads*head_dim, channel = h*D + d);
@@ -261,10 +263,23 @@ def segment_bytes(P: int, Hkv: int, D: int, C: int):
     return codes + 4 * metadata_scalars(P, H, C), codes
 
 
+CODE_BLOCK = 64       # channels of one code block (R-layout)
+
+
+def _code_blocks(D: int) -> int:
+    """Channel blocks per kv head: 1 for D <= 64, else D / 64 (R-layout)."""
+    if D <= CODE_BLOCK:
+        return 1
+    assert D % CODE_BLOCK == 0, "head_dim above 64 must be a multiple of 64"
+    return D // CODE_BLOCK
+
+
 def pack_nibbles(Q: np.ndarray, Hkv: int, D: int) -> np.ndarray:
-    """Q: [P, H] codes in [-8, 7] -> P*H/2 bytes in [kv_head][token][head_dim] order, even element low."""
+    """Q: [P, H] codes in [-8, 7] -> P*H/2 bytes in [kv_head][channel block][token][channel] order
+    (R-layout), even element in the low nibble (R-nibble)."""
     P, H = Q.shape
-    order = np.asarray(Q, dtype=np.int32).reshape(P, Hkv, D).transpose(1, 0, 2).reshape(-1)
+    nb = _code_blocks(D)
+    order = np.asarray(Q, dtype=np.int32).reshape(P, Hkv, nb, D // nb).transpose(1, 2, 0, 3).reshape(-1)
     nib = (order & 0xF).astype(np.uint8)
     return (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
 
@@ -272,11 +287,12 @@ def pack_nibbles(Q: np.ndarray, Hkv: int, D: int) -> np.ndarray:
 def unpack_nibbles(b: np.ndarray, P: int, Hkv: int, D: int) -> np.ndarray:
     """Inverse of pack_nibbles: bytes -> [P, H] signed codes in [-8, 7]."""
     b = np.asarray(b, dtype=np.uint8)
+    nb = _code_blocks(D)
     nib = np.empty(b.size * 2, dtype=np.int32)
     nib[0::2] = b & 0xF
     nib[1::2] = b >> 4
     q = np.where(nib >= 8, nib - 16, nib)
-    return q.reshape(Hkv, P, D).transpose(1, 0, 2).reshape(P, Hkv * D)
+    return q.reshape(Hkv, nb, P, D // nb).transpose(2, 0, 1, 3).reshape(P, Hkv * D)
 
 
 def build_anchor_segment(enc: dict, Hkv: int, D: int) -> np.ndarray:

@@ -183,16 +183,21 @@ def test_metadata_count_matches_page():
     assert (a, r) == (256 * 1024 // 2 + 4 * 1024 * (2 + 8), 256 * 1024 // 2) == (172032, 131072)
 
 
-def test_pack_layout_brute_force():
+@pytest.mark.parametrize("D", [4, 128, 192])
+def test_pack_layout_brute_force(D):
+    """Nibble e of the packed stream holds element (token t, kv head h, channel d) with
+    e = ((h * nb + d // W) * P + t) * W + d % W, W = min(D, 64) channels per block, nb = D / W."""
     rng = np.random.default_rng(1)
-    P, Hkv, D = 6, 3, 4
+    P, Hkv = 6, 3
+    W = min(D, 64)
+    nb = D // W
     Q = rng.integers(-8, 8, size=(P, Hkv * D))
     b = o.pack_nibbles(Q, Hkv, D)
     assert b.size == P * Hkv * D // 2
     for t in range(P):
         for h in range(Hkv):
             for d in range(D):
-                e = (h * P + t) * D + d                 # [kv_head][token][head_dim]
+                e = ((h * nb + d // W) * P + t) * W + d % W
                 nib = (int(b[e // 2]) >> (4 * (e % 2))) & 0xF
                 assert nib == (int(Q[t, h * D + d]) & 0xF)
     assert np.array_equal(o.unpack_nibbles(b, P, Hkv, D), Q)
