@@ -104,8 +104,14 @@ struct EncodeShared {
   static constexpr int kChunksPerTile = kTileTokens / C;
   double bnd[130];
   static constexpr bool kPacked = C <= 32;   // extremes as two BF16 halves of one word
-  uint32_t pext[kTG][kSlab][kPacked ? 1 : 2];  // [0]: min (packed: min low, max high), [1]: max
-  double psum[kTG][kSlab];                // after Stage 2: the waves' code staging (see stage_words)
+  static constexpr int kStageWords = 6144;     // code staging: 4 waves x 2 streams x 768 words
+  union {
+    struct {
+      uint32_t pext[kTG][kSlab][kPacked ? 1 : 2];  // [0]: min (packed: min low, max high), [1]: max
+      double psum[kTG][kSlab];
+    };
+    uint32_t stage[kStageWords];           // after Stage 2: the waves' code rows (see stage_word)
+  };
   uint32_t gpart[kThreads / kSlab][kSlab];  // page min / max of 8 partial rows, two BF16 per word
   float gmin[kSlab];                     // by column
   double D1[kSlab];
@@ -185,11 +191,22 @@ __device__ __forceinline__ void store_partials(EncodeShared<C>& sh, const uint4 
                                                int tg, int dg) {
   double sm[8];
   float cmn[8], cmx[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) { sm[j] = 0.0; cmn[j] = INFINITY; cmx[j] = -INFINITY; }
   if (act) {
+    // token 0 starts the sums and extremes, tokens 1..7 accumulate: no additions of 0 and
+    // no infinities to load on the common path
+    {
+      const uint32_t q[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
 #pragma unroll
-    for (int i = 0; i < kTokPerThread; ++i) {
+      for (int k = 0; k < 4; ++k) {
+        const float lo = bf16_lo_p(q[k]), hi = bf16_hi_p(q[k]);
+        sm[2 * k] = (double)lo;
+        sm[2 * k + 1] = (double)hi;
+        cmn[2 * k] = cmx[2 * k] = lo;
+        cmn[2 * k + 1] = cmx[2 * k + 1] = hi;
+      }
+    }
+#pragma unroll
+    for (int i = 1; i < kTokPerThread; ++i) {
       const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -202,6 +219,9 @@ __device__ __forceinline__ void store_partials(EncodeShared<C>& sh, const uint4 
         cmx[2 * k + 1] = fmaxf(cmx[2 * k + 1], hi);
       }
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { sm[j] = 0.0; cmn[j] = INFINITY; cmx[j] = -INFINITY; }
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -315,12 +335,30 @@ __device__ __forceinline__ bool in_band(uint32_t yb, uint32_t zband) {
   return static_cast<uint16_t>(yb) < static_cast<uint16_t>(2u * zband);
 }
 
+// The smallest of the low 16-bit halves of three words (v_min3_u16 reads the low halves of
+// its 32-bit sources, so no operand has to be unpacked first).
+__device__ __forceinline__ uint32_t min3_lo16(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_min3_u16 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Any of a token's 8 elements in the band: the smallest of the 8 moved fractions against
+// 2z, four 16-bit minima and one compare per token instead of one compare per element.
+__device__ __forceinline__ bool token_in_band(const uint32_t (&mb)[8], uint32_t zband) {
+  const uint32_t a = min3_lo16(mb[0], mb[1], mb[2]);
+  const uint32_t b = min3_lo16(mb[3], mb[4], mb[5]);
+  const uint32_t c = min3_lo16(mb[6], mb[7], a);
+  return in_band(min(b & 0xFFFFu, c & 0xFFFFu), zband);
+}
+
 // Code staging: wave w's 64 tokens of the slab (2 KB of code rows per stream) in words
-// 1024w .. 1024w + 511 (anchor) and the next 512 (residual) of the dead psum rows.  Word
+// 1536w .. 1536w + 767 (anchor) and the next 768 (residual) of the dead partial rows.  Word
 // (token group tgl of the wave, token i of the group, channel group dg) sits at
-// 64*tgl + 8*((i + tgl) & 7) + dg: the row of 8 words is rotated by the token group, so
-// the 32 lanes of a half-wave that write one i hit 32 different banks.
-__device__ __forceinline__ int stage_word(int tgl, int i, int dg) { return 64 * tgl + 8 * ((i + tgl) & 7) + dg; }
+// 96*tgl + 8*(tgl % 4) + 8*i + dg: the 8 words of token i start 8*(tgl % 4) words into a
+// 96-word row, so the 32 lanes of a half-wave that write one i hit 32 different banks, and
+// the offset of token i is the same constant for every lane (an immediate of the store).
+__device__ __forceinline__ int stage_word(int tgl, int i, int dg) { return 96 * tgl + 8 * (tgl & 3) + 8 * i + dg; }
 
 // Stages 3-4 ([Review] Mechanism 1, Stages 3-4, Eq. 7 and Eq. 9) for this thread's 8
 // tokens of the tile at t0.  Every element takes the float32 fast path; the rare
@@ -335,9 +373,9 @@ __device__ __forceinline__ void encode_tokens(EncodeShared<C>& sh, const EncodeA
   constexpr int G = C / kTokPerThread;
   const int tok0 = t0 + tg * kTokPerThread;
   const int wave = tid >> 6, lane = tid & 63, tgl = tg & 7;
-  uint32_t* st_a = reinterpret_cast<uint32_t*>(&sh.psum[0][0]) + wave * 1024;
-  uint32_t* st_r = st_a + 512;
-  static_assert(sizeof(sh.psum) >= (kThreads / 64) * 1024 * sizeof(uint32_t), "staging fits in psum");
+  uint32_t* st_a = sh.stage + wave * 1536;
+  uint32_t* st_r = st_a + 768;
+  static_assert((kThreads / 64) * 1536 <= EncodeShared<C>::kStageWords, "staging rows fit");
   if (tok0 < a.g.P) {
     const int kc = tg / G;                           // chunk within tile
     const float alpha = a.alpha, ylog2k = a.ylog2k;
@@ -361,24 +399,22 @@ __device__ __forceinline__ void encode_tokens(EncodeShared<C>& sh, const EncodeA
       const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
       uint32_t mb[8];
       float xf[8];
-      bool near[8];                                  // element j lies in the band (a lane mask each)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
         const float f = fmaf(x - ch[j], kk[j], ckn[j]);
         mb[j] = y_bits(f, alpha, ylog2k, ybias);
-        near[j] = in_band(mb[j], zband);
         xf[j] = f;
       }
       uint32_t aw, rw;
       pack8(mb, xf, &aw, &rw);
-      if (near[0] | near[1] | near[2] | near[3] | near[4] | near[5] | near[6] | near[7]) {
-        // the per-lane bit mask is formed here, on this rare path only: `one` comes out of an
-        // opaque step, so the compiler cannot move the mask's eight selects onto the fast path
+      if (token_in_band(mb, zband)) {
+        // which elements: formed on this rare path only; `one` comes out of an opaque step,
+        // so the compiler cannot move the mask's eight selects onto the fast path
         uint32_t one = 1u, bits = 0;
         asm volatile("" : "+v"(one));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bits |= (near[j] ? one : 0u) << j;
+        for (int j = 0; j < 8; ++j) bits |= (in_band(mb[j], zband) ? one : 0u) << j;
         do {                                         // one element at a time, lowest first
           const int j = __builtin_ctz(bits);
           bits &= bits - 1;
@@ -563,6 +599,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
   // of a half-wave meet in a bank.  The anchor table has 16 entries, which sit in 16
   // banks and are read conflict-free as they are.
   __shared__ float s_lut[FULL ? 256 * 32 : 16];
+  __shared__ uint32_t s_rows[FULL ? 1 : kThreads][9];   // anchor decode: code rows of the lanes
   if (FULL) {
     const float e = a.lut[tid];                                       // entry tid, all 32 copies
     float4* dst = reinterpret_cast<float4*>(s_lut + tid * 32);
@@ -589,10 +626,30 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecodeArgs a) {
     const uint8_t* res_codes = FULL ? a.residual + (size_t)page * g.res_seg + code_off : nullptr;
 
     uint32_t wa[kTokPerThread], wr[kTokPerThread];
+    if (FULL) {
 #pragma unroll
-    for (int i = 0; i < kTokPerThread; ++i) {
-      wa[i] = *reinterpret_cast<const uint32_t*>(anc_codes + (size_t)(tok0 + i) * kCodeRow);
-      if (FULL) wr[i] = *reinterpret_cast<const uint32_t*>(res_codes + (size_t)(tok0 + i) * kCodeRow);
+      for (int i = 0; i < kTokPerThread; ++i) {
+        wa[i] = *reinterpret_cast<const uint32_t*>(anc_codes + (size_t)(tok0 + i) * kCodeRow);
+        wr[i] = *reinterpret_cast<const uint32_t*>(res_codes + (size_t)(tok0 + i) * kCodeRow);
+      }
+    } else {
+      // The 8 lanes of this (token group, code block) need word dg % 8 of the group's 8 code
+      // rows: lane k loads row k whole (two 16-byte pieces, so a wave load covers 32 B runs
+      // instead of 4 B words) and the words are exchanged through LDS (rows padded to 9 words).
+      // The full decode keeps word loads: its 32 KB table leaves no LDS for this.
+      const int k = dg & 7;
+      const uint8_t* row = anc_codes - 4 * k + (size_t)(tok0 + k) * kCodeRow;
+      const uint4 r0 = *reinterpret_cast<const uint4*>(row), r1 = *reinterpret_cast<const uint4*>(row + 16);
+      uint32_t* mine = s_rows[tid];
+      mine[0] = r0.x; mine[1] = r0.y; mine[2] = r0.z; mine[3] = r0.w;
+      mine[4] = r1.x; mine[5] = r1.y; mine[6] = r1.z; mine[7] = r1.w;
+      // a wave reads only rows its own lanes wrote: LDS operations of one wave complete in
+      // order, so a wavefront-scope fence (no workgroup barrier) orders the reads after the writes
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int i = 0; i < kTokPerThread; ++i) wa[i] = s_rows[tid - k + i][k];
     }
     float A[8], B[8];
     {

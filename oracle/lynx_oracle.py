@@ -44,8 +44,8 @@ Readings (where the pages are silent, ambiguous or inconsistent):
             gamma_min f32[H], gamma_scale f32[H], mu f32[P/C][H],
             sigma f32[P/C][H] (H = kv_heads*head_dim, channel = h*D + d);
             the residual segment is the residual nibbles alone.
-  R-zero    the sign of a zero is not data: a zero gamma_min or gamma_scale is
-            stored as +0 whatever the signs of the zeros in the channel.
+  R-zero    the sign of a zero is not data: a zero gamma_min, gamma_scale or mu is
+            stored as +0 whatever the signs of the zeros it comes from.
   R-attn    decode attention is Eq. 1 over the anchor-only reconstruction;
             query head hq uses kv head hq // (Hq/Hkv) (contiguous groups).
 """
@@ -121,9 +121,10 @@ def chunk_view(A: np.ndarray, C: int) -> np.ndarray:
 
 
 def chunk_mean(Xn: np.ndarray, C: int):
-    """mu per (chunk, channel): the float64 mean, and its float32 stored value."""
+    """mu per (chunk, channel): the float64 mean, and its float32 stored value (a zero mean of
+    negative zeros stored as +0, R-zero)."""
     mu64 = chunk_view(Xn, C).mean(axis=1)
-    return mu64, mu64.astype(np.float32)
+    return mu64, (mu64 + 0.0).astype(np.float32)
 
 
 def chunk_sigma(Xn: np.ndarray, mu32: np.ndarray, C: int) -> np.ndarray:

@@ -110,6 +110,8 @@ def test_degenerate_pages(gpu, P):
     X[:, 0, 6] = np.where(np.arange(2 * P) % 2 == 0, 1e-38, -1e-38)   # near the subnormal range
     X[P:, 0, 7:] = 2.0                             # second page: constant except channels 0..6
     X[:, 0, 8] = rng.choice([-1.0, 1.0], size=2 * P) * 2.0 ** rng.integers(-20, 20, size=2 * P)
+    X[:, 0, 9] = np.abs(X[:, 0, 9])                # minimum zero ...
+    X[:32, 0, 9] = -0.0                            # ... and a chunk of negative zeros: mu = 0 stored as +0
     bits = o.f64_to_bf16_bits(X.astype(np.float64))
     run_codec(bits, P, C, 255.0, label=f"degenerate P{P}", bf16_share=None)
 

@@ -513,7 +513,15 @@ def test_signed_zero_metadata_is_plus_zero():
     X[:, 1] = -0.0
     enc = o.encode_page(X, 16, 255.0)
     assert np.all(enc["gmin"].view(np.uint32) == 0) and np.all(enc["gscale"].view(np.uint32) == 0)
+    assert np.all(enc["mu"].view(np.uint32) == 0) and np.all(enc["sigma"].view(np.uint32) == 0)
     assert np.all(enc["I"] == 0) and np.all(enc["S"] == 1)
+    # a live channel whose minimum is zero with one chunk of negative zeros: that chunk's
+    # X_n are all -0 and its mean is a zero, stored as +0
+    Y = np.abs(np.linspace(-3.0, 5.0, 32))[:, None]
+    Y[:16, 0] = -0.0
+    enc = o.encode_page(o.bf16_bits_to_f64(o.f64_to_bf16_bits(Y)), 16, 255.0)
+    assert enc["gmin"].view(np.uint32)[0] == 0 and enc["gscale"][0] > 0
+    assert enc["mu64"][0, 0] == 0 and enc["mu"].view(np.uint32)[0, 0] == 0
 
 
 def test_attention_anchor_paged_matches_contiguous():
