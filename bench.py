@@ -1,24 +1,33 @@
-"""Benchmark of the Lynx hot path on one MI355X: encode + anchor-only decode + full
-decode of a Llama-3-8B-shaped request, and the fused anchor-only decode attention.
+"""Benchmark of the Lynx hot path on one MI355X: encode + anchor-only decode + full decode
+of a Qwen3-235B-shaped long-context request streamed layer by layer, and the fused
+anchor-only decode attention.
 
 One step =
-  encode        32 layers x {K, V} x 16384 tokens x 8 kv heads x 128 (BF16, 2.15 GB),
-                P = 256, C = 64, alpha = 255, anchor + residual streams
-  decode_anchor the same request back to BF16 from the anchor segments
-  decode_full   the same request back to BF16 from anchor + residual
-  attn_anchor   16 sequences x 64 query heads / 8 kv heads x 32768-token context
-                over anchor segments (P = 256, C = 64, alpha = 255)
+  encode        94 layers x {K, V} x 131072 tokens x 4 kv heads x 128 (BF16, 25.2 GB resident
+                in HBM), P = 256, C = 64, alpha = 255, anchor + residual streams.  Streamed layer
+                by layer: one call per layer (its K and V, 1024 pages, 268 MB of BF16), the calls
+                alternating over two HIP streams, so that one call's last workgroups overlap the
+                next call's first ones (the library header advises this for many small calls)
+  decode_anchor the same request back to BF16 from the anchor segments, the same per-layer calls
+                (each layer into its own part of a request-sized output buffer)
+  decode_full   the same from anchor + residual
+  attn_anchor   16 sequences x 64 query heads / 8 kv heads x 32768-token context over anchor
+                segments (P = 256, C = 64, alpha = 255)
 Timed after the step, on its own (not part of `value`):
-  attn_verify   the verification pass over full codes: the same 16 sequences with
-                64 draft tokens each, anchor + residual segments
-  encode_to_host the request encoded in groups of 256 pages, each group's anchor and
-                residual segments copied to pinned host memory while the next group is
-                encoded (two streams), against a plain device-to-host copy of the same bytes
-Inputs are synthetic (Laplacian + per-channel offset + x100 outlier channels,
-seeded) and resident in HBM before the timed region.
+  attn_verify   the verification pass over full codes: the same 16 sequences with 64 draft
+                tokens each, anchor + residual segments
+  attn_anchor_c32 the attention of the step at the pages' chunk of 32 tokens
+  encode_to_host the first 8 layers of the request encoded in groups of 256 pages, each group's
+                anchor and residual segments copied to pinned host memory while the next group
+                is encoded (two streams), against a plain device-to-host copy of the same bytes
+Inputs are synthetic (Laplacian + per-channel offset + x100 outlier channels, seeded per
+layer) and resident in HBM before the timed region.
 
-Prints one JSON line (rank 0, N = 1).  value = BF16-equivalent KV bytes processed
-per second over the whole step (2 B x elements x 4 ops) in GB/s.
+Prints one JSON line (rank 0, N = 1).  value = BF16-equivalent KV bytes processed per second
+over the whole step (2 B x elements of the four ops) in GB/s.  Every launch of the step is
+bracketed by HIP events on its own stream: each op reports its time (first launch start to
+last launch end, on the timing stream) and the mean duration of its launches; the roofline
+object takes the dominant kernel's algorithmic bytes per launch over that mean duration.
 """
 from __future__ import annotations
 
@@ -34,15 +43,19 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-LAYERS, TOKENS, KVH, D = 32, 16384, 8, 128
+LAYERS, TOKENS, KVH, D = 94, 131072, 4, 128          # Qwen3-235B long context, per layer K and V
+SEED = 3
 P, C, ALPHA = 256, 64, 255.0
+LAYERS_PER_CALL = 1                                  # one call per layer (its K and V)
 AB, AHQ, AHKV, AT = 16, 64, 8, 32768
 AM = 64                      # draft tokens per sequence in the verification pass
 PIPE_GROUP = 256             # pages per group of the pipelined encode to host memory
+PIPE_LAYERS = 8              # layers of the request the pipelined encode to host memory covers
 MFMA_PEAK_TFLOPS = 2500.0    # dense float16 / bfloat16 MFMA
 KERNEL_SOURCES = ["decode_attention_lynx_amd/csrc/lynx_codec.hip", "decode_attention_lynx_amd/csrc/lynx_attn.hip",
                   "decode_attention_lynx_amd/csrc/lynx_common.hpp", "decode_attention_lynx_amd/csrc/lynx_abi.hip",
                   "decode_attention_lynx_amd/csrc/hbm_probe.hip", "decode_attention_lynx_amd/csrc/lynx_verify.hip"]
+CALLS = LAYERS // LAYERS_PER_CALL                    # launches per codec op and step
 
 
 def alg_bytes_per_elem(op: str) -> float:
@@ -60,18 +73,25 @@ def op_flops(op: str) -> float:
 
 
 def op_elems(op: str) -> int:
-    """KV elements one launch of an op processes (the copy counts 2-byte elements of 1 GiB)."""
-    return {"encode": LAYERS * 2 * TOKENS * KVH * D, "decode_anchor": LAYERS * 2 * TOKENS * KVH * D,
-            "decode_full": LAYERS * 2 * TOKENS * KVH * D, "attn_anchor": 2 * AB * AT * AHKV * D,
+    """KV elements one launch of an op processes (a codec launch is one call: LAYERS_PER_CALL layers
+    of K and V; the copy counts 2-byte elements of 1 GiB)."""
+    codec = LAYERS_PER_CALL * 2 * TOKENS * KVH * D
+    return {"encode": codec, "decode_anchor": codec, "decode_full": codec, "attn_anchor": 2 * AB * AT * AHKV * D,
             "attn_verify": 2 * AB * AT * AHKV * D, "attn_anchor_c32": 2 * AB * AT * AHKV * D,
             "copy": (1 << 30) // 2}[op]
 
 
+def op_launches(op: str) -> int:
+    """Launches of an op per step (the codec ops are streamed layer by layer)."""
+    return CALLS if op in ("encode", "decode_anchor", "decode_full") else 1
+
+
 # kernels (name, grid size in threads) that make up one launch of each op
+_CODEC_PAGES = LAYERS_PER_CALL * 2 * TOKENS // P
 OP_KERNELS = {
-    "encode": [("lynx::k_encode<%d, false>" % C, LAYERS * 2 * TOKENS // P * KVH * 2 * 256)],
-    "decode_anchor": [("lynx::k_decode<false, false>", None)],
-    "decode_full": [("lynx::k_decode<true, false>", None)],
+    "encode": [("lynx::k_encode<%d, false>" % C, _CODEC_PAGES * KVH * 2 * 256)],
+    "decode_anchor": [("lynx::k_decode<false, false>", _CODEC_PAGES * KVH * (P // 128) * 256)],
+    "decode_full": [("lynx::k_decode<true, false>", _CODEC_PAGES * KVH * (P // 128) * 256)],
     "attn_anchor": [("lynx::k_attn_anchor<%s>" % ("64, 1" if C % 64 == 0 else "64, 2" if P % 64 == 0 else "32, 1"), None),
                     ("lynx::k_attn_combine", None)],
     "attn_verify": [("lynx::k_verify<%d>" % (1 if C % 64 == 0 else 2), None), ("lynx::k_verify_combine", None)],
@@ -219,8 +239,8 @@ def probe_call(status: int):
 
 def _cpu_worker(job):
     """One worker of the CPU baseline: the float64 oracle, single-threaded, on pages of the
-    request (encode and both decoders) for `budget` seconds, then anchor attention of one
-    sequence over a 4096-token prefix.  Returns (BF16-equivalent bytes, oracle seconds, pages)."""
+    request (encode and both decoders) for about 70% of `budget` seconds, then the anchor attention
+    of one sequence over a 4096-token prefix.  Returns (BF16-equivalent bytes, oracle seconds, pages)."""
     wid, budget = job
     import numpy as np  # noqa: F401
     from decode_attention_lynx_amd import synth
@@ -233,7 +253,7 @@ def _cpu_worker(job):
     t_codec, pages = 0.0, 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget * 0.7 and pages < 4096:
-        bits = synth.make_kv_np(P, KVH, D, seed=0, layer=wid * 4096 + pages, kv_idx=0)
+        bits = synth.make_kv_np(P, KVH, D, seed=SEED, layer=wid * 4096 + pages, kv_idx=0)
         s = time.perf_counter()
         anc, res, _ = o.encode(bits, P, C, ALPHA)
         o.decode_anchor(anc, 1, P, KVH, D, C, ALPHA)
@@ -241,8 +261,8 @@ def _cpu_worker(job):
         t_codec += time.perf_counter() - s
         pages += 1
     T = 4096
-    kb = synth.make_kv_np(T, AHKV, D, seed=0, layer=wid, kv_idx=0)
-    vb = synth.make_kv_np(T, AHKV, D, seed=0, layer=wid, kv_idx=1)
+    kb = synth.make_kv_np(T, AHKV, D, seed=1, layer=wid, kv_idx=0)
+    vb = synth.make_kv_np(T, AHKV, D, seed=1, layer=wid, kv_idx=1)
     ka, _, _ = o.encode(kb, P, C, ALPHA)
     va, _, _ = o.encode(vb, P, C, ALPHA)
     qb = synth.make_q_np(1, AHQ, D, seed=wid)
@@ -257,10 +277,12 @@ def _cpu_worker(job):
 
 def cpu_baseline(cpu_seconds: float = 32.0):
     """The float64 oracle on a bounded sample of the same workload, one single-threaded
-    worker process per host core (at most 16), about `cpu_seconds` of CPU work in all.
-    Must run before this process touches the GPU: the workers are forked."""
+    worker process per host core of this process's affinity set, at most 16 (the host share of
+    one GPU on the boxes this runs on), about `cpu_seconds` of CPU work in all.  Must run
+    before this process touches the GPU: the workers are forked."""
     import multiprocessing as mp
-    n = max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    n = max(1, min(16, affinity))
     budget = max(2.0, cpu_seconds / n)
     jobs = [(w, budget) for w in range(n)]
     if n == 1:
@@ -271,10 +293,13 @@ def cpu_baseline(cpu_seconds: float = 32.0):
     rate = sum(b / t for b, t, _ in res)          # the workers run concurrently
     pages = sum(p for _, _, p in res)
     secs = sum(t for _, t, _ in res)
-    return {"value": round(rate / 1e9, 5), "unit": "GB/s", "cores": n, "kind": "oracle",
-            "sample": f"float64 numpy oracle, {n} single-threaded worker processes: encode+decode_anchor+"
-                      f"decode_full of {pages} pages (256 tok x 8 kvh x 128) and, per worker, anchor attention "
-                      f"of 1 sequence x 64 q-heads over a 4096-token prefix; {secs:.1f} s of CPU time"}
+    return {"value": round(rate / 1e9, 5), "unit": "GB/s", "cores": n, "affinity_cores": affinity,
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle, {n} single-threaded worker processes ({affinity} cores in the "
+                      f"affinity set, at most 16 used): encode+decode_anchor+decode_full of {pages} pages "
+                      f"({P} tok x {KVH} kvh x {D}) of the long-context request and, per worker, anchor "
+                      f"attention of 1 sequence x {AHQ} q / {AHKV} kv heads over a 4096-token prefix; "
+                      f"{secs:.1f} s of CPU time"}
 
 
 # The codec on the other request shapes (parity cases of the test suite), reported by
@@ -283,10 +308,10 @@ def cpu_baseline(cpu_seconds: float = 32.0):
 CODEC_WORKLOADS = [
     ("single KV page pair: K and V of 4096 tokens x 8 kv heads x 128 (16.8 MB, cache-resident)",
      1, 4096, 8, 4096, 0, [(64, 255.0)], False),
+    ("llama3-8b request: 32 layers x K,V x 16384 tokens x 8 kv heads x 128 (2.15 GB), one call per op",
+     32, 16384, 8, 256, 0, [(64, 255.0)], False),
     ("qwen-32b request: 64 layers x K,V x 16384 tokens x 8 kv heads x 128 (4.3 GB)",
      64, 16384, 8, 256, 2, [(c, al) for c in (32, 64, 128) for al in (15.0, 63.0, 255.0)], False),
-    ("qwen3-235b long context: 94 layers x K,V x 131072 tokens x 4 kv heads x 128 (25.2 GB), "
-     "one call per layer tensor", 94, 131072, 4, 256, 3, [(64, 255.0)], True),
 ]
 
 
@@ -392,11 +417,43 @@ def codec_workloads(reps: int, warmup: int) -> dict:
             "timing": "median of the event-timed repetitions; BF16 decode output; inputs resident in HBM"}
 
 
+class CodecCalls:
+    """The long-context request's per-layer codec calls, made through the C ABI with pointers
+    precomputed once (the binding's per-call checks are done once here for every slice), and
+    spread round-robin over `streams`."""
+
+    def __init__(self, L, kv, anchor, residual, out, a_sz, r_sz):
+        import ctypes
+        self.L = L
+        self.c_void = ctypes.c_void_p
+        tok_call = LAYERS_PER_CALL * 2 * TOKENS
+        self.pages_call = tok_call // P
+        self.kv = [kv.data_ptr() + i * tok_call * KVH * D * 2 for i in range(CALLS)]
+        self.out = [out.data_ptr() + i * tok_call * KVH * D * 2 for i in range(CALLS)]
+        self.anc = [anchor.data_ptr() + i * self.pages_call * a_sz for i in range(CALLS)]
+        self.res = [residual.data_ptr() + i * self.pages_call * r_sz for i in range(CALLS)]
+
+    def launch(self, op: str, i: int, stream_handle: int) -> None:
+        L, v, s = self.L, self.c_void, self.c_void(stream_handle)
+        if op == "encode":
+            st = L.lynx_encode(v(self.kv[i]), self.pages_call, P, KVH, D, C, ALPHA, 3, v(self.anc[i]),
+                               v(self.res[i]), s)
+        elif op == "decode_anchor":
+            st = L.lynx_decode_anchor(v(self.anc[i]), self.pages_call, P, KVH, D, C, ALPHA, 0, v(self.out[i]), s)
+        else:
+            st = L.lynx_decode_full(v(self.anc[i]), v(self.res[i]), self.pages_call, P, KVH, D, C, ALPHA, 0,
+                                    v(self.out[i]), s)
+        if st != 0:
+            raise RuntimeError(f"{op} call {i}: status {st}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
+                    help="HIP streams the per-layer codec calls alternate over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ops", default="encode,decode_anchor,decode_full,attn_anchor")
     ap.add_argument("--next-ops", default="attn_anchor_c32,attn_verify,encode_to_host",
@@ -438,6 +495,7 @@ def main():
 
     dev = torch.device("cuda:0")
     ops = args.ops.split(",")
+    next_ops = [x for x in args.next_ops.split(",") if x]
     print(f"[bench] generating request {LAYERS}x2x{TOKENS}x{KVH}x{D} and attention inputs", file=sys.stderr,
           flush=True)
     T_all = LAYERS * 2 * TOKENS
@@ -446,13 +504,12 @@ def main():
     for layer in range(LAYERS):
         for kv_idx in (0, 1):
             t0 = (layer * 2 + kv_idx) * TOKENS
-            synth.make_kv_torch(TOKENS, KVH, D, seed=0, layer=layer, kv_idx=kv_idx, out=kv[t0:t0 + TOKENS])
+            synth.make_kv_torch(TOKENS, KVH, D, seed=SEED, layer=layer, kv_idx=kv_idx, out=kv[t0:t0 + TOKENS])
     a_sz, r_sz = lynx.stream_sizes(P, KVH, D, C)
     anchor = torch.empty((n_pages, a_sz), dtype=torch.uint8, device=dev)
     residual = torch.empty((n_pages, r_sz), dtype=torch.uint8, device=dev)
-    out_a = torch.empty_like(kv)
-    out_f = torch.empty_like(kv)
-    next_ops = [x for x in args.next_ops.split(",") if x]
+    out = torch.empty_like(kv)
+    codec = CodecCalls(lynx.lib(), kv, anchor, residual, out, a_sz, r_sz)
     # attention inputs: segments of 16 sequences x 32768 tokens, encoded once (the residual
     # stream only when the verification pass is timed)
     akv = torch.empty((AB * AT, AHKV, D), dtype=torch.bfloat16, device=dev)
@@ -474,9 +531,10 @@ def main():
                            device=dev)
         o_ver = torch.empty((AB, AM, AHQ, D), dtype=torch.bfloat16, device=dev)
         lse_ver = torch.empty((AB, AM, AHQ), dtype=torch.float32, device=dev)
+    pipe_pages = PIPE_LAYERS * 2 * TOKENS // P
     if "encode_to_host" in next_ops + ops:
-        anchor_h = torch.empty((n_pages, a_sz), dtype=torch.uint8, pin_memory=True)
-        residual_h = torch.empty((n_pages, r_sz), dtype=torch.uint8, pin_memory=True)
+        anchor_h = torch.empty((pipe_pages, a_sz), dtype=torch.uint8, pin_memory=True)
+        residual_h = torch.empty((pipe_pages, r_sz), dtype=torch.uint8, pin_memory=True)
         staging = torch.empty(lynx.lib().lynx_encode_to_host_staging_bytes(PIPE_GROUP, P, KVH, D, C),
                               dtype=torch.uint8, device=dev)
         copy_stream = torch.cuda.Stream()
@@ -489,28 +547,54 @@ def main():
     copy_dst = torch.empty_like(copy_src)
     sink = torch.zeros(1 << 14, dtype=torch.uint8, device=dev)
 
-    def run(op):
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()               # default priority, like every stream here
+    streams = [stream, side][:args.streams]
+    handles = [st.cuda_stream for st in streams]
+
+    def run_codec(op, evs=None):
+        """All per-layer calls of a codec op, round-robin over the streams; `evs` receives one
+        (start, end) event pair per launch, recorded on the launch's own stream."""
+        if len(streams) > 1:
+            fork = torch.cuda.Event()
+            fork.record(stream)
+            for st in streams[1:]:
+                st.wait_event(fork)
+        for i in range(CALLS):
+            k = i % len(streams)
+            if evs is not None:
+                e0, e1 = evs[i]
+                e0.record(streams[k])
+            codec.launch(op, i, handles[k])
+            if evs is not None:
+                e1.record(streams[k])
+        for st in streams[1:]:
+            join = torch.cuda.Event()
+            join.record(st)
+            stream.wait_event(join)
+
+    def run(op, evs=None):
+        if op in ("encode", "decode_anchor", "decode_full"):
+            run_codec(op, evs)
+            return
+        if evs is not None:
+            evs[0][0].record(stream)
         if op == "copy":
             probe_call(probe.hbm_probe_copy(copy_src.data_ptr(), copy_dst.data_ptr(), copy_src.numel(),
                                             torch.cuda.current_stream().cuda_stream))
-        elif op == "encode":
-            lynx.encode(kv, P, C, ALPHA, anchor_out=anchor, residual_out=residual)
-        elif op == "decode_anchor":
-            lynx.decode_anchor(anchor, n_pages, P, KVH, D, C, ALPHA, out=out_a)
-        elif op == "decode_full":
-            lynx.decode_full(anchor, residual, n_pages, P, KVH, D, C, ALPHA, out=out_f)
         elif op == "attn_anchor":
             lynx.attn_anchor(q, att[0], att[1], AT, AHKV, P, C, ALPHA, workspace=ws, out=o_att)
         elif op == "encode_to_host":
             # one request per call, drained before the next is queued: with many requests queued
             # ahead on the two streams the copies were measured to slow down several times
-            lynx.encode_to_host(kv, P, C, ALPHA, PIPE_GROUP, anchor_host=anchor_h, residual_host=residual_h,
-                                staging=staging, compute_stream=torch.cuda.current_stream(), copy_stream=copy_stream)
-            torch.cuda.current_stream().wait_stream(copy_stream)
+            lynx.encode_to_host(kv[:pipe_pages * P], P, C, ALPHA, PIPE_GROUP, anchor_host=anchor_h,
+                                residual_host=residual_h, staging=staging, compute_stream=stream,
+                                copy_stream=copy_stream)
+            stream.wait_stream(copy_stream)
             copy_stream.synchronize()
         elif op == "d2h_copy":      # reference: the same bytes, already encoded, copied device -> host
-            anchor_h.copy_(anchor, non_blocking=True)
-            residual_h.copy_(residual, non_blocking=True)
+            anchor_h.copy_(anchor[:pipe_pages], non_blocking=True)
+            residual_h.copy_(residual[:pipe_pages], non_blocking=True)
         elif op == "attn_anchor_c32":
             lynx.attn_anchor(q, att32[0], att32[1], AT, AHKV, P, 32, ALPHA, workspace=ws32, out=o_att)
         elif op == "attn_verify":
@@ -518,23 +602,33 @@ def main():
                              out=o_ver, lse=lse_ver)
         else:
             raise ValueError(f"unknown op {op}")
+        if evs is not None:
+            evs[0][1].record(stream)
 
-    elems = {op: op_elems(op) for op in ops}
+    def new_events(op):
+        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(op_launches(op))]
+
     for _ in range(args.warmup):
         for op in ops:
             run(op)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev = {op: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)] for op in ops}
+    # op time: from an event before its first launch to one after its last (on the timing stream,
+    # which has joined the other stream); launch durations: events on each launch's own stream
+    span = {op: [] for op in ops}
+    launches = {op: [] for op in ops}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s_ in range(args.steps):
         for op in ops:
-            ev[op][s][0].record(stream)
-            run(op)
-            ev[op][s][1].record(stream)
-        print(f"[bench] step {s + 1}/{args.steps} enqueued", file=sys.stderr, flush=True)
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            evs = new_events(op)
+            a_.record(stream)
+            run(op, evs)
+            b_.record(stream)
+            span[op].append((a_, b_))
+            launches[op].append(evs)
+        print(f"[bench] step {s_ + 1}/{args.steps} enqueued", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -546,10 +640,10 @@ def main():
             run(op)
         nev[op] = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(args.steps)]
-        for s in range(args.steps):
-            nev[op][s][0].record(stream)
+        for s_ in range(args.steps):
+            nev[op][s_][0].record(stream)
             run(op)
-            nev[op][s][1].record(stream)
+            nev[op][s_][1].record(stream)
         torch.cuda.synchronize()
         print(f"[bench] {op}: {args.steps} launches timed, ms: "
               + " ".join(f"{a.elapsed_time(b):.3f}" for a, b in nev[op]), file=sys.stderr, flush=True)
@@ -571,14 +665,21 @@ def main():
            "write_GBs": probe_gbs(lambda: probe_call(probe.hbm_probe_write(copy_dst.data_ptr(), nb, sptr())), nb),
            "copy_GBs": probe_gbs(lambda: probe_call(probe.hbm_probe_copy(copy_src.data_ptr(), copy_dst.data_ptr(), nb,
                                                                        sptr())), 2 * nb)}
-    ms = {op: sum(a.elapsed_time(b) for a, b in ev[op]) / args.steps for op in ops}
+    ms = {op: sum(a.elapsed_time(b) for a, b in span[op]) / args.steps for op in ops}
+    launch_ms = {op: sum(e0.elapsed_time(e1) for evs in launches[op] for e0, e1 in evs)
+                 / (args.steps * op_launches(op)) for op in ops}
     step_ms = wall * 1e3 / args.steps
     per_op = {}
     for op in ops:
-        alg = alg_bytes_per_elem(op) * elems[op]
-        per_op[op] = {"ms": round(ms[op], 4), "bf16_equiv_GBs": round(2.0 * elems[op] / ms[op] / 1e6, 1),
+        nl = op_launches(op)
+        alg_launch = alg_bytes_per_elem(op) * op_elems(op)
+        alg = alg_launch * nl
+        per_op[op] = {"ms": round(ms[op], 4), "launches": nl,
+                      "bf16_equiv_GBs": round(2.0 * op_elems(op) * nl / ms[op] / 1e6, 1),
                       "alg_GBs": round(alg / ms[op] / 1e6, 1), "frac_hbm_peak": round(alg / ms[op] / 1e6 / HBM_PEAK_GBS, 4),
-                      "alg_bytes_per_launch": int(alg)}
+                      "alg_bytes": int(alg), "launch_us": round(launch_ms[op] * 1e3, 2),
+                      "alg_bytes_per_launch": int(alg_launch),
+                      "launch_frac_hbm_peak": round(alg_launch / launch_ms[op] / 1e6 / HBM_PEAK_GBS, 4)}
     next_rep = {}
     if "encode_to_host" in next_ops:
         # the plain copy it is measured against (not part of any step)
@@ -594,10 +695,10 @@ def main():
     for op in next_ops:
         t = sum(a.elapsed_time(b) for a, b in nev[op]) / args.steps
         if op == "encode_to_host":
-            nbytes = n_pages * (a_sz + r_sz)
+            nbytes = pipe_pages * (a_sz + r_sz)
             next_rep[op] = {"ms": round(t, 4), "host_GBs": round(nbytes / t / 1e6, 2),
-                            "bf16_equiv_GBs": round(2.0 * op_elems("encode") / t / 1e6, 1),
-                            "group_pages": PIPE_GROUP, "d2h_copy_ms": round(d2h_ms, 4),
+                            "bf16_equiv_GBs": round(2.0 * pipe_pages * P * KVH * D / t / 1e6, 1),
+                            "layers": PIPE_LAYERS, "group_pages": PIPE_GROUP, "d2h_copy_ms": round(d2h_ms, 4),
                             "d2h_copy_GBs": round(nbytes / d2h_ms / 1e6, 2),
                             "copy_over_pipeline": round(d2h_ms / t, 4)}
             continue
@@ -614,30 +715,34 @@ def main():
                         "alg_flops_per_launch": fl,
                         "alg_bytes_per_launch": int(alg_bytes_per_elem(op) * op_elems(op))}
     path_ops = [op for op in ops if op != "copy"]
-    total_bf16 = sum(2.0 * elems[op] for op in path_ops)
+    total_bf16 = sum(2.0 * op_elems(op) * op_launches(op) for op in path_ops)
     value = total_bf16 / (step_ms / 1e3) / 1e9
     dom = max(path_ops or ops, key=lambda o_: ms[o_])
-    achieved = per_op[dom]["alg_GBs"]
+    achieved = round(alg_bytes_per_elem(dom) * op_elems(dom) / launch_ms[dom] / 1e6, 1)
     rec = {
         "metric": "KV GB/s (BF16-equiv) encode/decode + anchor-attn, % of MI355X HBM peak",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "llama3-8b request codec (32 layers x K,V x 16384 tok x 8 kvh x 128 BF16, P=256, "
-                               "C=64, alpha=255: encode + decode_anchor + decode_full) + anchor-only decode "
-                               "attention (16 seq x 64 q / 8 kv heads x 128, 32768-token context)",
+        "config": {"workload": f"qwen3-235b long-context request codec ({LAYERS} layers x K,V x {TOKENS} tok x "
+                               f"{KVH} kvh x {D} BF16, 25.2 GB resident, P={P}, C={C}, alpha={ALPHA:g}: encode + "
+                               f"decode_anchor + decode_full, streamed layer by layer, {CALLS} calls per op "
+                               f"alternating over {len(streams)} HIP stream(s)) + anchor-only decode attention "
+                               f"({AB} seq x {AHQ} q / {AHKV} kv heads x {D}, {AT}-token context)",
                    "ops": per_op, "hbm_peak_GBs": HBM_PEAK_GBS, "hbm_measured": hbm,
                    "beyond_step": {"workload": f"attn_verify: verification pass over full codes ({AB} seq x {AM} "
                                                f"draft tokens x {AHQ} q / {AHKV} kv heads x {D}, {AT}-token "
-                                               "context), bound: mfma; encode_to_host: the request encoded "
-                                               f"in groups of {PIPE_GROUP} pages and copied to pinned host "
-                                               "memory, bound: the device-to-host link; attn_anchor_c32: the "
-                                               "anchor attention of the step at a chunk of 32 tokens, bound: hbm",
+                                               "context), bound: mfma; encode_to_host: the first "
+                                               f"{PIPE_LAYERS} layers of the request encoded in groups of "
+                                               f"{PIPE_GROUP} pages and copied to pinned host memory, bound: "
+                                               "the device-to-host link; attn_anchor_c32: the anchor attention "
+                                               "of the step at a chunk of 32 tokens, bound: hbm",
                                    "ops": next_rep},
                    "arith": "float32 codec (float64 statistics and boundary cases), float16 MFMA attention "
                             "with float32 accumulation"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dom)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dom),
+                     "per": "launch: algorithmic bytes of one launch over the mean launch duration"},
         "cpu_baseline": cpu_rec,
     }
     print(json.dumps(rec), flush=True)

@@ -42,9 +42,8 @@ namespace lynx {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kAttnWaves = 12;          // three per SIMD
 constexpr int kAttnWorkgroups = 256;   // workgroups the context splits aim for
-constexpr int kMaxGroup = 8;         // query heads per kv head handled by one workgroup
+constexpr int kMaxGroup = 16;        // query heads per kv head handled by one workgroup
 
 struct AttnArgs {
   const uint16_t* q;
@@ -158,8 +157,12 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int
   const size_t row0 = code_offset(a.P, kvh, 0, tin);   // block 0 of the head, token tin
   const uint8_t* kcb = a.kanc + seg + row0;
   const uint8_t* vcb = a.vanc + seg + row0;
-  // every code byte is read once: streaming loads, which keep the caches for the metadata
-  // (the page statistics are shared by all tiles of a page)
+  // every code byte is read once.  Key rows are read as 16-byte pieces that tile whole 512 B
+  // runs of each code block: streaming loads, which keep the caches for the metadata (the page
+  // statistics are shared by all tiles of a page).  Value rows are read as 4-byte words, one
+  // 32 B run of a code row per 8 lanes: plain (cached) loads, so the other half of each line
+  // the memory returns is still in L2 when the next row's load asks for it (with streaming
+  // loads these 32 B runs cost ~10% of the kernel time).
 #pragma unroll
   for (int mb = 0; mb < TILE / 16; ++mb) t.kw[mb] = ld_stream(kcb + lo.kcode + 16 * mb * kCodeRow);
 #pragma unroll
@@ -167,8 +170,7 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int row = 32 * ks + (r < 4 ? r : 12 + r);     // + 4g (in the lane offset)
-      t.vw[8 * ks + r] =
-          __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vcb + lo.vcode + row * kCodeRow));
+      t.vw[8 * ks + r] = *reinterpret_cast<const uint32_t*>(vcb + lo.vcode + row * kCodeRow);
     }
   const uint8_t* kmb = a.kanc + seg + a.codes + (size_t)kvh * kHeadDim * 4;
   const uint8_t* vmb = a.vanc + seg + a.codes + (size_t)kvh * kHeadDim * 4;
@@ -191,34 +193,54 @@ __device__ __forceinline__ void load_tile(const AttnArgs& a, int b, int kvh, int
   }
 }
 
-template <int TILE, int CPT>
-__global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void k_attn_anchor(AttnArgs a) {
+// Maximum over all 64 lanes (every lane ends with it).
+__device__ __forceinline__ float wave_max_all(float v) {
+  v = wave_max_g(v);
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));
+}
+
+// TILE tokens per wave step holding CPT chunks of CT = TILE / CPT tokens (8 .. 64).
+// GW = 8: the 16 MFMA columns are 8 query heads twice, the first 8 carrying the float16 high
+//         part of the folded query and the second 8 its remainder (groups of up to 8 heads);
+// GW = 16: the 16 columns are 16 query heads, the two parts of the folded query in two MFMAs.
+// WAVES waves per workgroup: 12 (three per SIMD) or 8 (two per SIMD, for the register use of
+// four chunks per tile).
+template <int TILE, int CPT, int GW, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WAVES / 4))) void k_attn_anchor(AttnArgs a) {
+  constexpr int CT = TILE / CPT;       // tokens per chunk
+  static_assert(CT >= 8 && (CT >= 16 || TILE == 32), "chunks of 8 tokens use 32-token tiles");
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile addressing stays scalar
   const int n = lane & 15, g = lane >> 4;
-  const int hh = n & 7;                 // query head (within the group) of this column
-  const bool lo_col = n >= 8;
+  const int hh = n & (GW - 1);          // query head (within the group) of this column
+  const bool lo_col = GW == 8 && n >= 8;
 
   // LDS: the replicated pair table during the loop, reused for the wave merge after it
   constexpr int kPairWords = 256 * 64;
-  // merge records: o of head h at word h*kMergeRow + d + d/32 (one pad word per 32
-  // channels: the writes of the 8 heads x 4 lane groups then fall in 32 banks)
+  // merge records of 8 heads at a time: o of head h at word h*kMergeRow + d + d/32 (one pad
+  // word per 32 channels: the writes of the 8 heads x 4 lane groups then fall in 32 banks)
   constexpr int kMergeRow = kHeadDim + 4;
-  constexpr int kMergeWords = kAttnWaves * kMaxGroup * (kMergeRow + 2);
+  constexpr int kMergeWords = 2 * WAVES * kMaxGroup + WAVES * 8 * kMergeRow;
   __shared__ uint32_t s_big[kPairWords > kMergeWords ? kPairWords : kMergeWords];
-  // per wave: (A_K, B_K) and (A_V, B_V) of channels 2i, 2i+1 at slot swz(i), where
-  // swz(16g + t) = 4t + g puts the 4 lane groups' simultaneous reads in different banks
-  __shared__ float4 s_kab[kAttnWaves][CPT][kHeadDim / 2];
-  __shared__ float4 s_vab[kAttnWaves][CPT][kHeadDim / 2];
+  // per wave: (A_K, B_K) of the chunk being folded, and (A_V, B_V) of every chunk of the tile,
+  // for channels 2i, 2i+1 at slot swz(i), where swz(16g + t) = 4t + g puts the 4 lane groups'
+  // simultaneous reads in different banks
+  __shared__ float4 s_kab[WAVES][kHeadDim / 2];
+  __shared__ float4 s_vab[WAVES][CPT][kHeadDim / 2];
   uint32_t* s_pair = s_big;
 
 #pragma unroll 8
-  for (int w = tid; w < kPairWords; w += kAttnWaves * 64) s_pair[w] = a.pair[w >> 6];   // word 64e + r: entry e, copy r
+  for (int w = tid; w < kPairWords; w += WAVES * 64) s_pair[w] = a.pair[w >> 6];   // word 64e + r: entry e, copy r
   const uint32_t lane4 = 4u * (uint32_t)lane;
 
-  // this lane's query slice (head hh, channels 32g .. 32g+31), kept as BF16 pairs
+  // this lane's query slice (head hh, channels 32g .. 32g+31), kept as BF16 pairs, and the
+  // largest |q| of the workgroup's heads (range of the folded query, below)
   uint32_t qw[16];
+  float qmax = 0.0f;
   {
     const bool live = hh < a.G;
     const uint16_t* qp = a.q + ((size_t)(b * a.Hq + kvh * a.G + (live ? hh : 0))) * kHeadDim + 32 * g;
@@ -230,8 +252,13 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
       qw[4 * v4 + 2] = live ? w.z : 0u;
       qw[4 * v4 + 3] = live ? w.w : 0u;
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(qw[i])), fabsf(bf16_hi(qw[i]))));
+    qmax = wave_max_all(qmax);
   }
   const float qscale = a.qscale;
+  // |q_d A_d| * qscale <= qmax * (gamma_scale + eps) * (1 + eps) * qscale, since sigma <= 1
+  const float qbound = qmax * (1.0f + (float)kEps) * qscale;
   const float lo_w = lo_col ? 1.0f : 0.0f;
   __syncthreads();
 
@@ -244,76 +271,116 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int seq_len = a.seq_lens == nullptr ? a.T : min(max(a.seq_lens[b], 0), a.T);
   const int t_begin = split * a.tiles_per_split;
   const int t_end = min((seq_len + TILE - 1) / TILE, t_begin + a.tiles_per_split);   // may be empty
-  float4 (*kab)[kHeadDim / 2] = s_kab[wave];
+  float4* kab = s_kab[wave];
   float4 (*vab)[kHeadDim / 2] = s_vab[wave];
+  const int slot = 4 * (lane & 15) + (lane >> 4);
 
   const TileOffsets toff = tile_offsets(lane, a.P);
 
-  // one 64-token tile of this wave: scores, online softmax, values
+  // one tile of this wave: scores, online softmax, values
   auto process = [&](const TileIn<TILE, CPT>& cur, int tile) {
+    // ---- range of the folded query.  A key channel of range gamma_scale folds into
+    //      |q~_d| <= |q_d| (gamma_scale + eps)(sigma + eps) qscale, which must stay inside
+    //      float16.  The key map carries 2^-E, E >= 0 the smallest exponent that keeps every
+    //      |q~| of the tile below 2^15 (from the tile's largest channel range), and the scores
+    //      are scaled back by 2^E in float32 before the softmax.  Ordinary KV has E = 0.  (The
+    //      reduction is done every tile: a branch around it, taken only when some lane's bound
+    //      is large, measured ~5% slower than the unconditional ~12 instructions.)
+    float sd, su;
+    {
+      const float mb_all = wave_max_all((fmaxf(cur.km[2], cur.km[3]) + (float)kEps) * qbound);
+      const int e = (int)((__float_as_uint(mb_all) >> 23) & 0xFFu) - 127;   // floor(log2)
+      const int E = max(0, e - 14);                                        // mb_all * 2^-E < 2^15
+      sd = __uint_as_float((uint32_t)(127 - E) << 23);
+      su = __uint_as_float((uint32_t)(127 + E) << 23);
+    }
+    const float qs = qscale * sd;
 
-    // ---- the chunk's affine maps for channels 2*lane, 2*lane+1, shared through LDS:
-    //      A = (gamma_scale+eps)(sigma+eps), B = gamma_min + mu (gamma_scale+eps);
-    //      the key map carries the softmax scale (base 2).  One 16-byte record per
-    //      channel pair, at slot swz(lane).
+    // ---- the value maps of the tile's chunks, A = (gamma_scale+eps)(sigma+eps),
+    //      B = gamma_min + mu (gamma_scale+eps), for channels 2*lane, 2*lane+1
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      float ak[2], bk[2], av[2], bv[2];
+      float av[2], bv[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const float d1k = cur.km[2 + e] + (float)kEps, d2k = cur.km[6 + 4 * k + e] + (float)kEps;
-        ak[e] = d1k * d2k * qscale;
-        bk[e] = fmaf(cur.km[4 + 4 * k + e], d1k, cur.km[e]) * qscale;
         const float d1v = cur.vm[2 + e] + (float)kEps, d2v = cur.vm[6 + 4 * k + e] + (float)kEps;
         av[e] = d1v * d2v;
         bv[e] = fmaf(cur.vm[4 + 4 * k + e], d1v, cur.vm[e]);
       }
-      const int slot = 4 * (lane & 15) + (lane >> 4);
-      kab[k][slot] = make_float4(ak[0], ak[1], bk[0], bk[1]);
       vab[k][slot] = make_float4(av[0], av[1], bv[0], bv[1]);
     }
-    __builtin_amdgcn_wave_barrier();
 
-    // ---- per chunk of the tile: fold its key map into the query, qt = q*A_K (float16
-    //      hi / lo by column) and beta = q.B_K, then the scores of its tokens:
-    //      S^T = L_K (tokens x 128) * qt (128 x 16 columns)
+    // ---- per chunk: its key map (with the softmax scale, base 2, and 2^-E) folded into the
+    //      query, qt = q*A_K as float16 high / low parts and beta = q.B_K, then the scores of
+    //      its tokens: S^T = L_K (tokens x 128) * qt (128 x 16 columns)
     constexpr int NS = TILE / 4;         // scores per lane: TILE/16 row blocks x 4
-    constexpr int MBC = TILE / 16 / CPT; // row blocks of 16 tokens per chunk
     float s[NS];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      h8 bq[4];
+      {
+        float ak[2], bk[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float d1k = cur.km[2 + e] + (float)kEps, d2k = cur.km[6 + 4 * k + e] + (float)kEps;
+          ak[e] = d1k * d2k * qs;
+          bk[e] = fmaf(cur.km[4 + 4 * k + e], d1k, cur.km[e]) * qs;
+        }
+        if (k > 0) __builtin_amdgcn_wave_barrier();   // the previous chunk's fold has read the slot
+        kab[slot] = make_float4(ak[0], ak[1], bk[0], bk[1]);
+        __builtin_amdgcn_wave_barrier();
+      }
+      h8 bq[4], bql[4];
       float beta = 0.0f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        uint32_t bw[4];
+        uint32_t bw[4], bwl[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const float4 ab = kab[k][4 * (4 * kk + e2) + g];   // channels 32g + 8kk + 2e2, +1
+          const float4 ab = kab[4 * (4 * kk + e2) + g];   // channels 32g + 8kk + 2e2, +1
           const uint32_t w = qw[4 * kk + e2];
           const float x0 = bf16_lo(w), x1 = bf16_hi(w);
           beta = fmaf(x0, ab.z, fmaf(x1, ab.w, beta));
           const float q0 = x0 * ab.x, q1 = x1 * ab.y;
-          // float16 split of the folded query: columns 0..7 take hi = rtz(q), columns
-          // 8..15 take rtz(q - hi); hi + lo carries ~22 bits of q
+          // float16 split of the folded query: hi = rtz(q), lo = rtz(q - hi); hi + lo carries
+          // ~22 bits of q
           const auto hi = __builtin_amdgcn_cvt_pkrtz(q0, q1);
-          const float r0 = fmaf(-(float)hi[0], lo_w, q0), r1 = fmaf(-(float)hi[1], lo_w, q1);
-          bw[e2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+          if constexpr (GW == 8) {          // columns 0..7 take hi, 8..15 take lo
+            const float r0 = fmaf(-(float)hi[0], lo_w, q0), r1 = fmaf(-(float)hi[1], lo_w, q1);
+            bw[e2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+          } else {
+            bw[e2] = __builtin_bit_cast(uint32_t, hi);
+            bwl[e2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(q0 - (float)hi[0], q1 - (float)hi[1]));
+          }
         }
         const u32x4v bv4 = {bw[0], bw[1], bw[2], bw[3]};
         bq[kk] = __builtin_bit_cast(h8, bv4);
+        if constexpr (GW == 16) {
+          const u32x4v bl4 = {bwl[0], bwl[1], bwl[2], bwl[3]};
+          bql[kk] = __builtin_bit_cast(h8, bl4);
+        }
       }
       beta = wave_sum_g(beta);
-      const float hb = 0.5f * beta;      // each of the two column halves carries half of beta
+      const float hb = GW == 8 ? 0.5f * beta : beta;   // GW 8: each of the two column halves carries half
+      // row blocks of 16 tokens of this chunk (a row block holds two chunks of 8 tokens: the
+      // lanes of rows 0..7, g < 2, take the first, g >= 2 the second)
+      constexpr int MB0 = CT >= 16 ? CT / 16 : 1;
 #pragma unroll
-      for (int mb = MBC * k; mb < MBC * (k + 1); ++mb) {
+      for (int mi = 0; mi < MB0; ++mi) {
+        const int mb = CT >= 16 ? k * (CT / 16) + mi : k / 2;
         f4 acc = f4{hb, hb, hb, hb};
         const uint32_t w4[4] = {cur.kw[mb].x, cur.kw[mb].y, cur.kw[mb].z, cur.kw[mb].w};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lookup_row(w4[kk], s_pair, lane4), bq[kk], acc, 0, 0, 0);
+        for (int kk = 0; kk < 4; ++kk) {
+          const h8 lk = lookup_row(w4[kk], s_pair, lane4);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lk, bq[kk], acc, 0, 0, 0);
+          if constexpr (GW == 16) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lk, bql[kk], acc, 0, 0, 0);
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[4 * mb + i] = acc[i] + dpp_row_ror8(acc[i]);
+        for (int i = 0; i < 4; ++i) {
+          const float v = GW == 8 ? acc[i] + dpp_row_ror8(acc[i]) : acc[i];
+          if (CT >= 16) s[4 * mb + i] = v;
+          else if ((g >> 1) == (k & 1)) s[4 * mb + i] = v;
+        }
       }
     }
     if ((tile + 1) * TILE > seq_len) {   // the sequence ends inside this tile: mask the tail
@@ -324,26 +391,27 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
           if (tile * TILE + 16 * mb + 4 * g + i >= seq_len) s[4 * mb + i] = -INFINITY;
     }
 
-    // ---- online softmax (base 2) for head hh over this tile's 64 tokens
+    // ---- online softmax (base 2) for the column's head over this tile's tokens; the scores
+    //      are in units of 2^-E
     float mt = s[0];
 #pragma unroll
     for (int i = 1; i < NS; ++i) mt = fmaxf(mt, s[i]);
-    mt = wave_max_g(mt);
+    mt = wave_max_g(mt) * su;
     const float m_new = fmaxf(m_run, mt);
     const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-    float lsum[CPT];                     // per chunk: its tokens' p of this lane
+    float lrb[TILE / 16];                // per row block: this lane's rows' p
     h8 pt[TILE / 32];
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) lsum[k] = 0.0f;
+    for (int mb = 0; mb < TILE / 16; ++mb) lrb[mb] = 0.0f;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const float p = __builtin_amdgcn_exp2f(s[i] - m_new);
-      lsum[i / (NS / CPT)] += p;
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[i], su, -m_new));
+      lrb[i >> 2] += p;
       pt[i >> 3][i & 7] = (_Float16)p;
     }
     float lsum_all = 0.0f;
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) lsum_all += lsum[k];
+    for (int mb = 0; mb < TILE / 16; ++mb) lsum_all += lrb[mb];
     l_run = fmaf(l_run, corr, lsum_all);
     if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0) {   // the running max moved for some head
 #pragma unroll
@@ -355,30 +423,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
     // block j holds d = 8*row + j.  Token pairs (2i, 2i+1) of a k-step are interleaved into
     // pair-table indices per channel.  Then the chunk's value map is undone:
     // o += A_V * T + B_V * sum(p), channel d = 32g + 8i + j.
-    constexpr int KSC = TILE / 32 / CPT;   // k-steps of 32 tokens per chunk
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const float lt = wave_sum_g(lsum[k]);
-      f4 tacc[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) tacc[j] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = KSC * k; ks < KSC * (k + 1); ++ks) {
-        uint32_t ev[4], od[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w0 = cur.vw[8 * ks + 2 * i], w1 = cur.vw[8 * ks + 2 * i + 1];
-          ev[i] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);   // byte k: channel 2k of tokens 2i, 2i+1
-          od[i] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);  // byte k: channel 2k+1
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t* src = (j & 1) ? od : ev;
-          const u32x4v r = {pair_at(s_pair, lane4, src[0], j >> 1), pair_at(s_pair, lane4, src[1], j >> 1),
-                            pair_at(s_pair, lane4, src[2], j >> 1), pair_at(s_pair, lane4, src[3], j >> 1)};
-          tacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, r), pt[ks], tacc[j], 0, 0, 0);
-        }
-      }
+    // The B operand of k-step ks holds, in lane group g, tokens 32ks + 4g + r (dwords 0, 1) and
+    // 32ks + 16 + 4g + r (dwords 2, 3), r = 0..3.
+    auto apply_map = [&](int k, const f4 (&tacc)[8], float lt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -388,48 +435,128 @@ __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu
           o_acc[2 * j2 + 1][i] = fmaf(ab.y, tacc[2 * j2 + 1][i], fmaf(ab.w, lt, o_acc[2 * j2 + 1][i]));
         }
       }
+    };
+    auto value_operands = [&](int ks, h8 (&av)[8]) {
+      uint32_t ev[4], od[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w0 = cur.vw[8 * ks + 2 * i], w1 = cur.vw[8 * ks + 2 * i + 1];
+        ev[i] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);   // byte k: channel 2k of tokens 2i, 2i+1
+        od[i] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);  // byte k: channel 2k+1
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t* src = (j & 1) ? od : ev;
+        const u32x4v r = {pair_at(s_pair, lane4, src[0], j >> 1), pair_at(s_pair, lane4, src[1], j >> 1),
+                          pair_at(s_pair, lane4, src[2], j >> 1), pair_at(s_pair, lane4, src[3], j >> 1)};
+        av[j] = __builtin_bit_cast(h8, r);
+      }
+    };
+    if constexpr (CT >= 32) {
+      constexpr int KSC = CT / 32;       // k-steps of 32 tokens per chunk
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        float lk = 0.0f;
+#pragma unroll
+        for (int mb = k * (CT / 16); mb < (k + 1) * (CT / 16); ++mb) lk += lrb[mb];
+        const float lt = wave_sum_g(lk);
+        f4 tacc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tacc[j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = KSC * k; ks < KSC * (k + 1); ++ks) {
+          uint32_t ev[4], od[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t w0 = cur.vw[8 * ks + 2 * i], w1 = cur.vw[8 * ks + 2 * i + 1];
+            ev[i] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);
+            od[i] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t* src = (j & 1) ? od : ev;
+            const u32x4v r = {pair_at(s_pair, lane4, src[0], j >> 1), pair_at(s_pair, lane4, src[1], j >> 1),
+                              pair_at(s_pair, lane4, src[2], j >> 1), pair_at(s_pair, lane4, src[3], j >> 1)};
+            tacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, r), pt[ks], tacc[j], 0, 0, 0);
+          }
+        }
+        apply_map(k, tacc, lt);
+      }
+    } else {
+      // chunks of 16 or 8 tokens: each k-step holds 32 / CT chunks; the table operands of the
+      // k-step are formed once and the products run once per chunk, on the probabilities of
+      // that chunk's tokens only (the others zeroed: whole dword pairs for a chunk of 16, and
+      // for a chunk of 8 also the lane groups of the other half)
+      constexpr int CK = 32 / CT;
+#pragma unroll
+      for (int ks = 0; ks < TILE / 32; ++ks) {
+        h8 av[8];
+        value_operands(ks, av);
+        const u32x4v pw = __builtin_bit_cast(u32x4v, pt[ks]);
+#pragma unroll
+        for (int c = 0; c < CK; ++c) {
+          const int hf = CT == 16 ? c : c >> 1;           // dword pair holding the chunk's tokens
+          const bool mine = CT == 16 ? true : (g >> 1) == (c & 1);
+          const uint32_t d0 = hf == 0 && mine ? pw[0] : 0u, d1 = hf == 0 && mine ? pw[1] : 0u;
+          const uint32_t d2 = hf == 1 && mine ? pw[2] : 0u, d3 = hf == 1 && mine ? pw[3] : 0u;
+          const u32x4v pm = {d0, d1, d2, d3};
+          const h8 pc = __builtin_bit_cast(h8, pm);
+          // this lane's p of the chunk's tokens: row block 2ks + hf, all its rows (CT = 16) or
+          // the rows of lane groups (c & 1)*2, +1 (CT = 8)
+          const float lt = wave_sum_g(mine ? lrb[2 * ks + hf] : 0.0f);
+          f4 tacc[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            tacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[j], pc, f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          apply_map(ks * CK + c, tacc, lt);
+        }
+      }
     }
     __builtin_amdgcn_wave_barrier();   // the next tile rewrites this wave's (A, B) tables
   };
 
-  // tiles t_begin + wave, + kAttnWaves, ...: one tile buffer per wave; three waves per SIMD
-  // hide each other's load latency (a second buffer would cost the third wave's registers)
+  // tiles t_begin + wave, + WAVES, ...: one tile buffer per wave; the other waves of the SIMD
+  // hide each other's load latency (a second buffer would cost a wave's registers)
   TileIn<TILE, CPT> cur;
-  for (int tile = t_begin + wave; tile < t_end; tile += kAttnWaves) {
+  for (int tile = t_begin + wave; tile < t_end; tile += WAVES) {
     load_tile(a, b, kvh, tile, toff, cur);
     process(cur, tile);
   }
 
-  // ---- merge the waves (columns 0..G-1 hold the result; 8..15 duplicate them)
+  // ---- merge the waves, 8 heads at a time (GW 8: columns 0..G-1 hold the result, 8..15
+  //      duplicate them; GW 16: column h holds head h)
   l_run = wave_sum_g(l_run);
   __syncthreads();                      // every wave is done with the pair table: reuse its LDS
   float (*s_m)[kMaxGroup] = reinterpret_cast<float (*)[kMaxGroup]>(s_big);
-  float (*s_l)[kMaxGroup] = reinterpret_cast<float (*)[kMaxGroup]>(s_big + kAttnWaves * kMaxGroup);
-  float (*s_o)[kMaxGroup][kMergeRow] =
-      reinterpret_cast<float (*)[kMaxGroup][kMergeRow]>(s_big + 2 * kAttnWaves * kMaxGroup);
-  if (g == 0 && n < kMaxGroup) { s_m[wave][n] = m_run; s_l[wave][n] = l_run; }
-  if (n < kMaxGroup) {
+  float (*s_l)[kMaxGroup] = reinterpret_cast<float (*)[kMaxGroup]>(s_big + WAVES * kMaxGroup);
+  float (*s_o)[8][kMergeRow] = reinterpret_cast<float (*)[8][kMergeRow]>(s_big + 2 * WAVES * kMaxGroup);
+  if (g == 0 && n < GW) { s_m[wave][n] = m_run; s_l[wave][n] = l_run; }
+  for (int h0 = 0; h0 < a.G; h0 += 8) {
+    if (n >= h0 && n < h0 + 8) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_o[wave][n][8 * (4 * g + i) + j + g] = o_acc[j][i];   // d = 32g + 8i + j
-  }
-  __syncthreads();
-  for (int idx = tid; idx < a.G * kHeadDim; idx += kAttnWaves * 64) {
-    const int h = idx / kHeadDim, d = idx - h * kHeadDim;
-    float M = s_m[0][h];
-#pragma unroll
-    for (int w = 1; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float o = 0.0f, l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
-      const float f = (s_m[w][h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
-      o = fmaf(s_o[w][h][d + (d >> 5)], f, o);
-      l = fmaf(s_l[w][h], f, l);
+        for (int i = 0; i < 4; ++i) s_o[wave][n - h0][8 * (4 * g + i) + j + g] = o_acc[j][i];   // d = 32g + 8i + j
     }
-    float* rec = a.ws + ((size_t)((b * a.Hq + kvh * a.G + h) * a.splits + split)) * (kHeadDim + 2);
-    rec[2 + d] = o;
-    if (d == 0) { rec[0] = M; rec[1] = l; }
+    __syncthreads();
+    const int nh = min(8, a.G - h0);
+    for (int idx = tid; idx < nh * kHeadDim; idx += WAVES * 64) {
+      const int hl = idx / kHeadDim, d = idx - hl * kHeadDim, h = h0 + hl;
+      float M = s_m[0][h];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) M = fmaxf(M, s_m[w][h]);
+      float o = 0.0f, l = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float f = (s_m[w][h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
+        o = fmaf(s_o[w][hl][d + (d >> 5)], f, o);
+        l = fmaf(s_l[w][h], f, l);
+      }
+      float* rec = a.ws + ((size_t)((b * a.Hq + kvh * a.G + h) * a.splits + split)) * (kHeadDim + 2);
+      rec[2 + d] = o;
+      if (d == 0) { rec[0] = M; rec[1] = l; }
+    }
+    __syncthreads();                    // the records of these heads are read before the next heads overwrite them
   }
 }
 
@@ -465,15 +592,34 @@ struct AttnPlan {
   int tile, cpt, splits, tiles_per_split, ntiles;
 };
 
-// Tile of the context: 64 tokens inside one chunk of 64 or more, or two chunks of 32 when
-// the pages hold whole 64-token tiles; 32 tokens for a chunk of 32 in pages of an odd
-// number of chunks; 0 for chunks the kernel does not take.  *cpt = chunks per tile.
+// Tile of the context (a tile lies inside one page): 64 tokens inside one chunk of 64 or
+// more; for a chunk of 32, two chunks when the pages hold whole 64-token tiles, else 32 tokens
+// of one chunk; for a chunk of 16, four chunks in pages of whole 64-token tiles; for a chunk
+// of 8, four chunks of a 32-token tile in pages of whole 32-token tiles; 0 for the shapes the
+// kernel does not take.  *cpt = chunks per tile.
 int attn_tile(int C, int P, int* cpt) {
   *cpt = 1;
   if (C % 64 == 0) return 64;
-  if (C != 32) return 0;
-  if (P % 64 == 0) { *cpt = 2; return 64; }
-  return 32;
+  if (C == 32) {
+    if (P % 64 == 0) { *cpt = 2; return 64; }
+    return 32;
+  }
+  if (C == 16 && P % 64 == 0) { *cpt = 4; return 64; }
+  if (C == 8 && P % 32 == 0) { *cpt = 4; return 32; }
+  return 0;
+}
+
+// Waves per workgroup for chunks-per-tile cpt and group width gw: 12 (three per SIMD) where
+// the registers allow it, 8 where four chunks per tile, or two chunks with 16 heads, need more.
+int attn_waves(int cpt, int gw) { return cpt >= 4 || (cpt == 2 && gw == 16) ? 8 : 12; }
+
+template <int GW>
+const void* attn_kernel(int tile, int cpt) {
+  if (tile == 32) return cpt == 4 ? reinterpret_cast<const void*>(&k_attn_anchor<32, 4, GW, 8>)
+                                  : reinterpret_cast<const void*>(&k_attn_anchor<32, 1, GW, 12>);
+  if (cpt == 4) return reinterpret_cast<const void*>(&k_attn_anchor<64, 4, GW, 8>);
+  if (cpt == 2) return reinterpret_cast<const void*>(&k_attn_anchor<64, 2, GW, GW == 16 ? 8 : 12>);
+  return reinterpret_cast<const void*>(&k_attn_anchor<64, 1, GW, 12>);
 }
 
 bool attn_plan(int batch, int ctx, int Hq, int Hkv, int D, int P, int C, AttnPlan* pl) {
@@ -482,8 +628,8 @@ bool attn_plan(int batch, int ctx, int Hq, int Hkv, int D, int P, int C, AttnPla
   pl->tile = attn_tile(C, P, &pl->cpt);
   if (D != kHeadDim || pl->tile == 0 || Hq / Hkv > kMaxGroup) return false;
   pl->ntiles = ctx / pl->tile;
-  // One workgroup per compute unit of the 256-CU gfx950 parts (12 waves fill a CU at this
-  // kernel's register use): long-lived workgroups, one table fill and one merge each.
+  // One workgroup per compute unit of the 256-CU gfx950 parts (12 or 8 waves fill a CU at
+  // this kernel's register use): long-lived workgroups, one table fill and one merge each.
   // The split count minimises rounds of workgroups x tiles per split (ties: fewer splits).
   const long long units = (long long)batch * Hkv;
   long long best_cost = -1;
@@ -580,12 +726,12 @@ int attn_launch(const void* q_dev, const void* k_anchor_dev, const void* v_ancho
   }
   for (int bt = 0; bt < 256; ++bt) a.pair[bt] = (uint32_t)lut[bt & 15] | ((uint32_t)lut[bt >> 4] << 16);
   void* kargs[] = {&a};
-  const void* fn = pl.tile == 32  ? reinterpret_cast<const void*>(&k_attn_anchor<32, 1>)
-                   : pl.cpt == 2 ? reinterpret_cast<const void*>(&k_attn_anchor<64, 2>)
-                                 : reinterpret_cast<const void*>(&k_attn_anchor<64, 1>);
+  // query groups of up to 8 heads: two MFMA columns per head (float16 high / low parts of the
+  // folded query); up to 16: one column per head
+  const void* fn = a.G <= 8 ? attn_kernel<8>(pl.tile, pl.cpt) : attn_kernel<16>(pl.tile, pl.cpt);
   hipError_t e = hipLaunchKernel(fn,
                                  dim3((unsigned)pl.splits, (unsigned)kv_heads, (unsigned)batch),
-                                 dim3(kAttnWaves * 64), kargs, 0, stream);
+                                 dim3(attn_waves(pl.cpt, a.G <= 8 ? 8 : 16) * 64), kargs, 0, stream);
   if (e != hipSuccess) return LYNX_ELAUNCH;
   e = hipLaunchKernel(reinterpret_cast<const void*>(&k_attn_combine), dim3((unsigned)(batch * q_heads)),
                       dim3(kHeadDim), kargs, 0, stream);

@@ -17,8 +17,9 @@
 // Decomposition: one workgroup (8 waves) per (sequence, kv head, block of 256 query
 // rows, context split); query row r = m*G + h (draft token m, query head h of the
 // group); each wave owns 32 rows as two MFMA column groups of 16.  The context is
-// walked in 64-token tiles (a tile lies inside one chunk, the chunk being a multiple
-// of 64).  Each tile is decoded once into LDS for all rows:
+// walked in 64-token tiles (a tile lies inside one page and holds one chunk of 64 or
+// more, or 2 or 4 whole chunks of 32 or 16 tokens, each token decoded with the map of its
+// own chunk).  Each tile is decoded once into LDS for all rows:
 //   * keys as K_hat * scale * log2(e) in float32, stored as BF16 high and low parts
 //     (K_hat ~ hi + lo to 16 bits), row-major [token][channel];
 //   * values as the raw table values L (float16), transposed [channel][token];
@@ -186,7 +187,7 @@ __device__ __forceinline__ float2 affine(float gmin, float gscale, float mu, flo
   return make_float2(d1 * d2 * scale, fmaf(mu, d1, gmin) * scale);
 }
 
-// CPT = chunks per 64-token tile (1 for a chunk of 64 or more, 2 for a chunk of 32)
+// CPT = chunks per 64-token tile (1 for a chunk of 64 or more, 2 / 4 for chunks of 32 / 16)
 template <int CPT>
 struct alignas(16) VerifyLds {
   float lut[256 * kLutCopies];             // float32 table, entry e copy c at e*16 + c
@@ -550,7 +551,9 @@ namespace {
 // pages of a multiple of 64 tokens (a tile then holds two whole chunks of one page); 0 otherwise.
 int verify_cpt(int C, int P) {
   if (C > 0 && C % kVTile == 0) return 1;
-  if (C == kVTile / 2 && P % kVTile == 0) return 2;
+  if (P % kVTile != 0) return 0;
+  if (C == kVTile / 2) return 2;
+  if (C == kVTile / 4) return 4;     // chunks of 8 would need 34 KB of maps: beyond the LDS
   return 0;
 }
 
@@ -668,8 +671,10 @@ int verify_launch_common(const void* q_dev, const void* k_anchor_dev, const void
     a.lut32[idx] = (float)v;
   }
   void* kargs[] = {&a};
-  const void* fn = verify_cpt(chunk, page_tokens) == 1 ? reinterpret_cast<const void*>(&k_verify<1>)
-                                                         : reinterpret_cast<const void*>(&k_verify<2>);
+  const int cpt = verify_cpt(chunk, page_tokens);
+  const void* fn = cpt == 1   ? reinterpret_cast<const void*>(&k_verify<1>)
+                   : cpt == 2 ? reinterpret_cast<const void*>(&k_verify<2>)
+                              : reinterpret_cast<const void*>(&k_verify<4>);
   hipError_t e = hipLaunchKernel(fn,
                                  dim3((unsigned)pl.splits, (unsigned)kv_heads, (unsigned)(batch * pl.rowblocks)),
                                  dim3(kVThreads), kargs, 0, stream);

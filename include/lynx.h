@@ -159,17 +159,22 @@ size_t lynx_attn_workspace_bytes(int batch, int ctx_tokens, int q_heads, int kv_
  *                  ctx_tokens/page_tokens consecutive segments starting at
  *                  segment b*(ctx_tokens/page_tokens), with kv_heads heads.
  *   q_heads      : a multiple of kv_heads; query head hq reads kv head
- *                  hq / (q_heads/kv_heads).  Group size q_heads/kv_heads <= 8.
+ *                  hq / (q_heads/kv_heads).  Group size q_heads/kv_heads <= 16
+ *                  (else LYNX_EUNSUPPORTED).
  *   ctx_tokens   : a positive multiple of page_tokens.
- *   chunk        : a multiple of 32 in this library (else LYNX_EUNSUPPORTED): each
- *                  wave step covers 64 tokens of one chunk, or, when chunk == 32, 64
- *                  tokens of two chunks if page_tokens is a multiple of 64 and 32
- *                  tokens of one chunk otherwise.
+ *   chunk        : a multiple of 64; or 32; or 16 with page_tokens a multiple of 64;
+ *                  or 8 with page_tokens a multiple of 32 (else LYNX_EUNSUPPORTED).
+ *                  A wave step covers a 64-token tile (one chunk of 64 or more, or two
+ *                  / four chunks of 32 / 16), or a 32-token tile (one chunk of 32 in
+ *                  pages of an odd number of chunks, or four chunks of 8).
  *   sm_scale     : > 0, or <= 0 to use 1/sqrt(head_dim).
  *   workspace_dev, ws_bytes : at least lynx_attn_workspace_bytes(...) bytes.
  *   out_dtype    : LYNX_OUT_BF16 or LYNX_OUT_F32.
  *   out_dev      : [batch][q_heads][head_dim] of out_dtype, written.
  * Supported by this library: head_dim == 128.
+ * Range: the key map folded into the query is carried in float16 with a power-of-two
+ * exponent chosen per tile, so keys of any BF16 range are scored correctly; the scores
+ * themselves (q . k * sm_scale) and the output must be finite in float32.
  */
 int lynx_attn_anchor(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev,
                      int batch, int ctx_tokens, int q_heads, int kv_heads, int head_dim,
@@ -255,8 +260,8 @@ size_t lynx_attn_verify_workspace_bytes(int batch, int n_query, int ctx_tokens, 
  *                  segments; sequence b's context is the ctx_tokens/page_tokens
  *                  consecutive segments starting at segment b*(ctx_tokens/page_tokens).
  *   q_heads      : a multiple of kv_heads (query head hq reads kv head hq / (q_heads/kv_heads)).
- *   chunk        : a multiple of 64, or 32 with page_tokens a multiple of 64, in this library
- *                  (else LYNX_EUNSUPPORTED).
+ *   chunk        : a multiple of 64, or 32 or 16 with page_tokens a multiple of 64, in this
+ *                  library (else LYNX_EUNSUPPORTED).
  *   sm_scale     : > 0, or <= 0 to use 1/sqrt(head_dim).
  *   workspace_dev, ws_bytes : at least lynx_attn_verify_workspace_bytes(...) bytes.
  *   out_dtype    : LYNX_OUT_BF16 or LYNX_OUT_F32; out_dev [batch][n_query][q_heads][head_dim].

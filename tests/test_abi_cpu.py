@@ -127,8 +127,12 @@ def test_attention_validation():
     assert attn(dt=5) == lynx.LYNX_EINVAL
     assert attn(T=0) == lynx.LYNX_EINVAL
     assert attn(D=64) == lynx.LYNX_EUNSUPPORTED
-    assert attn(C=16, P=256) == lynx.LYNX_EUNSUPPORTED          # chunk not a multiple of 32
-    assert attn(Hq=18, Hkv=2) == lynx.LYNX_EUNSUPPORTED         # group of 9 query heads
+    assert attn(C=16, P=256) == lynx.LYNX_ENOSPACE              # chunk 16: supported, workspace too small
+    assert attn(C=16, P=96, T=960) == lynx.LYNX_EUNSUPPORTED    # chunk 16 in pages of no whole 64-token tile
+    assert attn(C=8, P=256) == lynx.LYNX_ENOSPACE               # chunk 8: supported
+    assert attn(C=8, P=48, T=960) == lynx.LYNX_EUNSUPPORTED     # chunk 8 in pages of no whole 32-token tile
+    assert attn(Hq=32, Hkv=2) == lynx.LYNX_ENOSPACE             # group of 16: supported
+    assert attn(Hq=34, Hkv=2) == lynx.LYNX_EUNSUPPORTED         # group of 17 query heads
     assert attn(q=ODD) == lynx.LYNX_EALIGN
     assert attn(out=None) == lynx.LYNX_EALIGN
     assert attn(ws=ODD) == lynx.LYNX_EALIGN
@@ -138,7 +142,8 @@ def test_attention_validation():
 
 
 @pytest.mark.parametrize("B,T,Hq,Hkv,P,C", [(16, 32768, 64, 8, 256, 64), (2, 1024, 16, 2, 256, 64),
-                                            (3, 320, 8, 1, 64, 64), (2, 512, 8, 2, 256, 32), (1, 64, 2, 2, 64, 64)])
+                                            (3, 320, 8, 1, 64, 64), (2, 512, 8, 2, 256, 32), (1, 64, 2, 2, 64, 64),
+                                            (1, 96, 8, 1, 32, 32), (2, 512, 32, 2, 256, 16), (1, 96, 8, 1, 32, 8)])
 def test_attention_workspace_bytes(B, T, Hq, Hkv, P, C):
     """One (m, l, o[128]) float32 record per (sequence, query head, context split); the splits
     cover the context's tiles with no empty split."""
@@ -146,14 +151,15 @@ def test_attention_workspace_bytes(B, T, Hq, Hkv, P, C):
     rec = (128 + 2) * 4
     assert ws > 0 and ws % (B * Hq * rec) == 0
     splits = ws // (B * Hq * rec)
-    tile = 64 if C % 64 == 0 else 32
+    tile = 64 if C % 64 == 0 or (C in (16, 32) and P % 64 == 0) else 32
     ntiles = T // tile
     per = -(-ntiles // splits)
     assert 1 <= splits <= ntiles and (splits - 1) * per < ntiles <= splits * per
 
 
 def test_attention_workspace_bytes_unsupported():
-    assert lynx.attn_workspace_bytes(2, 1024, 16, 2, 128, 256, 16) == 0
+    assert lynx.attn_workspace_bytes(2, 960, 16, 2, 128, 96, 16) == 0
+    assert lynx.attn_workspace_bytes(2, 1024, 34, 2, 128, 256, 64) == 0
     assert lynx.attn_workspace_bytes(2, 1000, 16, 2, 128, 256, 64) == 0
     assert lynx.attn_workspace_bytes(2, 1024, 16, 2, 64, 256, 64) == 0
 
@@ -174,7 +180,8 @@ def test_verify_validation():
     assert verify(sm=float("nan")) == lynx.LYNX_EINVAL
     assert verify(dt=3) == lynx.LYNX_EINVAL
     assert verify(D=64) == lynx.LYNX_EUNSUPPORTED
-    assert verify(C=16, P=256) == lynx.LYNX_EUNSUPPORTED        # chunk neither 32 nor a multiple of 64
+    assert verify(C=16, P=256) == lynx.LYNX_ENOSPACE            # chunk 16: supported
+    assert verify(C=8, P=256) == lynx.LYNX_EUNSUPPORTED         # chunk 8: not in the verification kernel
     assert verify(T=960, P=96, C=32) == lynx.LYNX_EUNSUPPORTED   # chunk 32 in pages of 96: tiles cross pages
     assert verify(C=32, P=256) == lynx.LYNX_ENOSPACE             # chunk 32: supported
     assert verify(kr=ODD) == lynx.LYNX_EALIGN
@@ -187,7 +194,8 @@ def test_verify_validation():
 
 @pytest.mark.parametrize("B,M,T,Hq,Hkv,P,C", [(16, 64, 32768, 64, 8, 256, 64), (2, 4, 1024, 16, 2, 256, 64),
                                               (1, 17, 256, 64, 8, 256, 64), (3, 1, 320, 8, 1, 64, 64),
-                                              (2, 5, 512, 12, 4, 256, 128), (2, 4, 1024, 16, 2, 256, 32)])
+                                              (2, 5, 512, 12, 4, 256, 128), (2, 4, 1024, 16, 2, 256, 32),
+                                              (2, 4, 1024, 64, 4, 256, 16)])
 def test_verify_workspace_bytes(B, M, T, Hq, Hkv, P, C):
     """One (m, l, 0, 0, o[128]) float32 record per (sequence, draft token, query head, context split);
     the splits cover the context's 64-token tiles with no empty split."""
@@ -201,7 +209,7 @@ def test_verify_workspace_bytes(B, M, T, Hq, Hkv, P, C):
 
 
 def test_verify_workspace_bytes_unsupported():
-    assert lynx.attn_verify_workspace_bytes(2, 4, 1024, 16, 2, 128, 256, 16) == 0
+    assert lynx.attn_verify_workspace_bytes(2, 4, 1024, 16, 2, 128, 256, 8) == 0
     assert lynx.attn_verify_workspace_bytes(2, 4, 960, 16, 2, 128, 96, 32) == 0
     assert lynx.attn_verify_workspace_bytes(2, 4, 1000, 16, 2, 128, 256, 64) == 0
     assert lynx.attn_verify_workspace_bytes(2, 0, 1024, 16, 2, 128, 256, 64) == 0
@@ -254,7 +262,7 @@ def test_verify_paged_validation():
     assert call(maxp=0) == lynx.LYNX_EINVAL
     assert call(bt=None) == lynx.LYNX_EALIGN
     assert call(sl=ctypes.c_void_p(GOOD.value + 2)) == lynx.LYNX_EALIGN
-    assert call(C=16) == lynx.LYNX_EUNSUPPORTED
+    assert call(C=8) == lynx.LYNX_EUNSUPPORTED
     assert call(maxp=1 << 24) == lynx.LYNX_EUNSUPPORTED
     assert call() == lynx.LYNX_ENOSPACE
     assert call(B=0) == lynx.LYNX_OK

@@ -29,8 +29,8 @@ def test_counter_summary_calibrates_against_the_copy(tmp_path):
     fetch = {("hbm_probe::k_probe_copy(unsigned int const*)", 2097152): [gib_kib / 2] * 3,
              (f"void lynx::k_encode<{bench.C}, false>(lynx::EncodeArgs)", enc_grid): [1000.0, 1002.0],
              (f"void lynx::k_encode<{bench.C}, false>(lynx::EncodeArgs)", enc_grid // 2): [7.0],   # setup encode, ignored
-             ("void lynx::k_decode<false, false>(lynx::DecodeArgs)", 524288): [10.0],
-             ("void lynx::k_decode<true, false>(lynx::DecodeArgs)", 524288): [20.0],
+             ("void lynx::k_decode<false, false>(lynx::DecodeArgs)", bench.OP_KERNELS["decode_anchor"][0][1]): [10.0],
+             ("void lynx::k_decode<true, false>(lynx::DecodeArgs)", bench.OP_KERNELS["decode_full"][0][1]): [20.0],
              ("void lynx::k_attn_anchor<64, 1>(lynx::AttnArgs)", 4096): [30.0],
              ("lynx::k_attn_combine(lynx::AttnArgs)", 131072): [1.0],
              ("void lynx::k_verify<1>(lynx::(anonymous namespace)::VerifyArgs)", 131072): [40.0],

@@ -28,6 +28,21 @@ def load_maker():
     return mk
 
 
+def stored_ablation():
+    out, section = {}, None
+    for line in open(os.path.join(HERE, "golden", "accuracy_vnmse.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        if line.startswith("["):
+            section = line
+            continue
+        if section == "[ablation]" and not line.startswith("config"):
+            name, full, anchor = [x.strip() for x in line.split("|")]
+            out[name] = (float(full), float(anchor))
+    return out
+
+
 def stored_methods():
     out, section = {}, None
     for line in open(os.path.join(HERE, "golden", "accuracy_vnmse.txt")):
@@ -70,3 +85,31 @@ def test_vnmse_through_the_gpu_path(gpu):
             want = stored[name][col]
             print(f"[accuracy] q x {s}: {name} vNMSE gpu {val:.4e} oracle {want:.4e}", flush=True)
             assert abs(val - want) <= 0.05 * want + 2e-7
+
+
+@pytest.mark.parametrize("label,P,C,alpha", [("C=16", 256, 16, 255.0), ("C=32", 256, 32, 255.0),
+                                             ("alpha=2000", 256, 64, 2000.0), ("P=512", 512, 64, 255.0)])
+def test_ablation_rows_through_the_gpu_path(gpu, label, P, C, alpha):
+    """Rows of the reviewer's ablation (chunk size, alpha, page size) at query scale 0.1: the GPU
+    path's vNMSE for Lynx (full codes, verification kernel) and Lynx-INT4 (anchor attention)
+    against the stored oracle values."""
+    mk = load_maker()
+    k, v, q = mk.inputs()
+    T, Hkv, M = mk.T, mk.HKV, mk.M
+    print(f"[accuracy] ablation {label}", flush=True)
+    kt = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).cuda()
+    vt = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda()
+    ka, kr = lynx.encode(kt, P, C, alpha)
+    va, vr = lynx.encode(vt, P, C, alpha)
+    qb = mk.scaled(q, mk.ABLATION_Q)
+    ref = acc.attention_outputs(qb, o.bf16_bits_to_f64(k), o.bf16_bits_to_f64(v), T)
+    qt = torch.from_numpy(np.ascontiguousarray(qb).view(np.int16)).view(torch.bfloat16).cuda()
+    full, _ = lynx.attn_verify(qt, ka, kr, va, vr, T, Hkv, P, C, alpha, out_dtype=torch.float32)
+    anchor = torch.stack([lynx.attn_anchor(qt[:, m].contiguous(), ka, va, T, Hkv, P, C, alpha,
+                                           out_dtype=torch.float32) for m in range(M)], dim=1)
+    torch.cuda.synchronize()
+    want_full, want_anchor = stored_ablation()[label]
+    for name, val, want in (("Lynx", acc.vnmse(full.cpu().numpy().astype(np.float64), ref), want_full),
+                            ("Lynx-INT4", acc.vnmse(anchor.cpu().numpy().astype(np.float64), ref), want_anchor)):
+        print(f"[accuracy] {label} {name}: vNMSE gpu {val:.4e} oracle {want:.4e}", flush=True)
+        assert abs(val - want) <= 0.05 * want + 2e-7
