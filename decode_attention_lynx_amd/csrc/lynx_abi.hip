@@ -1,6 +1,7 @@
 // C ABI of liblynx: argument validation, parameter blocks and kernel launches.
 // Every argument error is detected here, on the host, before any launch.  The
-// library allocates nothing and keeps no state between calls.
+// library allocates no device memory; the only state kept between calls is the
+// per-GPU address of the no-allocation attention's buffer (lynx_attn.hip).
 //
 // Sources, cited by page title and section:
 //   [Review] "Lynx: Progressive Speculative KV Cache Transfer for Disaggregated
@@ -282,6 +283,14 @@ int lynx_attn_anchor(const void* q_dev, const void* k_anchor_dev, const void* v_
   return attn_anchor_launch(q_dev, k_anchor_dev, v_anchor_dev, batch, ctx_tokens, q_heads, kv_heads, head_dim,
                             page_tokens, chunk, alpha, sm_scale, workspace_dev, ws_bytes, out_dtype, out_dev,
                             static_cast<hipStream_t>(hip_stream));
+}
+
+int lynx_attn_anchor_noalloc(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev, int batch,
+                             int ctx_tokens, int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk,
+                             float alpha, float sm_scale, int out_dtype, void* out_dev, void* hip_stream) {
+  return attn_anchor_noalloc_launch(q_dev, k_anchor_dev, v_anchor_dev, batch, ctx_tokens, q_heads, kv_heads,
+                                    head_dim, page_tokens, chunk, alpha, sm_scale, out_dtype, out_dev,
+                                    static_cast<hipStream_t>(hip_stream));
 }
 
 int lynx_attn_anchor_paged(const void* q_dev, const void* k_anchor_pool_dev, const void* v_anchor_pool_dev,

@@ -36,6 +36,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 namespace lynx {
 
@@ -662,11 +663,14 @@ size_t attn_workspace_bytes(int batch, int ctx, int Hq, int Hkv, int D, int P, i
 
 namespace {
 
-// Shared by the contiguous and the paged entry points (block_table == nullptr: contiguous).
-int attn_launch(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev, int batch, int ctx_tokens,
-                int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk, float alpha, float sm_scale,
-                void* workspace_dev, size_t ws_bytes, int out_dtype, void* out_dev, const int32_t* block_table,
-                const int32_t* seq_lens, int max_pages, int n_pool, hipStream_t stream) {
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Every argument check of the anchor attention except those of the workspace: LYNX_OK with
+// *need the workspace bytes (0 for an empty batch, which has nothing to do).
+int attn_check(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev, int batch, int ctx_tokens,
+               int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk, float alpha, float sm_scale,
+               int out_dtype, const void* out_dev, size_t* need) {
+  *need = 0;
   if (batch < 0 || ctx_tokens <= 0 || q_heads <= 0 || kv_heads <= 0 || head_dim <= 0 || page_tokens <= 0 ||
       chunk <= 0)
     return LYNX_EINVAL;
@@ -681,10 +685,24 @@ int attn_launch(const void* q_dev, const void* k_anchor_dev, const void* v_ancho
   if (batch == 0) return LYNX_OK;
   AttnPlan pl;
   if (!attn_plan(batch, ctx_tokens, q_heads, kv_heads, head_dim, page_tokens, chunk, &pl)) return LYNX_EINVAL;
-  const size_t need = (size_t)batch * q_heads * pl.splits * (kHeadDim + 2) * sizeof(float);
-  auto al16 = [](const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  if (!al16(q_dev) || !al16(k_anchor_dev) || !al16(v_anchor_dev) || !al16(out_dev) || !al16(workspace_dev))
+  if (!aligned16(q_dev) || !aligned16(k_anchor_dev) || !aligned16(v_anchor_dev) || !aligned16(out_dev))
     return LYNX_EALIGN;
+  *need = (size_t)batch * q_heads * pl.splits * (kHeadDim + 2) * sizeof(float);
+  return LYNX_OK;
+}
+
+// Shared by the contiguous and the paged entry points (block_table == nullptr: contiguous).
+int attn_launch(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev, int batch, int ctx_tokens,
+                int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk, float alpha, float sm_scale,
+                void* workspace_dev, size_t ws_bytes, int out_dtype, void* out_dev, const int32_t* block_table,
+                const int32_t* seq_lens, int max_pages, int n_pool, hipStream_t stream) {
+  size_t need = 0;
+  const int st = attn_check(q_dev, k_anchor_dev, v_anchor_dev, batch, ctx_tokens, q_heads, kv_heads, head_dim,
+                            page_tokens, chunk, alpha, sm_scale, out_dtype, out_dev, &need);
+  if (st != LYNX_OK || batch == 0) return st;
+  AttnPlan pl;
+  attn_plan(batch, ctx_tokens, q_heads, kv_heads, head_dim, page_tokens, chunk, &pl);
+  if (!aligned16(workspace_dev)) return LYNX_EALIGN;
   if (ws_bytes < need) return LYNX_ENOSPACE;
 
   AttnArgs a;
@@ -761,6 +779,56 @@ int attn_anchor_paged_launch(const void* q_dev, const void* k_anchor_pool, const
   return attn_launch(q_dev, k_anchor_pool, v_anchor_pool, batch, max_pages * page_tokens, q_heads, kv_heads,
                      head_dim, page_tokens, chunk, alpha, sm_scale, workspace_dev, ws_bytes, out_dtype, out_dev,
                      block_table, seq_lens, max_pages, n_pool, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The anchor attention without caller workspace: its split-context partial records go to
+// `scratch`, a device array of LYNX_ATTN_SCRATCH_BYTES that every GPU the library runs on holds
+// for the life of the process.  In host code `scratch` names a host-side stand-in, not the
+// device memory: its device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is handed to the kernels.  No allocation happens.
+// Every record the combine pass reads is written by the attention kernel of the same call, so
+// nothing needs clearing; calls that overlap on one GPU (on different streams) share the array
+// and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[LYNX_ATTN_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// Device address of the current device's `scratch`, looked up on the first call on that device.
+int scratch_address(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return LYNX_ELAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return LYNX_ELAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return LYNX_OK;
+}
+
+}  // namespace
+
+int attn_anchor_noalloc_launch(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev, int batch,
+                               int ctx_tokens, int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk,
+                               float alpha, float sm_scale, int out_dtype, void* out_dev, hipStream_t stream) {
+  // every argument error first, on the host; then the records this shape needs against the buffer
+  size_t need = 0;
+  int st = attn_check(q_dev, k_anchor_dev, v_anchor_dev, batch, ctx_tokens, q_heads, kv_heads, head_dim,
+                      page_tokens, chunk, alpha, sm_scale, out_dtype, out_dev, &need);
+  if (st != LYNX_OK || batch == 0) return st;
+  if (need > (size_t)LYNX_ATTN_SCRATCH_BYTES) return LYNX_ENOSPACE;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != LYNX_OK) return st;
+  return attn_launch(q_dev, k_anchor_dev, v_anchor_dev, batch, ctx_tokens, q_heads, kv_heads, head_dim, page_tokens,
+                     chunk, alpha, sm_scale, ws, need, out_dtype, out_dev, nullptr, nullptr, 0, 0, stream);
 }
 
 }  // namespace lynx

@@ -22,6 +22,9 @@ int attn_anchor_launch(const void* q_dev, const void* k_anchor_dev, const void* 
                        int ctx_tokens, int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk,
                        float alpha, float sm_scale, void* workspace_dev, size_t ws_bytes, int out_dtype,
                        void* out_dev, hipStream_t stream);
+int attn_anchor_noalloc_launch(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev, int batch,
+                               int ctx_tokens, int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk,
+                               float alpha, float sm_scale, int out_dtype, void* out_dev, hipStream_t stream);
 int attn_anchor_paged_launch(const void* q_dev, const void* k_anchor_pool, const void* v_anchor_pool, int n_pool,
                              const int32_t* block_table, const int32_t* seq_lens, int batch, int max_pages,
                              int q_heads, int kv_heads, int head_dim, int page_tokens, int chunk, float alpha,

@@ -27,7 +27,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblynx.so"
 EXPORTS = ("lynx_strerror", "lynx_stream_sizes", "lynx_encode", "lynx_decode_anchor", "lynx_decode_full",
            "lynx_attn_workspace_bytes", "lynx_attn_anchor", "lynx_attn_verify_workspace_bytes", "lynx_attn_verify",
            "lynx_attn_anchor_paged", "lynx_encode_to_host_staging_bytes", "lynx_encode_to_host",
-           "lynx_attn_verify_paged")
+           "lynx_attn_verify_paged", "lynx_attn_anchor_noalloc")
+ATTN_SCRATCH_BYTES = 32 << 20    # LYNX_ATTN_SCRATCH_BYTES
 
 _lib = None
 
@@ -68,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.lynx_encode_to_host.restype = c_int
         L.lynx_encode_to_host.argtypes = [c_void] + [c_int] * 5 + [c_float, c_int, c_void, c_size, c_void, c_void,
                                                                  c_void, c_void]
+        L.lynx_attn_anchor_noalloc.restype = c_int
+        L.lynx_attn_anchor_noalloc.argtypes = [c_void, c_void, c_void] + [c_int] * 7 + [c_float, c_float, c_int,
+                                                                                        c_void, c_void]
         L.lynx_attn_anchor_paged.restype = c_int
         L.lynx_attn_anchor_paged.argtypes = [c_void, c_void, c_void, c_int, c_void, c_void] + [c_int] * 7 + [
             c_float, c_float, c_void, c_size, c_int, c_void, c_void]
@@ -250,6 +254,28 @@ def attn_anchor(q, k_anchor, v_anchor, ctx_tokens: int, kv_heads: int, page_toke
     _check(lib().lynx_attn_anchor(_ptr(q), _ptr(k_anchor), _ptr(v_anchor), B, ctx_tokens, Hq, kv_heads, D,
                                   page_tokens, chunk, alpha, sm_scale, _ptr(workspace), workspace.numel(), code,
                                   _ptr(out), _stream(stream)), "lynx_attn_anchor")
+    return out
+
+
+def attn_anchor_noalloc(q, k_anchor, v_anchor, ctx_tokens: int, kv_heads: int, page_tokens: int, chunk: int,
+                        alpha: float, sm_scale: float = 0.0, out_dtype=None, out=None, stream=None):
+    """attn_anchor without a workspace: the library's per-GPU buffer holds the partial results
+    (no device allocation by the library; `out` is allocated here when not given)."""
+    import torch
+    B, Hq, D = q.shape
+    _need(q, "q", 0, (torch.bfloat16,))
+    a_sz, _ = stream_sizes(page_tokens, kv_heads, D, chunk)
+    seg = B * _pages(ctx_tokens, page_tokens) * a_sz
+    _need(k_anchor, "k_anchor", seg)
+    _need(v_anchor, "v_anchor", seg)
+    dt = torch.float32 if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=dt, device=q.device)
+    code = _out_code(out)
+    _need(out, "out", B * Hq * D * out.element_size())
+    _check(lib().lynx_attn_anchor_noalloc(_ptr(q), _ptr(k_anchor), _ptr(v_anchor), B, ctx_tokens, Hq, kv_heads, D,
+                                          page_tokens, chunk, alpha, sm_scale, code, _ptr(out), _stream(stream)),
+           "lynx_attn_anchor_noalloc")
     return out
 
 

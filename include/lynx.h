@@ -10,8 +10,11 @@
  *
  * Conventions for every entry point
  *   - Pointers named *_dev are device pointers (hipMalloc'd or torch CUDA
- *     tensors), owned by the caller, 16-byte aligned.  The library allocates
- *     nothing, keeps no global state, and is re-entrant.
+ *     tensors), owned by the caller, 16-byte aligned.  The library allocates no
+ *     device memory and is re-entrant; its only state is the per-GPU partial-result
+ *     buffer of lynx_attn_anchor_noalloc (a static device array, and its address per
+ *     GPU once looked up).  lynx_encode_to_host creates and destroys four HIP events
+ *     per call to order its two streams.
  *   - `hip_stream` is a hipStream_t (NULL = the legacy default stream).  Work is
  *     enqueued asynchronously on it; the host is never synchronised.  Calls on
  *     different streams may run at once (give each its own output buffers): many
@@ -181,6 +184,26 @@ int lynx_attn_anchor(const void* q_dev, const void* k_anchor_dev, const void* v_
                      int page_tokens, int chunk, float alpha, float sm_scale,
                      void* workspace_dev, size_t ws_bytes, int out_dtype, void* out_dev,
                      void* hip_stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): lynx_attn_anchor without a workspace argument.  Its
+ * split-context partial results go to a library-owned device buffer of LYNX_ATTN_SCRATCH_BYTES,
+ * one per GPU, held from the library's first use on that GPU until the process ends; the call
+ * allocates and frees nothing (the buffer's device address is looked up once per GPU, on the
+ * first call made with that GPU current).
+ *   Arguments and results as lynx_attn_anchor, without workspace_dev / ws_bytes.
+ *   Errors: those of lynx_attn_anchor; LYNX_ENOSPACE when the shape needs more than
+ *   LYNX_ATTN_SCRATCH_BYTES of partial results (lynx_attn_workspace_bytes(...) says how much);
+ *   LYNX_ELAUNCH when the buffer's address cannot be obtained.
+ *   Calls that overlap on one GPU (different streams, or different host threads) share the
+ *   buffer and race: order them on one stream.
+ */
+#define LYNX_ATTN_SCRATCH_BYTES (32u << 20)
+int lynx_attn_anchor_noalloc(const void* q_dev, const void* k_anchor_dev, const void* v_anchor_dev,
+                             int batch, int ctx_tokens, int q_heads, int kv_heads, int head_dim,
+                             int page_tokens, int chunk, float alpha, float sm_scale, int out_dtype,
+                             void* out_dev, void* hip_stream);
 
 /*
  * Staging bytes lynx_encode_to_host needs for groups of group_pages pages: two groups'

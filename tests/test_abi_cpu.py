@@ -295,3 +295,17 @@ def test_binding_refuses_buffers_before_any_launch():
     with pytest.raises(ValueError, match="bytes"):
         lynx._need(torch.zeros(4, dtype=torch.uint8), "x", 5, device="cpu")
     assert lynx._need(torch.zeros(5, dtype=torch.uint8), "x", 5, device="cpu") is not None
+
+
+def test_attention_noalloc_validation():
+    """The no-allocation entry point refuses, on the host and before any launch, a shape whose
+    partial results exceed its per-GPU buffer, and reports argument errors as lynx_attn_anchor."""
+    def call(B=2, T=1024, Hq=16, Hkv=2, P=256, C=64, dt=lynx.OUT_F32, q=GOOD, out=GOOD):
+        return lynx.lib().lynx_attn_anchor_noalloc(q, GOOD, GOOD, B, T, Hq, Hkv, 128, P, C, 255.0, 0.0, dt, out,
+                                                   None)
+    assert lynx.attn_workspace_bytes(1024, 256, 64, 8, 128, 256, 64) > lynx.ATTN_SCRATCH_BYTES
+    assert call(B=1024, T=256, Hq=64, Hkv=8) == lynx.LYNX_ENOSPACE
+    assert call(T=1000) == lynx.LYNX_EINVAL
+    assert call(Hq=34) == lynx.LYNX_EUNSUPPORTED
+    assert call(dt=7) == lynx.LYNX_EINVAL
+    assert call(B=0) == lynx.LYNX_OK
