@@ -5,9 +5,9 @@ anchor-only decode attention.
 One step =
   encode        94 layers x {K, V} x 131072 tokens x 4 kv heads x 128 (BF16, 25.2 GB resident
                 in HBM), P = 256, C = 64, alpha = 255, anchor + residual streams.  Streamed layer
-                by layer: one call per layer (its K and V, 1024 pages, 268 MB of BF16), the calls
-                alternating over two HIP streams, so that one call's last workgroups overlap the
-                next call's first ones (the library header advises this for many small calls)
+                by layer: one call per layer (its K and V, 1024 pages, 268 MB of BF16), the 94
+                calls back to back on one HIP stream (--streams 2 alternates them over two
+                streams, which overlaps each call's tail with the next call's start)
   decode_anchor the same request back to BF16 from the anchor segments, the same per-layer calls
                 (each layer into its own part of a request-sized output buffer)
   decode_full   the same from anchor + residual
@@ -16,6 +16,8 @@ One step =
 Timed after the step, on its own (not part of `value`):
   attn_verify   the verification pass over full codes: the same 16 sequences with 64 draft
                 tokens each, anchor + residual segments
+  codec_two_streams the step's encode, decode_anchor and decode_full with their per-layer calls
+                alternating over two HIP streams (each op timed on its own)
   attn_anchor_c32 the attention of the step at the pages' chunk of 32 tokens
   encode_to_host the first 8 layers of the request encoded in groups of 256 pages, each group's
                 anchor and residual segments copied to pinned host memory while the next group
@@ -24,10 +26,12 @@ Inputs are synthetic (Laplacian + per-channel offset + x100 outlier channels, se
 layer) and resident in HBM before the timed region.
 
 Prints one JSON line (rank 0, N = 1).  value = BF16-equivalent KV bytes processed per second
-over the whole step (2 B x elements of the four ops) in GB/s.  Every launch of the step is
-bracketed by HIP events on its own stream: each op reports its time (first launch start to
-last launch end, on the timing stream) and the mean duration of its launches; the roofline
-object takes the dominant kernel's algorithmic bytes per launch over that mean duration.
+over the whole step (2 B x elements of the four ops) in GB/s.  Each op of the step is
+bracketed by HIP events on the stream its kernels run on; its launches run back to back, so
+the op time over its launch count is the mean launch duration (the kernel trace of the same
+command agrees within the ~1 us between launches).  The roofline object takes the dominant
+kernel's algorithmic bytes per launch over that mean duration.  (Events around every launch
+were measured to add ~10 us between launches, and are not used.)
 """
 from __future__ import annotations
 
@@ -92,8 +96,8 @@ OP_KERNELS = {
     "encode": [("lynx::k_encode<%d, false>" % C, _CODEC_PAGES * KVH * 2 * 256)],
     "decode_anchor": [("lynx::k_decode<false, false>", _CODEC_PAGES * KVH * (P // 128) * 256)],
     "decode_full": [("lynx::k_decode<true, false>", _CODEC_PAGES * KVH * (P // 128) * 256)],
-    "attn_anchor": [("lynx::k_attn_anchor<%s>" % ("64, 1" if C % 64 == 0 else "64, 2" if P % 64 == 0 else "32, 1"), None),
-                    ("lynx::k_attn_combine", None)],
+    "attn_anchor": [("lynx::k_attn_anchor<%s, 8, 12>" % ("64, 1" if C % 64 == 0 else "64, 2" if P % 64 == 0 else "32, 1"),
+                     None), ("lynx::k_attn_combine", None)],
     "attn_verify": [("lynx::k_verify<%d>" % (1 if C % 64 == 0 else 2), None), ("lynx::k_verify_combine", None)],
     "copy": [("hbm_probe::k_probe_copy", None)],
 }
@@ -452,11 +456,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
-                    help="HIP streams the per-layer codec calls alternate over")
+    ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
+                    help="HIP streams the per-layer codec calls alternate over (with 2, launches of "
+                         "consecutive layers overlap and a launch's duration no longer measures it alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ops", default="encode,decode_anchor,decode_full,attn_anchor")
-    ap.add_argument("--next-ops", default="attn_anchor_c32,attn_verify,encode_to_host",
+    ap.add_argument("--next-ops", default="codec_two_streams,attn_anchor_c32,attn_verify,encode_to_host",
                     help="ops timed after the step, on their own (empty: none)")
     ap.add_argument("--counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="summarise two rocprofv3 --pmc runs of this benchmark into per-op HBM bytes")
@@ -550,11 +555,10 @@ def main():
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()               # default priority, like every stream here
     streams = [stream, side][:args.streams]
-    handles = [st.cuda_stream for st in streams]
 
-    def run_codec(op, evs=None):
-        """All per-layer calls of a codec op, round-robin over the streams; `evs` receives one
-        (start, end) event pair per launch, recorded on the launch's own stream."""
+    def run_codec(op, streams=streams):
+        """All per-layer calls of a codec op, round-robin over the streams."""
+        handles = [st.cuda_stream for st in streams]
         if len(streams) > 1:
             fork = torch.cuda.Event()
             fork.record(stream)
@@ -562,23 +566,16 @@ def main():
                 st.wait_event(fork)
         for i in range(CALLS):
             k = i % len(streams)
-            if evs is not None:
-                e0, e1 = evs[i]
-                e0.record(streams[k])
             codec.launch(op, i, handles[k])
-            if evs is not None:
-                e1.record(streams[k])
         for st in streams[1:]:
             join = torch.cuda.Event()
             join.record(st)
             stream.wait_event(join)
 
-    def run(op, evs=None):
+    def run(op):
         if op in ("encode", "decode_anchor", "decode_full"):
-            run_codec(op, evs)
+            run_codec(op)
             return
-        if evs is not None:
-            evs[0][0].record(stream)
         if op == "copy":
             probe_call(probe.hbm_probe_copy(copy_src.data_ptr(), copy_dst.data_ptr(), copy_src.numel(),
                                             torch.cuda.current_stream().cuda_stream))
@@ -602,39 +599,45 @@ def main():
                              out=o_ver, lse=lse_ver)
         else:
             raise ValueError(f"unknown op {op}")
-        if evs is not None:
-            evs[0][1].record(stream)
-
-    def new_events(op):
-        return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(op_launches(op))]
 
     for _ in range(args.warmup):
         for op in ops:
             run(op)
     torch.cuda.synchronize()
-    # op time: from an event before its first launch to one after its last (on the timing stream,
-    # which has joined the other stream); launch durations: events on each launch's own stream
+    # op time: from an event before its first launch to one after its last, on the stream the
+    # launches run on (with two streams: the timing stream, which the other one has joined)
     span = {op: [] for op in ops}
-    launches = {op: [] for op in ops}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s_ in range(args.steps):
         for op in ops:
             a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            evs = new_events(op)
             a_.record(stream)
-            run(op, evs)
+            run(op)
             b_.record(stream)
             span[op].append((a_, b_))
-            launches[op].append(evs)
         print(f"[bench] step {s_ + 1}/{args.steps} enqueued", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     # ops beyond the step, timed on their own with the same warmup and step counts
     nev = {}
-    for op in next_ops:
+    two = {}
+    if "codec_two_streams" in next_ops:
+        for op in ("encode", "decode_anchor", "decode_full"):
+            for _ in range(args.warmup):
+                run_codec(op, [stream, side])
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for a_, b_ in evs:
+                a_.record(stream)
+                run_codec(op, [stream, side])
+                b_.record(stream)
+            torch.cuda.synchronize()
+            two[op] = sum(a_.elapsed_time(b_) for a_, b_ in evs) / args.steps
+        print("[bench] codec_two_streams: " + ", ".join(f"{k} {v:.3f} ms" for k, v in two.items()), file=sys.stderr,
+              flush=True)
+    for op in [x for x in next_ops if x != "codec_two_streams"]:
         # the host-copy pipeline's first runs pay for first-touch of the pinned pages: warm longer
         for _ in range(max(args.warmup, 5) if op == "encode_to_host" else args.warmup):
             run(op)
@@ -666,8 +669,7 @@ def main():
            "copy_GBs": probe_gbs(lambda: probe_call(probe.hbm_probe_copy(copy_src.data_ptr(), copy_dst.data_ptr(), nb,
                                                                        sptr())), 2 * nb)}
     ms = {op: sum(a.elapsed_time(b) for a, b in span[op]) / args.steps for op in ops}
-    launch_ms = {op: sum(e0.elapsed_time(e1) for evs in launches[op] for e0, e1 in evs)
-                 / (args.steps * op_launches(op)) for op in ops}
+    launch_ms = {op: ms[op] / op_launches(op) for op in ops}   # back-to-back launches of one stream
     step_ms = wall * 1e3 / args.steps
     per_op = {}
     for op in ops:
@@ -692,7 +694,11 @@ def main():
         c1.record(stream)
         torch.cuda.synchronize()
         d2h_ms = c0.elapsed_time(c1) / args.steps
-    for op in next_ops:
+    if two:
+        next_rep["codec_two_streams"] = {
+            op: {"ms": round(t, 4), "frac_hbm_peak": round(alg_bytes_per_elem(op) * op_elems(op) * CALLS / t / 1e6
+                                                           / HBM_PEAK_GBS, 4)} for op, t in two.items()}
+    for op in [x for x in next_ops if x != "codec_two_streams"]:
         t = sum(a.elapsed_time(b) for a, b in nev[op]) / args.steps
         if op == "encode_to_host":
             nbytes = pipe_pages * (a_sz + r_sz)
@@ -730,7 +736,9 @@ def main():
                                f"alternating over {len(streams)} HIP stream(s)) + anchor-only decode attention "
                                f"({AB} seq x {AHQ} q / {AHKV} kv heads x {D}, {AT}-token context)",
                    "ops": per_op, "hbm_peak_GBs": HBM_PEAK_GBS, "hbm_measured": hbm,
-                   "beyond_step": {"workload": f"attn_verify: verification pass over full codes ({AB} seq x {AM} "
+                   "beyond_step": {"workload": "codec_two_streams: the step's codec ops with their per-layer "
+                                               "calls alternating over two streams (op time; launches overlap); "
+                                               f"attn_verify: verification pass over full codes ({AB} seq x {AM} "
                                                f"draft tokens x {AHQ} q / {AHKV} kv heads x {D}, {AT}-token "
                                                "context), bound: mfma; encode_to_host: the first "
                                                f"{PIPE_LAYERS} layers of the request encoded in groups of "
@@ -742,7 +750,8 @@ def main():
                             "with float32 accumulation"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(dom),
-                     "per": "launch: algorithmic bytes of one launch over the mean launch duration"},
+                     "per": "launch: algorithmic bytes of one launch over the mean launch duration "
+                            "(op time / launches, launches back to back on one stream)"},
         "cpu_baseline": cpu_rec,
     }
     print(json.dumps(rec), flush=True)

@@ -31,7 +31,7 @@ def test_counter_summary_calibrates_against_the_copy(tmp_path):
              (f"void lynx::k_encode<{bench.C}, false>(lynx::EncodeArgs)", enc_grid // 2): [7.0],   # setup encode, ignored
              ("void lynx::k_decode<false, false>(lynx::DecodeArgs)", bench.OP_KERNELS["decode_anchor"][0][1]): [10.0],
              ("void lynx::k_decode<true, false>(lynx::DecodeArgs)", bench.OP_KERNELS["decode_full"][0][1]): [20.0],
-             ("void lynx::k_attn_anchor<64, 1>(lynx::AttnArgs)", 4096): [30.0],
+             ("void lynx::k_attn_anchor<64, 1, 8, 12>(lynx::AttnArgs)", 4096): [30.0],
              ("lynx::k_attn_combine(lynx::AttnArgs)", 131072): [1.0],
              ("void lynx::k_verify<1>(lynx::(anonymous namespace)::VerifyArgs)", 131072): [40.0],
              ("lynx::k_verify_combine(lynx::(anonymous namespace)::VerifyArgs)", 8388608): [2.0]}
