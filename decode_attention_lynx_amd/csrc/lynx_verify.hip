@@ -22,16 +22,20 @@
 // own chunk).  Each tile is decoded once into LDS for all rows:
 //   * keys as K_hat * scale * log2(e) in float32, stored as BF16 high and low parts
 //     (K_hat ~ hi + lo to 16 bits), row-major [token][channel];
-//   * values as the raw table values L (float16), transposed [channel][token];
-// and the decode of tile i+1 runs in the same step as the products over tile i
-// (two LDS buffers, one barrier per tile), so the decode's vector work overlaps
-// the matrix work.  Per tile and wave:
+//   * values as V_hat * 2^-E in float16 (E a power-of-two range exponent, 0 for ordinary
+//     KV), transposed [channel][token] in the k order of the value MFMA's operand;
+// the decode of tile i+1 runs in the same step as the products over tile i (two LDS
+// buffers, one barrier per tile).  Per tile and wave:
 //   scores  S^T[token, row] = K_hi q + K_lo q on MFMA 16x16x32 bf16 (the BF16 query
 //           is exact in this format); each key fragment read feeds both groups;
 //   online softmax in base 2 per row, the running maximum moved only when a tile
 //           raises it by more than 8 (probabilities stay below 2^8, exact in range);
-//   values  T^T[d, row] = sum_t L_V[d, t] p[t, row] on MFMA 16x16x32 f16, and
-//           O += A_V T + B_V sum(p) (the value map applied after the product).
+//   values  O^T[d, row] += sum_t V_hat[d, t] p[t, row] on MFMA 16x16x32 f16, o held in
+//           units of 2^E.
+// LDS traffic bounds this loop: per 64-token tile a workgroup reads 48 KB of key and
+// value operands per wave (384 KB) and moves ~176 KB in the decode, against ~128 B per
+// clock; the layout keeps every product operand one 16-byte read and the key buffers
+// within the 64 KB reach of an LDS instruction's immediate offset.
 // Each wave writes a partial (m, l, o[128]) per row and split; k_verify_combine
 // merges the splits with the log-sum-exp rule and returns O and the natural-log
 // LSE of each row's scaled scores.
@@ -60,7 +64,7 @@ constexpr int kVGroups = 2;                // MFMA column groups (16 rows each) 
 constexpr int kVRows = 16 * kVGroups * kVWaves;   // query rows per workgroup (256)
 static_assert(kVThreads == 512, "the tile decode maps 512 threads onto 64 tokens x 128 channels");
 constexpr int kVTile = 64;                 // context tokens per step
-constexpr int kLutCopies = 16;             // copies of each table entry (lane l reads copy l % 16)
+constexpr int kLutCopies = 32;             // copies of each table entry (lane l reads copy l % 32)
 constexpr int kRec = kHeadDim + 4;         // floats per partial record (o 16-byte aligned)
 constexpr int kVWorkgroups = 256;          // workgroups the context splits aim for (one per CU)
 constexpr float kLazyMax = 8.0f;           // the running maximum moves only beyond this (base 2)
@@ -112,7 +116,7 @@ __device__ __forceinline__ uint32_t bf16x2(float a, float b) {
 
 // One tile's raw codes for this thread.
 struct CodeIn {
-  uint2 ka, kr;          // key codes: token tid/8, channels 16*(tid%8) .. +15
+  uint32_t ka[2], kr[2]; // key codes: tokens tid/16 and tid/16 + 32, channels 8*(tid%16) .. +7
   uint32_t va[2], vr[2]; // value codes: tokens 2*(tid%32), +1; channels 8*(tid/32) .. +7
 };
 
@@ -140,12 +144,13 @@ __device__ __forceinline__ TileAddr tile_addr(const VerifyArgs& a, int b, int kv
 
 __device__ __forceinline__ void load_codes(const VerifyArgs& a, int b, int kvh, int tile, int tid, CodeIn& in) {
   const TileAddr ta = tile_addr(a, b, kvh, tile);
-  {
-    // channels 16*(tid%8) .. +15: code block (tid%8)/4, bytes 8*(tid%4) .. +7 of its row
-    const size_t off = ta.row0 + (size_t)((tid & 7) >> 2) * a.P * kCodeRow + (size_t)(tid >> 3) * kCodeRow +
-                       8 * (tid & 3);
-    in.ka = *reinterpret_cast<const uint2*>(a.kanc + ta.seg * a.anc_seg + off);
-    in.kr = *reinterpret_cast<const uint2*>(a.kres + ta.seg * a.codes + off);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    // channels 8*(tid%16) .. +7: code block (tid%16)/8, dword tid%8 of the row of token tid/16 + 32r
+    const size_t off = ta.row0 + (size_t)((tid & 15) >> 3) * a.P * kCodeRow + (size_t)((tid >> 4) + 32 * r) * kCodeRow +
+                       4 * (tid & 7);
+    in.ka[r] = *reinterpret_cast<const uint32_t*>(a.kanc + ta.seg * a.anc_seg + off);
+    in.kr[r] = *reinterpret_cast<const uint32_t*>(a.kres + ta.seg * a.codes + off);
   }
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -190,14 +195,26 @@ __device__ __forceinline__ float2 affine(float gmin, float gscale, float mu, flo
 // CPT = chunks per 64-token tile (1 for a chunk of 64 or more, 2 / 4 for chunks of 32 / 16)
 template <int CPT>
 struct alignas(16) VerifyLds {
-  float lut[256 * kLutCopies];             // float32 table, entry e copy c at e*16 + c
+  // the key parts first: the products' reads of both buffers then sit within the 64 KB reach of
+  // an LDS instruction's immediate offset
   uint32_t kh[2][kVTile * 64];             // K_hat BF16 high parts, [token][channel pair], per buffer
   uint32_t kl[2][kVTile * 64];             // K_hat BF16 low parts
-  uint32_t lv[2][kHeadDim * (kVTile / 2)]; // V_hat * 2^-E as float16, [channel][token pair]
+  uint32_t lv[2][kHeadDim * (kVTile / 2)]; // V_hat * 2^-E as float16, [channel][token slot]
+  float lut[256 * kLutCopies];             // float32 table, entry e copy c at e*32 + c
   float2 abk[2][CPT][kHeadDim + kHeadDim / 16];  // (A_K, B_K) of channel c at c + c/16, scaled
   float2 abv[2][CPT][kHeadDim];            // (A_V, B_V) 2^-E per channel
   int vexp[2];                             // E of the tile in each slot
 };
+
+// Value rows: row d holds the 64 tokens of channel d in eight 16-byte slots.  Slot 4ks + g holds
+// tokens 32ks + 4g + 0..3 then 32ks + 16 + 4g + 0..3, the k order of one lane's f16 MFMA operand
+// (the layout of the probabilities), so that the operand is one 16-byte read; slot s sits at
+// s ^ ((d >> 1) & 7), which puts the 16 rows one read spans on distinct banks.  Word of the
+// token pair 2tp, 2tp + 1 of channel d:
+__device__ __forceinline__ int lv_word(int d, int tp) {
+  const int slot = 4 * (tp >> 4) + ((tp >> 1) & 3);
+  return d * (kVTile / 2) + 4 * (slot ^ ((d >> 1) & 7)) + 2 * ((tp >> 3) & 1) + (tp & 1);
+}
 
 // Smallest e >= 0 with (|A| + |B|) 2^-e <= kF16Safe: a bound on |V_hat| 2^-e over the chunk,
 // since |L| <= 1.
@@ -255,41 +272,38 @@ __device__ __forceinline__ void write_maps(VerifyLds<CPT>& L, int buf, const Met
 template <int CPT>
 __device__ __forceinline__ void decode_tile(VerifyLds<CPT>& L, int buf, const CodeIn& in, int tid, int lcopy) {
   {
-    // keys: token t = tid/8, channels 16*(tid%8) + k, K_hat = A*L + B split into BF16 hi + lo;
-    // row t holds 16 columns of 16 B (8 channels each), column c16 at c16 ^ (t & 15)
-    const int t = tid >> 3, e8 = tid & 7;
-    const float2* abk = L.abk[buf][CPT == 1 ? 0 : t / (kVTile / CPT)];   // wave-uniform chunk
-    const uint32_t aw[2] = {in.ka.x, in.ka.y}, rw[2] = {in.kr.x, in.kr.y};
-    uint32_t hi[8], lo[8];
+    // keys: tokens tid/16 and tid/16 + 32, channels 8*(tid%16) + k, K_hat = A*L + B split into
+    // BF16 hi + lo; row t holds 16 columns of 16 B (8 channels each), column c16 at c16 ^ (t & 15),
+    // so the 16 lanes of one token write its whole row.  A thread reads the maps of its 8 channels
+    // once for both tokens (twice when they fall in different chunks).
+    const int cu = tid & 15, t0 = tid >> 4;
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      // byte k of ev / od: full code of channel 2k / 2k+1 of this word
-      const uint32_t ev = (aw[w] & 0x0F0F0F0Fu) | ((rw[w] << 4) & 0xF0F0F0F0u);
-      const uint32_t od = ((aw[w] >> 4) & 0x0F0F0F0Fu) | (rw[w] & 0xF0F0F0F0u);
+    for (int r = 0; r < 2; ++r) {
+      const int t = t0 + 32 * r;
+      // the padding spreads the 16 channel units' maps over distinct banks
+      const float2* abk = L.abk[buf][CPT == 1 ? 0 : t / (kVTile / CPT)];
+      // byte k of ev / od: full code of channel 8cu + 2k / 2k+1
+      const uint32_t ev = (in.ka[r] & 0x0F0F0F0Fu) | ((in.kr[r] << 4) & 0xF0F0F0F0u);
+      const uint32_t od = ((in.ka[r] >> 4) & 0x0F0F0F0Fu) | (in.kr[r] & 0xF0F0F0F0u);
+      uint32_t hi[4], lo[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int ch = 16 * e8 + 8 * w + 2 * k;
-        // the 8 threads of a token read 8 channels 16 apart: the padding puts them in 8 banks
-        const float2 ab0 = abk[ch + e8], ab1 = abk[ch + 1 + e8];
+        const int ch = 8 * cu + 2 * k;
+        const float2 ab0 = abk[ch + (ch >> 4)], ab1 = abk[ch + 1 + (ch >> 4)];
         const float x0 = fmaf(ab0.x, L.lut[((ev >> (8 * k)) & 0xFFu) * kLutCopies + lcopy], ab0.y);
         const float x1 = fmaf(ab1.x, L.lut[((od >> (8 * k)) & 0xFFu) * kLutCopies + lcopy], ab1.y);
         const uint32_t h = bf16x2(x0, x1);
-        hi[4 * w + k] = h;
-        lo[4 * w + k] = bf16x2(x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xFFFF0000u));
+        hi[k] = h;
+        lo[k] = bf16x2(x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xFFFF0000u));
       }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c16 = (2 * e8 + h) ^ (t & 15);
-      *reinterpret_cast<uint4*>(&L.kh[buf][t * 64 + 4 * c16]) = make_uint4(hi[4 * h], hi[4 * h + 1], hi[4 * h + 2], hi[4 * h + 3]);
-      *reinterpret_cast<uint4*>(&L.kl[buf][t * 64 + 4 * c16]) = make_uint4(lo[4 * h], lo[4 * h + 1], lo[4 * h + 2], lo[4 * h + 3]);
+      const int c16 = cu ^ (t & 15);
+      *reinterpret_cast<uint4*>(&L.kh[buf][t * 64 + 4 * c16]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(&L.kl[buf][t * 64 + 4 * c16]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
   }
   {
     // values: channels 8*(tid/32) + j, tokens 2*(tid%32), +1: V_hat = A*L + B (times 2^-E)
-    // as float16 pairs, transposed.  Row d holds 16 units of 8 B (4 tokens); unit u sits at
-    // u ^ (d & 15).  A wave's 64 lanes write 2 channels x 32 token pairs: at most 2 lanes
-    // per bank.
+    // as float16 pairs, transposed into the slots of lv_word.
     const int c8 = tid >> 5, tq = tid & 31;
     const uint32_t ev0 = (in.va[0] & 0x0F0F0F0Fu) | ((in.vr[0] << 4) & 0xF0F0F0F0u);
     const uint32_t od0 = ((in.va[0] >> 4) & 0x0F0F0F0Fu) | (in.vr[0] & 0xF0F0F0F0u);
@@ -303,8 +317,7 @@ __device__ __forceinline__ void decode_tile(VerifyLds<CPT>& L, int buf, const Co
       const int d = 8 * c8 + j;
       const float2 ab = L.abv[buf][CPT == 1 ? 0 : tq / (kVTile / 2 / CPT)][d];   // the tokens' chunk
       const vf2 x = {fmaf(ab.x, L.lut[i0 * kLutCopies + lcopy], ab.y), fmaf(ab.x, L.lut[i1 * kLutCopies + lcopy], ab.y)};
-      const int unit = (tq >> 1) ^ (d & 15);
-      L.lv[buf][d * (kVTile / 2) + 2 * unit + (tq & 1)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, vh2));
+      L.lv[buf][lv_word(d, tq)] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, vh2));
     }
   }
 }
@@ -426,6 +439,14 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
             if (tok0 + 16 * (e >> 2) + 4 * g + (e & 3) >= seq_len) s[gq][e] = -INFINITY;
       }
 
+      // ---- the value operands of the tile, read ahead of the softmax (which hides their latency):
+      //      lane (n, g) of step ks takes channel 16j + n, slot 4ks + g
+      auto vread = [&](int j, int ks) {
+        const int d = 16 * j + n;
+        const uint4 w = *reinterpret_cast<const uint4*>(&L.lv[par][d * (kVTile / 2) + 4 * ((4 * ks + g) ^ ((d >> 1) & 7))]);
+        return vu4{w.x, w.y, w.z, w.w};
+      };
+
       // ---- online softmax: p = 2^(s - m_run), the maximum moved (and o, l rescaled) only
       //      where the tile exceeds it by more than kLazyMax, so p < 2^kLazyMax
       vh8 pt[kVGroups][2];
@@ -463,17 +484,14 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
       // (the layout of the probabilities); the values are read in the same order.
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int d = 16 * j + n;
+        const vu4 v0 = vread(j, 0), v1 = vread(j, 1);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int u0 = (8 * ks + g) ^ n, u1 = (8 * ks + 4 + g) ^ n;     // (d & 15) == n
-          const uint2 w0 = *reinterpret_cast<const uint2*>(&L.lv[par][d * (kVTile / 2) + 2 * u0]);
-          const uint2 w1 = *reinterpret_cast<const uint2*>(&L.lv[par][d * (kVTile / 2) + 2 * u1]);
-          const vu4 va4 = {w0.x, w0.y, w1.x, w1.y};
+        for (int gq = 0; gq < kVGroups; ++gq)
+          o_acc[gq][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(vh8, v0), pt[gq][0], o_acc[gq][j], 0, 0, 0);
 #pragma unroll
-          for (int gq = 0; gq < kVGroups; ++gq)
-            o_acc[gq][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(vh8, va4), pt[gq][ks], o_acc[gq][j], 0, 0, 0);
-        }
+        for (int gq = 0; gq < kVGroups; ++gq)
+          o_acc[gq][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(vh8, v1), pt[gq][1], o_acc[gq][j], 0, 0, 0);
+        if (j % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // bound the value operands held in registers
       }
     }
 
