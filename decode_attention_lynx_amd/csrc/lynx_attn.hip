@@ -16,18 +16,20 @@
 // a dense contraction over the raw nibble table values, which runs on MFMA.
 // Likewise sum_t p_t v_hat[t,d] = A_V[c,d] sum_t p_t L[n_td] + B_V[c,d] sum_t p_t.
 //
-// Decomposition: one workgroup (12 waves) per (sequence, kv head, context split);
-// each wave walks 64-token tiles (one tile lies inside one chunk because the
-// chunk is a multiple of 64) with an online softmax, the 12 waves merge in LDS
-// and write one partial (m, l, o[128]) per query head; k_attn_combine merges the
-// splits with the log-sum-exp rule.
+// Decomposition: one workgroup (12 or 8 waves) per (sequence, kv head, context split);
+// each wave walks tiles of 64 tokens (32 for pages of an odd number of 32-token chunks, or
+// chunks of 8) with an online softmax; a tile holds one chunk of 64 or more, or 2 or 4
+// whole chunks, each folded with its own map.  The waves merge in LDS and write one partial
+// (m, l, o[128]) per query head; k_attn_combine merges the splits with the log-sum-exp rule.
 //
 // MFMA v_mfma_f32_16x16x32_f16 (A 16x32, B 32x16, C 16x16; lane l supplies row /
 // column l % 16 and the k-block l / 16; C rows 4*(l/16)..+3, column l % 16):
-//   scores  S^T[token, col] = sum_d L[token, d] * qt[d, col]: A = nibble-table
-//           values of 16 tokens, B = the folded query, columns 0..7 = the float16
-//           high part of q*A per head, columns 8..15 = the float16 remainder, so
-//           one MFMA carries a ~22-bit query; the two halves are added after.
+//   scores  S^T[token, col] = sum_d L[token, d] * qt[d, col]: A = nibble-table values of
+//           16 tokens, B = the folded query in float16 hi + lo parts (~22 bits): for groups
+//           of up to 8 heads columns 0..7 hold the high parts and 8..15 the remainders (one
+//           MFMA, the halves added after); for groups of 9..16 heads column h is head h and
+//           the two parts take two MFMAs.  The key map carries a per-tile power-of-two
+//           exponent that keeps every folded |q| inside float16, undone in float32.
 //   values  O^T[d, col] += sum_t L_V[t, d] * p[t, col]: A = table values of 16
 //           channels over 32 tokens, B = float16 probabilities.
 #include "../../include/lynx.h"
