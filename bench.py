@@ -19,6 +19,9 @@ Timed after the step, on its own (not part of `value`):
   codec_two_streams the step's encode, decode_anchor and decode_full with their per-layer calls
                 alternating over two HIP streams (each op timed on its own)
   attn_anchor_c32 the attention of the step at the pages' chunk of 32 tokens
+  attn_anchor_paged, attn_verify_paged  the anchor attention and the verification pass through
+                a block table: each sequence's pages scattered over the pool of the same
+                segments by a seeded permutation, full lengths (to compare with the contiguous form)
   encode_to_host the first 8 layers of the request encoded in groups of 256 pages, each group's
                 anchor and residual segments copied to pinned host memory while the next group
                 is encoded (two streams), against a plain device-to-host copy of the same bytes
@@ -68,12 +71,13 @@ def alg_bytes_per_elem(op: str) -> float:
     meta = 8.0 / C + 8.0 / P
     return {"encode": 2.0 + 1.0 + meta, "decode_anchor": 0.5 + meta + 2.0, "decode_full": 1.0 + meta + 2.0,
             "attn_anchor": 0.5 + meta, "attn_verify": 1.0 + meta, "copy": 4.0,
-            "attn_anchor_c32": 0.5 + 8.0 / 32 + 8.0 / P}[op]
+            "attn_anchor_c32": 0.5 + 8.0 / 32 + 8.0 / P, "attn_anchor_paged": 0.5 + meta,
+            "attn_verify_paged": 1.0 + meta}[op]
 
 
 def op_flops(op: str) -> float:
     """Algorithmic flops of one launch: 2 x (q.k) + 2 x (p.v) per (query, head, context token, channel)."""
-    return {"attn_verify": 4.0 * AB * AM * AHQ * AT * D}.get(op, 0.0)
+    return {"attn_verify": 4.0 * AB * AM * AHQ * AT * D, "attn_verify_paged": 4.0 * AB * AM * AHQ * AT * D}.get(op, 0.0)
 
 
 def op_elems(op: str) -> int:
@@ -82,6 +86,7 @@ def op_elems(op: str) -> int:
     codec = LAYERS_PER_CALL * 2 * TOKENS * KVH * D
     return {"encode": codec, "decode_anchor": codec, "decode_full": codec, "attn_anchor": 2 * AB * AT * AHKV * D,
             "attn_verify": 2 * AB * AT * AHKV * D, "attn_anchor_c32": 2 * AB * AT * AHKV * D,
+            "attn_anchor_paged": 2 * AB * AT * AHKV * D, "attn_verify_paged": 2 * AB * AT * AHKV * D,
             "copy": (1 << 30) // 2}[op]
 
 
@@ -461,7 +466,8 @@ def main():
                          "consecutive layers overlap and a launch's duration no longer measures it alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ops", default="encode,decode_anchor,decode_full,attn_anchor")
-    ap.add_argument("--next-ops", default="codec_two_streams,attn_anchor_c32,attn_verify,encode_to_host",
+    ap.add_argument("--next-ops", default="codec_two_streams,attn_anchor_c32,attn_anchor_paged,attn_verify,"
+                                          "attn_verify_paged,encode_to_host",
                     help="ops timed after the step, on their own (empty: none)")
     ap.add_argument("--counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="summarise two rocprofv3 --pmc runs of this benchmark into per-op HBM bytes")
@@ -522,7 +528,8 @@ def main():
     for kv_idx in (0, 1):
         for b in range(AB):
             synth.make_kv_torch(AT, AHKV, D, seed=1, layer=b, kv_idx=kv_idx, out=akv[b * AT:(b + 1) * AT])
-        att[kv_idx], att_res[kv_idx] = lynx.encode(akv, P, C, ALPHA, residual="attn_verify" in next_ops + ops)
+        att[kv_idx], att_res[kv_idx] = lynx.encode(akv, P, C, ALPHA, residual=any(
+            o_.startswith("attn_verify") for o_ in next_ops + ops))
         if "attn_anchor_c32" in next_ops + ops:      # the same KV at the pages' chunk of 32 tokens
             att32[kv_idx], _ = lynx.encode(akv, P, 32, ALPHA, residual=False)
     del akv
@@ -530,12 +537,27 @@ def main():
     ws = torch.empty(lynx.attn_workspace_bytes(AB, AT, AHQ, AHKV, D, P, C), dtype=torch.uint8, device=dev)
     o_att = torch.empty((AB, AHQ, D), dtype=torch.bfloat16, device=dev)
     ws32 = torch.empty(lynx.attn_workspace_bytes(AB, AT, AHQ, AHKV, D, P, 32), dtype=torch.uint8, device=dev)
-    if "attn_verify" in next_ops + ops:
+    if any(o_.startswith("attn_verify") for o_ in next_ops + ops):
         qv = synth.make_q_torch(AB * AM, AHQ, D, seed=2).view(AB, AM, AHQ, D)
         ws_v = torch.empty(lynx.attn_verify_workspace_bytes(AB, AM, AT, AHQ, AHKV, D, P, C), dtype=torch.uint8,
                            device=dev)
         o_ver = torch.empty((AB, AM, AHQ, D), dtype=torch.bfloat16, device=dev)
         lse_ver = torch.empty((AB, AM, AHQ), dtype=torch.float32, device=dev)
+    if any(o_.endswith("_paged") for o_ in next_ops + ops):
+        # block table: sequence b's page p is pool segment perm[b * npages + p] (a seeded permutation
+        # of the same segments the contiguous form reads), every sequence at its full length
+        import numpy as np
+        npg = AT // P
+        perm = torch.from_numpy(np.random.default_rng(7).permutation(AB * npg).astype(np.int32))
+        block_table = perm.view(AB, npg).contiguous().to(dev)
+        seq_lens = torch.full((AB,), AT, dtype=torch.int32, device=dev)
+        # the contiguous form reads segment b * npages + p: the pools hold the same segments at the
+        # permuted positions, so both forms see the same sequences
+        pool_k = torch.empty_like(att[0]); pool_k[perm.long().to(dev)] = att[0]
+        pool_v = torch.empty_like(att[1]); pool_v[perm.long().to(dev)] = att[1]
+        if any(o_.startswith("attn_verify") for o_ in next_ops + ops):
+            pool_kr = torch.empty_like(att_res[0]); pool_kr[perm.long().to(dev)] = att_res[0]
+            pool_vr = torch.empty_like(att_res[1]); pool_vr[perm.long().to(dev)] = att_res[1]
     pipe_pages = PIPE_LAYERS * 2 * TOKENS // P
     if "encode_to_host" in next_ops + ops:
         anchor_h = torch.empty((pipe_pages, a_sz), dtype=torch.uint8, pin_memory=True)
@@ -597,6 +619,12 @@ def main():
         elif op == "attn_verify":
             lynx.attn_verify(qv, att[0], att_res[0], att[1], att_res[1], AT, AHKV, P, C, ALPHA, workspace=ws_v,
                              out=o_ver, lse=lse_ver)
+        elif op == "attn_anchor_paged":
+            lynx.attn_anchor_paged(q, pool_k, pool_v, block_table, seq_lens, AHKV, P, C, ALPHA, workspace=ws,
+                                   out=o_att)
+        elif op == "attn_verify_paged":
+            lynx.attn_verify_paged(qv, pool_k, pool_kr, pool_v, pool_vr, block_table, seq_lens, AHKV, P, C, ALPHA,
+                                   workspace=ws_v, out=o_ver, lse=lse_ver)
         else:
             raise ValueError(f"unknown op {op}")
 
@@ -708,11 +736,11 @@ def main():
                             "d2h_copy_GBs": round(nbytes / d2h_ms / 1e6, 2),
                             "copy_over_pipeline": round(d2h_ms / t, 4)}
             continue
-        if op == "attn_anchor_c32":
+        if op in ("attn_anchor_c32", "attn_anchor_paged"):
             ab = alg_bytes_per_elem(op) * op_elems(op)
             next_rep[op] = {"ms": round(t, 4), "alg_GBs": round(ab / t / 1e6, 1),
-                            "frac_hbm_peak": round(ab / t / 1e6 / HBM_PEAK_GBS, 4), "chunk": 32,
-                            "alg_bytes_per_launch": int(ab)}
+                            "frac_hbm_peak": round(ab / t / 1e6 / HBM_PEAK_GBS, 4),
+                            "chunk": 32 if op == "attn_anchor_c32" else C, "alg_bytes_per_launch": int(ab)}
             continue
         fl = op_flops(op)
         next_rep[op] = {"ms": round(t, 4), "TFLOPs": round(fl / t / 1e9, 1),
@@ -744,7 +772,10 @@ def main():
                                                f"{PIPE_LAYERS} layers of the request encoded in groups of "
                                                f"{PIPE_GROUP} pages and copied to pinned host memory, bound: "
                                                "the device-to-host link; attn_anchor_c32: the anchor attention "
-                                               "of the step at a chunk of 32 tokens, bound: hbm",
+                                               "of the step at a chunk of 32 tokens, bound: hbm; "
+                                               "attn_anchor_paged / attn_verify_paged: the same attentions "
+                                               "through a block table (pages scattered over the pool by a "
+                                               "seeded permutation, full lengths)",
                                    "ops": next_rep},
                    "arith": "float32 codec (float64 statistics and boundary cases), float16 MFMA attention "
                             "with float32 accumulation"},

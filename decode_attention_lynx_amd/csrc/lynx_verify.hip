@@ -126,7 +126,15 @@ struct TileAddr {
   int kc;         // chunk of the tile within its page
 };
 
-__device__ __forceinline__ TileAddr tile_addr(const VerifyArgs& a, int b, int kvh, int tile) {
+// Block-table entry of `tile`'s page (paged form; 0 otherwise), fetched a step ahead of its use
+// as a vector load: fetched at its use, the wait for it would also wait for every load issued
+// before it (the loads of a wave complete in order).
+__device__ __forceinline__ int fetch_segment(const VerifyArgs& a, int b, int tile) {
+  if (a.block_table == nullptr) return 0;
+  return __builtin_nontemporal_load(a.block_table + (size_t)b * a.max_pages + tile * kVTile / a.P);
+}
+
+__device__ __forceinline__ TileAddr tile_addr(const VerifyArgs& a, int b, int kvh, int tile, int fetched) {
   const int tok = tile * kVTile;
   const int page = tok / a.P;
   const int tin = tok - page * a.P;
@@ -134,16 +142,16 @@ __device__ __forceinline__ TileAddr tile_addr(const VerifyArgs& a, int b, int kv
   if (a.block_table == nullptr) {
     t.seg = (size_t)b * a.npages + page;
   } else {
-    const int sg = a.block_table[(size_t)b * a.max_pages + page];
-    t.seg = (size_t)min(max(sg, 0), a.n_pool - 1);
+    t.seg = (size_t)min(max(__builtin_amdgcn_readfirstlane(fetched), 0), a.n_pool - 1);
   }
   t.row0 = code_offset(a.P, kvh, 0, tin);
   t.kc = tin / a.C;
   return t;
 }
 
-__device__ __forceinline__ void load_codes(const VerifyArgs& a, int b, int kvh, int tile, int tid, CodeIn& in) {
-  const TileAddr ta = tile_addr(a, b, kvh, tile);
+__device__ __forceinline__ void load_codes(const VerifyArgs& a, int b, int kvh, int tile, int fetched, int tid,
+                                           CodeIn& in) {
+  const TileAddr ta = tile_addr(a, b, kvh, tile, fetched);
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     // channels 8*(tid%16) .. +7: code block (tid%16)/8, dword tid%8 of the row of token tid/16 + 32r
@@ -170,8 +178,9 @@ struct MetaIn {
 };
 
 template <int CPT>
-__device__ __forceinline__ MetaIn<CPT> load_meta(const VerifyArgs& a, int b, int kvh, int tile, int tid) {
-  const TileAddr ta = tile_addr(a, b, kvh, tile);
+__device__ __forceinline__ MetaIn<CPT> load_meta(const VerifyArgs& a, int b, int kvh, int tile, int fetched,
+                                                 int tid) {
+  const TileAddr ta = tile_addr(a, b, kvh, tile, fetched);
   const int c = 2 * (tid & 63);
   const uint8_t* seg = (tid < 64 ? a.kanc : a.vanc) + ta.seg * a.anc_seg + a.codes;
   const float* meta = reinterpret_cast<const float*>(seg) + kvh * kHeadDim + c;
@@ -384,24 +393,27 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
   const bool mapper = wave < 2;          // wave-uniform
   MetaIn<CPT> meta;
   int E_map = 0;
+  const int f0 = fetch_segment(a, b, t_begin), f1 = fetch_segment(a, b, min(t_begin + 1, t_last));
+  int f_cur = fetch_segment(a, b, min(t_begin + 2, t_last));   // the tile whose codes step i loads: i + 2
   if (mapper) {
-    write_maps(L, 0, load_meta<CPT>(a, b, kvh, t_begin, tid), a.qscale, tid, E_map);
-    write_maps(L, 1, load_meta<CPT>(a, b, kvh, min(t_begin + 1, t_last), tid), a.qscale, tid, E_map);
-    meta = load_meta<CPT>(a, b, kvh, min(t_begin + 2, t_last), tid);
+    write_maps(L, 0, load_meta<CPT>(a, b, kvh, t_begin, f0, tid), a.qscale, tid, E_map);
+    write_maps(L, 1, load_meta<CPT>(a, b, kvh, min(t_begin + 1, t_last), f1, tid), a.qscale, tid, E_map);
+    meta = load_meta<CPT>(a, b, kvh, min(t_begin + 2, t_last), f_cur, tid);
   }
   CodeIn cin;
-  load_codes(a, b, kvh, t_begin, tid, cin);
+  load_codes(a, b, kvh, t_begin, f0, tid, cin);
   __syncthreads();                       // the table and the maps of tiles 0 and 1 are in LDS
   E_acc = L.vexp[0];
   decode_tile(L, 0, cin, tid, lcopy);
-  load_codes(a, b, kvh, min(t_begin + 1, t_last), tid, cin);
+  load_codes(a, b, kvh, min(t_begin + 1, t_last), f1, tid, cin);
 
   // step i (buffer par = i & 1): decode tile i+1 into the other buffer, products over tile i,
   // maps of tile i+2 into slot par
   auto step = [&](int i, int par) {
     __syncthreads();   // buffer par is decoded; buffer 1-par and maps slot par are free
+    const int f_next = fetch_segment(a, b, min(t_begin + i + 3, t_last));
     decode_tile(L, 1 - par, cin, tid, lcopy);
-    load_codes(a, b, kvh, min(t_begin + i + 2, t_last), tid, cin);
+    load_codes(a, b, kvh, min(t_begin + i + 2, t_last), f_cur, tid, cin);
 
     if (wave_live) {
       // ---- scores minus m_run, S^T[token, row] of both groups: tokens 16mb + 4g + e, row n
@@ -507,8 +519,9 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
     // ---- maps of tile i+2 into slot par (read by the decode in step i+1)
     if (mapper) {
       write_maps(L, par, meta, a.qscale, tid, E_map);
-      meta = load_meta<CPT>(a, b, kvh, min(t_begin + i + 3, t_last), tid);
+      meta = load_meta<CPT>(a, b, kvh, min(t_begin + i + 3, t_last), f_next, tid);
     }
+    f_cur = f_next;
   };
 
   for (int i = 0; i < nt; i += 2) {
