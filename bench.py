@@ -666,8 +666,12 @@ def main():
         print("[bench] codec_two_streams: " + ", ".join(f"{k} {v:.3f} ms" for k, v in two.items()), file=sys.stderr,
               flush=True)
     for op in [x for x in next_ops if x != "codec_two_streams"]:
-        # the host-copy pipeline's first runs pay for first-touch of the pinned pages: warm longer
-        for _ in range(max(args.warmup, 5) if op == "encode_to_host" else args.warmup):
+        # the host-copy pipeline's first runs pay for first-touch of the pinned pages, and the
+        # compute-bound verification pass runs ~10% slower over its first ~10 launches after the
+        # memory-bound ops (the clocks settle): warm those longer
+        warm = max(args.warmup, 5) if op == "encode_to_host" else \
+            max(args.warmup, 10) if op.startswith("attn_verify") else args.warmup
+        for _ in range(warm):
             run(op)
         nev[op] = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(args.steps)]
