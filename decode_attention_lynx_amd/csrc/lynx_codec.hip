@@ -181,43 +181,45 @@ __device__ __forceinline__ void load_tile(uint4 (&v)[kTokPerThread], const uint1
 // The same BF16 -> float unpacking as bf16_lo / bf16_hi, written as a byte permutation.
 // Passes that unpack the same words a second time use this form, so the compiler
 // recomputes the floats there instead of keeping the first pass's copies live.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo_p(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x01000c0cu)); }
 __device__ __forceinline__ float bf16_hi_p(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x03020c0cu)); }
 
 // Per-thread statistics of its 8 tokens x 8 channels, stored to the LDS partial rows:
 // float64 sum, min, max (Stage 2 needs all three; Stage 1 needs min and max).
 template <int C>
-__device__ __forceinline__ void store_partials(EncodeShared<C>& sh, const uint4 (&v)[kTokPerThread], bool act,
-                                               int tg, int dg) {
+__device__ __forceinline__ void store_partials(EncodeShared<C>& sh, const uint4 (&v)[kTokPerThread],
+                                               float (&xs)[kTokPerThread][8], bool act, int tg, int dg) {
   double sm[8];
   float cmn[8], cmx[8];
   if (act) {
-    // token 0 starts the sums and extremes, tokens 1..7 accumulate: no additions of 0 and
-    // no infinities to load on the common path
-    {
-      const uint32_t q[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+    // The BF16 values are unpacked once, into the float32 registers that the encode reads
+    // too, as a BF16 -> float conversion (the same shift and mask), which the compiler knows
+    // yields canonical floats: the minima and maxima below, in the same block, then need no
+    // canonicalising instruction per element.
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float lo = bf16_lo_p(q[k]), hi = bf16_hi_p(q[k]);
-        sm[2 * k] = (double)lo;
-        sm[2 * k + 1] = (double)hi;
-        cmn[2 * k] = cmx[2 * k] = lo;
-        cmn[2 * k + 1] = cmx[2 * k + 1] = hi;
-      }
-    }
-#pragma unroll
-    for (int i = 1; i < kTokPerThread; ++i) {
+    for (int i = 0; i < kTokPerThread; ++i) {
       const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float lo = bf16_lo_p(q[k]), hi = bf16_hi_p(q[k]);
-        sm[2 * k] += (double)lo;
-        sm[2 * k + 1] += (double)hi;
-        cmn[2 * k] = fminf(cmn[2 * k], lo);
-        cmx[2 * k] = fmaxf(cmx[2 * k], lo);
-        cmn[2 * k + 1] = fminf(cmn[2 * k + 1], hi);
-        cmx[2 * k + 1] = fmaxf(cmx[2 * k + 1], hi);
+        const f32x2_t f = __builtin_convertvector(__builtin_bit_cast(bf16x2_t, q[k]), f32x2_t);
+        xs[i][2 * k] = f.x;
+        xs[i][2 * k + 1] = f.y;
       }
+    }
+    // token 0 starts the sums, tokens 1..7 accumulate (no additions of 0); the extremes of
+    // the 8 tokens as trees of minima and maxima
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sm[j] = (double)xs[0][j];
+#pragma unroll
+      for (int i = 1; i < kTokPerThread; ++i) sm[j] += (double)xs[i][j];
+      // nested as three-operand minima / maxima: four instructions for 8 values
+      cmn[j] = fminf(fminf(fminf(fminf(xs[0][j], xs[1][j]), xs[2][j]), fminf(fminf(xs[3][j], xs[4][j]), xs[5][j])),
+                     fminf(xs[6][j], xs[7][j]));
+      cmx[j] = fmaxf(fmaxf(fmaxf(fmaxf(xs[0][j], xs[1][j]), xs[2][j]), fmaxf(fmaxf(xs[3][j], xs[4][j]), xs[5][j])),
+                     fmaxf(xs[6][j], xs[7][j]));
     }
   } else {
 #pragma unroll
@@ -369,7 +371,7 @@ __device__ __forceinline__ int stage_word(int tgl, int i, int dg) { return 96 * 
 // as 16 bytes per lane, 1 KB contiguous per store instruction.
 template <int C>
 __device__ __forceinline__ void encode_tokens(EncodeShared<C>& sh, const EncodeArgs& a, const EncodeUnit& u,
-                                              const uint4 (&v)[kTokPerThread], int t0, int tid, int tg, int dg) {
+                                              const float (&xs)[kTokPerThread][8], int t0, int tid, int tg, int dg) {
   constexpr int G = C / kTokPerThread;
   const int tok0 = t0 + tg * kTokPerThread;
   const int wave = tid >> 6, lane = tid & 63, tgl = tg & 7;
@@ -396,13 +398,11 @@ __device__ __forceinline__ void encode_tokens(EncodeShared<C>& sh, const EncodeA
     }
 #pragma unroll
     for (int i = 0; i < kTokPerThread; ++i) {
-      const uint32_t q[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
       uint32_t mb[8];
       float xf[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float x = (j & 1) ? bf16_hi(q[j >> 1]) : bf16_lo(q[j >> 1]);
-        const float f = fmaf(x - ch[j], kk[j], ckn[j]);
+        const float f = fmaf(xs[i][j] - ch[j], kk[j], ckn[j]);
         mb[j] = y_bits(f, alpha, ylog2k, ybias);
         xf[j] = f;
       }
@@ -418,8 +418,9 @@ __device__ __forceinline__ void encode_tokens(EncodeShared<C>& sh, const EncodeA
         do {                                         // one element at a time, lowest first
           const int j = __builtin_ctz(bits);
           bits &= bits - 1;
-          const uint32_t w = (j >> 1) == 0 ? q[0] : (j >> 1) == 1 ? q[1] : (j >> 1) == 2 ? q[2] : q[3];
-          const float x = (j & 1) ? bf16_hi_p(w) : bf16_lo_p(w);
+          float x = xs[i][0];
+#pragma unroll
+          for (int jj = 1; jj < 8; ++jj) x = j == jj ? xs[i][jj] : x;
           const float4 cs = cst_t[j * 8];
           // the fast path's Y again (same operations), to find the boundary it lies near:
           // the moved fraction is below 2z, so byte 2 is the code just above that boundary
@@ -546,9 +547,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C >= 3
 
   for (int i = tid; i < 129; i += kThreads) sh.bnd[i] = a.bnd[i];
 
-  uint4 v[kTokPerThread];
-  load_tile(v, u.X, t0, tg, g);
-  store_partials(sh, v, t0 + tg * kTokPerThread < g.P, tg, dg);
+  float xs[kTokPerThread][8];      // this thread's 8 tokens x 8 channels, unpacked by store_partials
+  {
+    uint4 v[kTokPerThread];
+    load_tile(v, u.X, t0, tg, g);
+    store_partials(sh, v, xs, t0 + tg * kTokPerThread < g.P, tg, dg);
+  }
   __syncthreads();
   if (!PAGE_STORED) {
     page_stats(sh, tid);
@@ -556,7 +560,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(C >= 3
   }
   chunk_stats(sh, u.meta, u.cbase, t0, tid, g, PAGE_STORED);
   __syncthreads();
-  encode_tokens(sh, a, u, v, t0, tid, tg, dg);
+  encode_tokens(sh, a, u, xs, t0, tid, tg, dg);
 }
 
 template __global__ void k_encode<8, false>(EncodeArgs);
