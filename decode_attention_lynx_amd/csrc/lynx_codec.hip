@@ -178,13 +178,9 @@ __device__ __forceinline__ void load_tile(uint4 (&v)[kTokPerThread], const uint1
   }
 }
 
-// The same BF16 -> float unpacking as bf16_lo / bf16_hi, written as a byte permutation.
-// Passes that unpack the same words a second time use this form, so the compiler
-// recomputes the floats there instead of keeping the first pass's copies live.
+// Two BF16 values as a vector for the BF16 -> float conversion of the statistics pass.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float bf16_lo_p(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x01000c0cu)); }
-__device__ __forceinline__ float bf16_hi_p(uint32_t w) { return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x03020c0cu)); }
 
 // Per-thread statistics of its 8 tokens x 8 channels, stored to the LDS partial rows:
 // float64 sum, min, max (Stage 2 needs all three; Stage 1 needs min and max).
