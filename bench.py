@@ -65,6 +65,11 @@ KERNEL_SOURCES = ["decode_attention_lynx_amd/csrc/lynx_codec.hip", "decode_atten
 CALLS = LAYERS // LAYERS_PER_CALL                    # launches per codec op and step
 
 
+STEP_OPS = ("encode", "decode_anchor", "decode_full", "attn_anchor")
+NEXT_OPS = ("codec_two_streams", "attn_anchor_c32", "attn_anchor_paged", "attn_verify", "attn_verify_paged",
+            "encode_to_host")
+
+
 def alg_bytes_per_elem(op: str) -> float:
     """Algorithmic HBM bytes per KV element (BF16 in/out 2 B, codes 0.5 B per stream,
     float32 metadata 8/C + 8/P B)."""
@@ -465,9 +470,8 @@ def main():
                     help="HIP streams the per-layer codec calls alternate over (with 2, launches of "
                          "consecutive layers overlap and a launch's duration no longer measures it alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--ops", default="encode,decode_anchor,decode_full,attn_anchor")
-    ap.add_argument("--next-ops", default="codec_two_streams,attn_anchor_c32,attn_anchor_paged,attn_verify,"
-                                          "attn_verify_paged,encode_to_host",
+    ap.add_argument("--ops", default=",".join(STEP_OPS))
+    ap.add_argument("--next-ops", default=",".join(NEXT_OPS),
                     help="ops timed after the step, on their own (empty: none)")
     ap.add_argument("--counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="summarise two rocprofv3 --pmc runs of this benchmark into per-op HBM bytes")

@@ -141,3 +141,14 @@ def test_util_summary_averages_every_counter_per_kernel(tmp_path):
     assert ver[-3:] == ["131072", "35", "52"]
     dec = [ln for ln in text if "k_decode" in ln][0].split()
     assert dec[-2:] == ["nan", "49"]
+
+
+def test_every_default_op_has_its_byte_and_flop_counts():
+    """Each op the bench runs by default (the step and beyond it) has algorithmic bytes and
+    elements, and the compute-bound ones their flops, so no report line divides by nothing."""
+    next_ops = [o for o in bench.NEXT_OPS if o not in ("codec_two_streams", "encode_to_host")]
+    assert {"attn_anchor_c32", "attn_anchor_paged", "attn_verify", "attn_verify_paged"} <= set(next_ops)
+    for op in list(bench.STEP_OPS) + next_ops:
+        assert bench.alg_bytes_per_elem(op) > 0 and bench.op_elems(op) > 0, op
+    for op in ("attn_verify", "attn_verify_paged"):
+        assert bench.op_flops(op) == 4.0 * bench.AB * bench.AM * bench.AHQ * bench.AT * bench.D
