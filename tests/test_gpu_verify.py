@@ -199,7 +199,7 @@ def test_verify_full_size_sampled(gpu):
         check(got[b:b + 1], got_lse[b:b + 1], ref_o, ref_lse, bound, f"seq {b}")
 
 
-@pytest.mark.parametrize("C", [64, 32])
+@pytest.mark.parametrize("C", [64, 32, 16])
 def test_verify_paged_variable_lengths(gpu, C):
     """A shuffled pool of pages behind a block table, with lengths ending inside a tile, on a tile
     edge, inside a page, at one token and at zero (O = 0, LSE = -inf)."""
