@@ -60,7 +60,7 @@ def make_case(B, Hq, Hkv, T, P, C, alpha, seed):
     (2, 12, 4, 512, 256, 128, 63.0),     # group of 3 query heads, chunk of 128
     (1, 2, 2, 64, 64, 64, 15.0),         # one tile, group of 1
     (1, 64, 8, 2048, 256, 64, 255.0),    # the full head geometry, short context
-    (2, 16, 2, 1024, 256, 32, 255.0),    # chunk of 32 (the pages' own setting): 32-token tiles
+    (2, 16, 2, 1024, 256, 32, 255.0),    # chunk of 32 (the pages' own setting): two chunks per 64-token tile
     (1, 8, 1, 96, 32, 32, 63.0),         # chunk 32, three pages of one chunk each
     (1, 16, 2, 8192, 4096, 256, 255.0),  # two 4096-token pages, chunks of 256 (four tiles each)
     (2, 16, 2, 1024, 256, 16, 255.0),    # chunk of 16: four chunks per 64-token tile
