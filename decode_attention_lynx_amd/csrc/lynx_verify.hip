@@ -29,7 +29,8 @@
 //   scores  S^T[token, row] = K_hi q + K_lo q on MFMA 16x16x32 bf16 (the BF16 query
 //           is exact in this format); each key fragment read feeds both groups;
 //   online softmax in base 2 per row, the running maximum moved only when a tile
-//           raises it by more than 8 (probabilities stay below 2^8, exact in range);
+//           raises it by more than 8 or a lane's sum of its 16 probabilities of the tile
+//           reaches 2^12 (so probabilities stay below 2^12, exact in range);
 //   values  O^T[d, row] += sum_t V_hat[d, t] p[t, row] on MFMA 16x16x32 f16, o held in
 //           units of 2^E.
 // LDS traffic bounds this loop: per 64-token tile a workgroup reads 48 KB of key and
@@ -68,6 +69,7 @@ constexpr int kLutCopies = 32;             // copies of each table entry (lane l
 constexpr int kRec = kHeadDim + 4;         // floats per partial record (o 16-byte aligned)
 constexpr int kVWorkgroups = 256;          // workgroups the context splits aim for (one per CU)
 constexpr float kLazyMax = 8.0f;           // the running maximum moves only beyond this (base 2)
+constexpr float kLazySumBound = 4096.0f;   // bound on a lane's sum of its 16 probabilities of a tile
 constexpr float kF16Safe = 60000.0f;       // largest |value| stored as float16 (maximum 65504)
 
 struct VerifyArgs {
@@ -172,25 +174,29 @@ __device__ __forceinline__ void load_codes(const VerifyArgs& a, int b, int kvh, 
 
 // gamma_min, gamma_scale, mu and sigma of channels 2l, 2l+1 of the tile's CPT chunks, for
 // lane l of wave 0 (keys) or wave 1 (values)
+// (each channel pair held as one 64-bit value, so that its two halves stay one register pair
+// from the load to the use: split, a copy of one half made the wave wait for the load right
+// after issuing it)
 template <int CPT>
 struct MetaIn {
-  float2 gmin, gscale, mu[CPT], sigma[CPT];
+  uint64_t gmin, gscale, mu[CPT], sigma[CPT];
 };
+__device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float((uint32_t)v); }
+__device__ __forceinline__ float hi_f(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
 
 template <int CPT>
 __device__ __forceinline__ MetaIn<CPT> load_meta(const VerifyArgs& a, int b, int kvh, int tile, int fetched,
-                                                 int tid) {
+                                                 int wave, int lane) {
   const TileAddr ta = tile_addr(a, b, kvh, tile, fetched);
-  const int c = 2 * (tid & 63);
-  const uint8_t* seg = (tid < 64 ? a.kanc : a.vanc) + ta.seg * a.anc_seg + a.codes;
-  const float* meta = reinterpret_cast<const float*>(seg) + kvh * kHeadDim + c;
+  const uint8_t* seg = (wave == 0 ? a.kanc : a.vanc) + ta.seg * a.anc_seg + a.codes;
+  const float* meta = reinterpret_cast<const float*>(seg) + kvh * kHeadDim + 2 * lane;
   MetaIn<CPT> m;
-  m.gmin = *reinterpret_cast<const float2*>(meta);
-  m.gscale = *reinterpret_cast<const float2*>(meta + a.H);
+  m.gmin = *reinterpret_cast<const uint64_t*>(meta);
+  m.gscale = *reinterpret_cast<const uint64_t*>(meta + a.H);
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    m.mu[k] = *reinterpret_cast<const float2*>(meta + 2 * (size_t)a.H + (size_t)(ta.kc + k) * a.H);
-    m.sigma[k] = *reinterpret_cast<const float2*>(meta + 2 * (size_t)a.H + (size_t)(a.nck + ta.kc + k) * a.H);
+    m.mu[k] = *reinterpret_cast<const uint64_t*>(meta + 2 * (size_t)a.H + (size_t)(ta.kc + k) * a.H);
+    m.sigma[k] = *reinterpret_cast<const uint64_t*>(meta + 2 * (size_t)a.H + (size_t)(a.nck + ta.kc + k) * a.H);
   }
   return m;
 }
@@ -231,9 +237,11 @@ __device__ __forceinline__ int value_exponent(float2 ab) {
   const float bound = fabsf(ab.x) + fabsf(ab.y);
   if (bound <= kF16Safe) return 0;
   if (!(bound < INFINITY)) return 126;
-  int ex;
-  (void)frexpf(bound / kF16Safe, &ex);     // bound / kF16Safe <= 2^ex
-  return ex;
+  // bound = m 2^x with m in [0.5, 1), kF16Safe = ms 2^16 (ms = 60000 / 65536, exact): e = x - 16
+  // when m <= ms, else x - 15
+  int x;
+  const float m = frexpf(bound, &x);
+  return x - 16 + (m > kF16Safe / 65536.0f ? 1 : 0);
 }
 
 // Maps of one tile into slot `buf`: wave 0 writes the key maps of channels 2l, 2l+1, wave 1
@@ -241,22 +249,21 @@ __device__ __forceinline__ int value_exponent(float2 ab) {
 // (held in E_map by wave 1).
 template <int CPT>
 __device__ __forceinline__ void write_maps(VerifyLds<CPT>& L, int buf, const MetaIn<CPT>& m, float qscale,
-                                           int tid, int& E_map) {
-  const int l = tid & 63;
-  if (tid < 64) {
+                                           int wave, int l, int& E_map) {
+  if (wave == 0) {
     const int c = 2 * l + (l >> 3);       // channel 2l at 2l + 2l/16
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      L.abk[buf][k][c] = affine(m.gmin.x, m.gscale.x, m.mu[k].x, m.sigma[k].x, qscale);
-      L.abk[buf][k][c + 1] = affine(m.gmin.y, m.gscale.y, m.mu[k].y, m.sigma[k].y, qscale);
+      L.abk[buf][k][c] = affine(lo_f(m.gmin), lo_f(m.gscale), lo_f(m.mu[k]), lo_f(m.sigma[k]), qscale);
+      L.abk[buf][k][c + 1] = affine(hi_f(m.gmin), hi_f(m.gscale), hi_f(m.mu[k]), hi_f(m.sigma[k]), qscale);
     }
   } else {
     float2 ab0[CPT], ab1[CPT];
     int e = 0;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
-      ab0[k] = affine(m.gmin.x, m.gscale.x, m.mu[k].x, m.sigma[k].x, 1.0f);
-      ab1[k] = affine(m.gmin.y, m.gscale.y, m.mu[k].y, m.sigma[k].y, 1.0f);
+      ab0[k] = affine(lo_f(m.gmin), lo_f(m.gscale), lo_f(m.mu[k]), lo_f(m.sigma[k]), 1.0f);
+      ab1[k] = affine(hi_f(m.gmin), hi_f(m.gscale), hi_f(m.mu[k]), hi_f(m.sigma[k]), 1.0f);
       e = max(e, max(value_exponent(ab0[k]), value_exponent(ab1[k])));
     }
     if (__builtin_amdgcn_ballot_w64(e > E_map) != 0) {   // values beyond the range so far: rare
@@ -286,6 +293,11 @@ __device__ __forceinline__ void decode_tile(VerifyLds<CPT>& L, int buf, const Co
     // so the 16 lanes of one token write its whole row.  A thread reads the maps of its 8 channels
     // once for both tokens (twice when they fall in different chunks).
     const int cu = tid & 15, t0 = tid >> 4;
+    // the BF16 pairs (-1, 0) and (0, -1) from registers (an inline constant of a packed BF16
+    // operand is not read as such a pair)
+    uint32_t nlo = 0x0000BF80u, nhi = 0xBF800000u;
+    asm volatile("" : "+v"(nlo), "+v"(nhi));
+    const vb2 neg_lo = __builtin_bit_cast(vb2, nlo), neg_hi = __builtin_bit_cast(vb2, nhi);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int t = t0 + 32 * r;
@@ -303,7 +315,10 @@ __device__ __forceinline__ void decode_tile(VerifyLds<CPT>& L, int buf, const Co
         const float x1 = fmaf(ab1.x, L.lut[((od >> (8 * k)) & 0xFFu) * kLutCopies + lcopy], ab1.y);
         const uint32_t h = bf16x2(x0, x1);
         hi[k] = h;
-        lo[k] = bf16x2(x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xFFFF0000u));
+        // x - hi, exact in float32, as a dot product of the BF16 pair with (-1, 0) / (0, -1)
+        const vb2 hv = __builtin_bit_cast(vb2, h);
+        lo[k] = bf16x2(__builtin_amdgcn_fdot2_f32_bf16(hv, neg_lo, x0, false),
+                       __builtin_amdgcn_fdot2_f32_bf16(hv, neg_hi, x1, false));
       }
       const int c16 = cu ^ (t & 15);
       *reinterpret_cast<uint4*>(&L.kh[buf][t * 64 + 4 * c16]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
@@ -367,7 +382,8 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
 
   // Online softmax state per row (base 2).  The key products start from -m_run, so they
   // yield s - m_run directly; m_run moves only when a tile exceeds it by more than
-  // kLazyMax.  o_acc is held in units of 2^E_acc (the values' range exponent).
+  // kLazyMax or a lane's probabilities of a tile sum to kLazySumBound or more.  o_acc is held
+  // in units of 2^E_acc (the values' range exponent).
   float m_run[kVGroups], l_run[kVGroups];
   vf4 cinit[kVGroups];
   vf4 o_acc[kVGroups][8];
@@ -390,15 +406,14 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
   if (nt > 0) {
 
   // prologue: maps of tiles 0 and 1, codes of tiles 0 and 1, tile 0 decoded into buffer 0
-  const bool mapper = wave < 2;          // wave-uniform
-  MetaIn<CPT> meta;
+  const bool mapper = wave < 2;          // wave-uniform: wave 0 keys, wave 1 values
   int E_map = 0;
   const int f0 = fetch_segment(a, b, t_begin), f1 = fetch_segment(a, b, min(t_begin + 1, t_last));
   int f_cur = fetch_segment(a, b, min(t_begin + 2, t_last));   // the tile whose codes step i loads: i + 2
   if (mapper) {
-    write_maps(L, 0, load_meta<CPT>(a, b, kvh, t_begin, f0, tid), a.qscale, tid, E_map);
-    write_maps(L, 1, load_meta<CPT>(a, b, kvh, min(t_begin + 1, t_last), f1, tid), a.qscale, tid, E_map);
-    meta = load_meta<CPT>(a, b, kvh, min(t_begin + 2, t_last), f_cur, tid);
+    write_maps(L, 0, load_meta<CPT>(a, b, kvh, t_begin, f0, wave, lane), a.qscale, wave, lane, E_map);
+    write_maps(L, 1, load_meta<CPT>(a, b, kvh, min(t_begin + 1, t_last), f1, wave, lane), a.qscale, wave, lane,
+               E_map);
   }
   CodeIn cin;
   load_codes(a, b, kvh, t_begin, f0, tid, cin);
@@ -413,6 +428,10 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
     __syncthreads();   // buffer par is decoded; buffer 1-par and maps slot par are free
     const int f_next = fetch_segment(a, b, min(t_begin + i + 3, t_last));
     decode_tile(L, 1 - par, cin, tid, lcopy);
+    // the metadata of tile i+2 (written as maps at the end of this step: loaded and used within one
+    // step, so that no copy of it crosses the loop) ahead of its codes
+    MetaIn<CPT> meta;
+    if (mapper) meta = load_meta<CPT>(a, b, kvh, min(t_begin + i + 2, t_last), f_cur, wave, lane);
     load_codes(a, b, kvh, min(t_begin + i + 2, t_last), f_cur, tid, cin);
 
     if (wave_live) {
@@ -453,42 +472,56 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
 
       // ---- the value operands of the tile, read ahead of the softmax (which hides their latency):
       //      lane (n, g) of step ks takes channel 16j + n, slot 4ks + g
+      //      ((d >> 1) & 7 == (n >> 1) & 7, so block j is a constant offset from two lane bases)
+      const uint32_t* vbase0 = &L.lv[par][n * (kVTile / 2) + 4 * (g ^ ((n >> 1) & 7))];
+      const uint32_t* vbase1 = &L.lv[par][n * (kVTile / 2) + 4 * ((4 + g) ^ ((n >> 1) & 7))];
       auto vread = [&](int j, int ks) {
-        const int d = 16 * j + n;
-        const uint4 w = *reinterpret_cast<const uint4*>(&L.lv[par][d * (kVTile / 2) + 4 * ((4 * ks + g) ^ ((d >> 1) & 7))]);
+        const uint4 w = *reinterpret_cast<const uint4*>((ks ? vbase1 : vbase0) + 16 * (kVTile / 2) * j);
         return vu4{w.x, w.y, w.z, w.w};
       };
 
-      // ---- online softmax: p = 2^(s - m_run), the maximum moved (and o, l rescaled) only
-      //      where the tile exceeds it by more than kLazyMax, so p < 2^kLazyMax
+      // ---- online softmax: p = 2^(s - m_run) as is while every lane's sum of its 16 p stays
+      //      below kLazySumBound (so every p does), with no tile maximum taken; otherwise (rare,
+      //      and on the first tile) the row's maximum moves to the tile's where the tile exceeds
+      //      it by more than kLazyMax or a lane sum reached the bound, o and l are rescaled and p
+      //      is taken again
       vh8 pt[kVGroups][2];
 #pragma unroll
       for (int gq = 0; gq < kVGroups; ++gq) {
-        float mt = s[gq][0];
-#pragma unroll
-        for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[gq][e]);
-        mt = group_max(mt);                               // tile maximum minus m_run (or itself)
-        const float base = m_run[gq] == -INFINITY ? 0.0f : m_run[gq];
-        const bool up = mt + base > m_run[gq] + kLazyMax;
-        const float sub = up ? mt : 0.0f;                 // where the maximum moves
-        if (__builtin_amdgcn_ballot_w64(up) != 0) {
-          const float corr = up ? __builtin_amdgcn_exp2f(m_run[gq] - (mt + base)) : 1.0f;
-          if (up) {
-            m_run[gq] = mt + base;
-            cinit[gq] = vf4{-m_run[gq], -m_run[gq], -m_run[gq], -m_run[gq]};
-          }
-          l_run[gq] *= corr;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) o_acc[gq][j] *= corr;
-        }
+        float p[16];
         float lsum = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(s[gq][e] - sub);
-          lsum += p;
-          pt[gq][e >> 3][e & 7] = (_Float16)p;
+          p[e] = __builtin_amdgcn_exp2f(s[gq][e]);
+          lsum += p[e];
+        }
+        const bool ok = lsum < kLazySumBound && m_run[gq] != -INFINITY;
+        if (__builtin_amdgcn_ballot_w64(!ok) != 0) {
+          float mt = s[gq][0];
+#pragma unroll
+          for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[gq][e]);
+          mt = group_max(mt);                               // tile maximum minus m_run (or itself)
+          const bool big = group_max(ok ? 0.0f : 1.0f) != 0.0f;   // some lane of the row failed
+          const float base = m_run[gq] == -INFINITY ? 0.0f : m_run[gq];
+          const bool up = mt + base > m_run[gq] + kLazyMax || (big && mt != -INFINITY);
+          if (up) {
+            const float corr = __builtin_amdgcn_exp2f(m_run[gq] - (mt + base));
+            m_run[gq] = mt + base;
+            cinit[gq] = vf4{-m_run[gq], -m_run[gq], -m_run[gq], -m_run[gq]};
+            l_run[gq] *= corr;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o_acc[gq][j] *= corr;
+            lsum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              p[e] = __builtin_amdgcn_exp2f(s[gq][e] - mt);
+              lsum += p[e];
+            }
+          }
         }
         l_run[gq] += lsum;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pt[gq][e >> 3][e & 7] = (_Float16)p[e];
       }
 
       // ---- values: O^T[d, row] += sum_t V_hat[d, t] p[t, row], d = 16j + 4g + e of block j.
@@ -518,8 +551,7 @@ __global__ __launch_bounds__(kVThreads) void k_verify(VerifyArgs a) {
     }
     // ---- maps of tile i+2 into slot par (read by the decode in step i+1)
     if (mapper) {
-      write_maps(L, par, meta, a.qscale, tid, E_map);
-      meta = load_meta<CPT>(a, b, kvh, min(t_begin + i + 3, t_last), f_next, tid);
+      write_maps(L, par, meta, a.qscale, wave, lane, E_map);
     }
     f_cur = f_next;
   };
