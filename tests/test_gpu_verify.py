@@ -150,6 +150,52 @@ def test_verify_values_beyond_float16_range(gpu):
           "range")
 
 
+def test_verify_scores_rising_inside_splits(gpu):
+    """Keys grow by 1.6x per tile inside each context split (8 sequences x 8 kv heads make 4 splits
+    of 4 tiles), so a row's maximum rises tile after tile: some rises stay within what the kernel's
+    probabilities absorb without moving its running maximum (below 8 in base 2), some may or may not
+    (8 to 12: a lane's probabilities then sum to 2^12 or not), others move it (above 12); the
+    inputs are checked to hold all three kinds.  Same bars as the small cases."""
+    B, M, Hq, Hkv, T, P, C, alpha = 8, 2, 16, 8, 1024, 256, 64, 255.0
+    npg, G = T // P, Hq // Hkv
+    kf = np.concatenate([o.bf16_bits_to_f64(synth.make_kv_np(T, Hkv, 128, seed=33, layer=b, kv_idx=0))
+                         for b in range(B)]).reshape(B, T, Hkv, 128)
+    kf *= (1.6 ** ((np.arange(T) // 64) % 4))[None, :, None, None]
+    kb = o.f64_to_bf16_bits(kf.reshape(B * T, Hkv, 128))
+    vb = np.concatenate([synth.make_kv_np(T, Hkv, 128, seed=33, layer=b, kv_idx=1) for b in range(B)])
+    ka, kr, _ = o.encode(kb, P, C, alpha)
+    va, vr, _ = o.encode(vb, P, C, alpha)
+    qb = synth.make_q_np(B * M, Hq, 128, seed=33).reshape(B, M, Hq, 128)
+    # the kernel's plan: 4 context splits of 4 tiles
+    ws = lynx.attn_verify_workspace_bytes(B, M, T, Hq, Hkv, 128, P, C)
+    assert ws == B * M * Hq * 4 * 132 * 4
+    # each row's tile maximum against the running maximum of the tiles before it in its split (base 2)
+    q = o.bf16_bits_to_f64(qb)
+    to_base2 = np.log2(np.e) / np.sqrt(128)
+    rises = []
+    for b in range(B):
+        K = o.decode_full(ka[b * npg:(b + 1) * npg].reshape(-1), kr[b * npg:(b + 1) * npg].reshape(-1), npg, P,
+                          Hkv, 128, C, alpha)
+        for h in range(Hkv):
+            s = (q[b, :, h * G:(h + 1) * G, :].reshape(M * G, 128) @ K[:, h, :].T) * to_base2
+            tmax = s.reshape(M * G, T // 64, 64).max(axis=2)
+            for sp in range(4):
+                run = tmax[:, 4 * sp]
+                for j in range(1, 4):
+                    rises.append(tmax[:, 4 * sp + j] - run)
+                    run = np.maximum(run, tmax[:, 4 * sp + j])
+    rises = np.concatenate(rises)
+    assert np.any((rises > 0.5) & (rises < 8.0)) and np.any((rises > 8.0) & (rises < 12.0))
+    assert np.any(rises > 12.0)
+    ref_o, ref_lse = o.attention_verify(qb, ka, kr, va, vr, B, M, T, Hq, Hkv, 128, P, C, alpha)
+    out, lse = lynx.attn_verify(bf16_tensor(qb), upload(ka), upload(kr), upload(va), upload(vr), T, Hkv, P, C,
+                                alpha)
+    torch.cuda.synchronize()
+    bound = lse_bound(qb, ka, kr, B, M, T, Hq, Hkv, P, C, alpha)
+    check(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref_o, ref_lse, bound,
+          "rising")
+
+
 def test_verify_lse_merges_context_halves(gpu):
     """The LSE returned for two halves of a context merges to the whole (the rule a caller uses to
     add the draft tokens' own keys): O = (e^{l1} O1 + e^{l2} O2) / (e^{l1} + e^{l2})."""
