@@ -127,19 +127,28 @@ def test_verify_without_lse_and_sm_scale(gpu):
           "sm_scale")
 
 
-def test_verify_values_beyond_float16_range(gpu):
-    """Values the kernel cannot hold as float16 (|V| up to ~2*10^6 from token 1088 on) take its
-    power-of-two range exponent.  With 8 sequences of 32 one-tile pages the context splits hold
-    2 tiles each, so the exponent grows inside a split (tiles 16 -> 17); the bar is unchanged."""
+@pytest.mark.parametrize("factor", [4096.0, 128.0])
+def test_verify_values_beyond_float16_range(gpu, factor):
+    """Values the kernel cannot hold as float16 (|V| up to ~2*10^6 from token 1088 on at a factor
+    of 4096; ~8*10^4 at 128, where several pages' bound |A_V| + |B_V| falls between 60000 and
+    2^16, the edge of the exponent's first step) take its power-of-two range exponent.  With 8
+    sequences of 32 one-tile pages the context splits hold 2 tiles each, so the exponent grows
+    inside a split (tiles 16 -> 17); the bar is unchanged."""
     B, M, Hq, Hkv, T, P, C, alpha = 8, 4, 16, 2, 2048, 64, 64, 255.0
     kb = np.concatenate([synth.make_kv_np(T, Hkv, 128, seed=21, layer=b, kv_idx=0) for b in range(B)])
     vf = np.concatenate([o.bf16_bits_to_f64(synth.make_kv_np(T, Hkv, 128, seed=21, layer=b, kv_idx=1))
                          for b in range(B)]).reshape(B, T, Hkv, 128)
-    vf[:, 17 * 64:] *= 4096.0                  # a power of two: the BF16 values stay exact
+    vf[:, 17 * 64:] *= factor                  # a power of two: the BF16 values stay exact
     assert np.abs(vf).max() > 65504.0
     vb = o.f64_to_bf16_bits(vf.reshape(B * T, Hkv, 128))
     ka, kr, _ = o.encode(kb, P, C, alpha)
-    va, vr, _ = o.encode(vb, P, C, alpha)
+    va, vr, pages = o.encode(vb, P, C, alpha)
+    # the pages' bound on |V_hat| (|A_V| + |B_V| over their chunks and channels)
+    bound = np.array([(np.abs((pg["gscale"] + 1e-6) * (pg["sigma"] + 1e-6)) +
+                       np.abs(pg["gmin"] + pg["mu"] * (pg["gscale"] + 1e-6))).max() for pg in pages])
+    assert np.any(bound > 65536.0)
+    if factor == 128.0:
+        assert np.any((bound > 60000.0) & (bound < 65536.0))
     qb = synth.make_q_np(B * M, Hq, 128, seed=21).reshape(B, M, Hq, 128)
     ref_o, ref_lse = o.attention_verify(qb, ka, kr, va, vr, B, M, T, Hq, Hkv, 128, P, C, alpha)
     out, lse = lynx.attn_verify(bf16_tensor(qb), upload(ka), upload(kr), upload(va), upload(vr), T, Hkv, P, C,
