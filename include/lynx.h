@@ -290,7 +290,8 @@ size_t lynx_attn_verify_workspace_bytes(int batch, int n_query, int ctx_tokens, 
  *   out_dtype    : LYNX_OUT_BF16 or LYNX_OUT_F32; out_dev [batch][n_query][q_heads][head_dim].
  *   lse_dev      : float32 [batch][n_query][q_heads], written; may be NULL.
  * Keys are formed in float32 and carried as BF16 high + low parts (~16 significant
- * bits); values as float16 table values with the affine map applied in float32.
+ * bits); values are formed in float32 and carried in float16 after a power-of-two range
+ * scaling (so values beyond float16's range are supported), with float32 accumulation.
  * Supported by this library: head_dim == 128.  Asynchronous on hip_stream.
  */
 int lynx_attn_verify(const void* q_dev, const void* k_anchor_dev, const void* k_residual_dev,
