@@ -162,6 +162,55 @@ def counter_summary(fetch_csv: str, write_csv: str, out_json: str) -> str:
     return "\n".join(lines)
 
 
+def workload_counter_summary(fetch_csv: str, write_csv: str, chunk: int) -> str:
+    """HBM bytes per dispatch of the codec kernels in two rocprofv3 --pmc runs of
+    `--codec-workloads --cw-chunk <chunk>` (FETCH_SIZE, then WRITE_SIZE), scaled by the copy
+    calibration stored in profiles/traffic.json, against the algorithmic bytes of the dispatch.
+    For 256-token pages one encoder or decoder thread covers 64 elements (a workgroup of 256
+    threads: one 64-channel slab of a page, or one 128-token tile of a kv head), so a grid of G
+    threads moves G * 64 elements; the 4096-token page's kernels are listed without a rate."""
+    import csv
+    from collections import defaultdict
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        cal = json.load(f)["calibration"]
+
+    def read(path, counter):
+        acc = defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+                if name.startswith("lynx::"):
+                    acc[(name, int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+        return acc
+
+    fetch, write = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
+    lines = [f"calibration (profiles/traffic.json): FETCH_SIZE x {cal['fetch_factor']}, WRITE_SIZE x {cal['write_factor']}; "
+             f"chunk {chunk}, 256-token pages",
+             f"{'kernel':34s} {'grid':>9s} {'n':>4s} {'FETCH KiB':>12s} {'WRITE KiB':>12s} {'HBM bytes':>12s} "
+             f"{'algorithmic':>12s} {'ratio':>7s}"]
+    for key in sorted(fetch):
+        name, grid = key
+        fk = sum(fetch[key]) / len(fetch[key])
+        wk = sum(write[key]) / len(write[key]) if key in write else float("nan")
+        hbm = fk * 1024.0 * cal["fetch_factor"] + wk * 1024.0 * cal["write_factor"]
+        per_elem = None
+        if name.startswith("lynx::k_encode<") and name.endswith(", false>"):
+            per_elem = 3.0 + 8.0 / int(name.split("<")[1].split(",")[0]) + 8.0 / 256
+        elif name == "lynx::k_decode<false, false>":
+            per_elem = 2.5 + 8.0 / chunk + 8.0 / 256
+        elif name == "lynx::k_decode<true, false>":
+            per_elem = 3.0 + 8.0 / chunk + 8.0 / 256
+        if per_elem is None:
+            lines.append(f"{name:34s} {grid:9d} {len(fetch[key]):4d} {fk:12.1f} {wk:12.1f} {hbm:12.0f} {'-':>12s} {'-':>7s}")
+        else:
+            alg = per_elem * grid * 64
+            lines.append(f"{name:34s} {grid:9d} {len(fetch[key]):4d} {fk:12.1f} {wk:12.1f} {hbm:12.0f} {alg:12.0f} "
+                         f"{hbm / alg:7.4f}")
+    return "\n".join(lines)
+
+
 def util_summary(counter_csv: str) -> str:
     """Per (kernel, grid) averages of every counter in a rocprofv3 --pmc CSV of this benchmark
     (for instance the derived MfmaUtil and VALUBusy percentages and raw instruction counts)."""
@@ -332,7 +381,7 @@ CODEC_WORKLOADS = [
 SETTLE_LAUNCHES = 16   # untimed encodes before a workload's first timed setting
 
 
-def codec_workloads(reps: int, warmup: int) -> dict:
+def codec_workloads(reps: int, warmup: int, chunk: int = 0) -> dict:
     """Encode and both decoders (BF16 out) on each workload of CODEC_WORKLOADS: median launch
     time over `reps` event-timed repetitions (a repetition of a per-tensor workload covers all
     its layer tensors), algorithmic GB/s and fraction of HBM peak."""
@@ -356,6 +405,8 @@ def codec_workloads(reps: int, warmup: int) -> dict:
         elems = n_t * tokens * kvh * D
         out = torch.empty((tokens if per_tensor else n_t * tokens, kvh, D), dtype=torch.bfloat16, device=dev)
         outs = [out, torch.empty_like(out)] if per_tensor else [out]
+        if chunk:
+            settings = [(c_, al) for c_, al in settings if c_ == chunk]
         for si, (c_, al) in enumerate(settings):
             a_sz, r_sz = lynx.stream_sizes(pt, kvh, D, c_)
             anc = torch.empty((n_pages, a_sz), dtype=torch.uint8, device=dev)
@@ -487,7 +538,14 @@ def main():
                     help="summarise a rocprofv3 --pmc run of this benchmark: every counter per kernel and grid")
     ap.add_argument("--codec-workloads", action="store_true",
                     help="instead of the step: time the codec on the other request shapes (one JSON line)")
+    ap.add_argument("--cw-chunk", type=int, default=0,
+                    help="with --codec-workloads: only the settings of this chunk size")
+    ap.add_argument("--workload-counter-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs of --codec-workloads --cw-chunk C per kernel and grid")
     args = ap.parse_args()
+    if args.workload_counter_summary:
+        print(workload_counter_summary(*args.workload_counter_summary, chunk=args.cw_chunk or 64))
+        return
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
         return
@@ -502,7 +560,8 @@ def main():
               "attention shard by page / sequence with no exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.codec_workloads:
-        print(json.dumps(codec_workloads(reps=max(args.steps, 5), warmup=max(args.warmup, 1))), flush=True)
+        print(json.dumps(codec_workloads(reps=max(args.steps, 5), warmup=max(args.warmup, 1), chunk=args.cw_chunk)),
+              flush=True)
         return
 
     # the CPU oracle first, while no process has touched the GPU (its workers are forked)

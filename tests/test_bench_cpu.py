@@ -152,3 +152,30 @@ def test_every_default_op_has_its_byte_and_flop_counts():
         assert bench.alg_bytes_per_elem(op) > 0 and bench.op_elems(op) > 0, op
     for op in ("attn_verify", "attn_verify_paged"):
         assert bench.op_flops(op) == 4.0 * bench.AB * bench.AM * bench.AHQ * bench.AT * bench.D
+
+
+def test_workload_counter_summary_rates_the_codec_dispatches(tmp_path):
+    """Per (kernel, grid) HBM bytes of the codec-workload counter runs against G * 64 elements of
+    algorithmic bytes, with the copy calibration of profiles/traffic.json."""
+    cal = json.load(open(os.path.join(bench.ROOT, "profiles", "traffic.json")))["calibration"]
+    grid = 4194304                                   # a 2.15 GB request: 268 M elements
+    alg_enc = (3.0 + 8.0 / 64 + 8.0 / 256) * grid * 64
+    fetch = {("void lynx::k_encode<64, false>(lynx::EncodeArgs)", grid):
+             [alg_enc * 2 / 3 / 1024 / cal["fetch_factor"]] * 2,
+             ("void lynx::k_decode<true, false>(lynx::DecodeArgs)", grid): [1.0],
+             ("void lynx::k_page_finish(lynx::EncodeArgs)", 2048): [3.0]}
+    write = {("void lynx::k_encode<64, false>(lynx::EncodeArgs)", grid):
+             [alg_enc / 3 / 1024 / cal["write_factor"]] * 2,
+             ("void lynx::k_decode<true, false>(lynx::DecodeArgs)", grid): [2.0],
+             ("void lynx::k_page_finish(lynx::EncodeArgs)", 2048): [1.0]}
+    fields = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
+    write_rows(fp, kernel_rows("FETCH_SIZE", fetch), fields)
+    write_rows(wp, kernel_rows("WRITE_SIZE", write), fields)
+    lines = bench.workload_counter_summary(str(fp), str(wp), chunk=64).splitlines()
+    enc = [ln for ln in lines if "k_encode<64" in ln][0].split()
+    assert enc[-1] == "1.0000" and int(enc[-2]) == round(alg_enc)
+    dec = [ln for ln in lines if "k_decode<true" in ln][0].split()
+    assert int(dec[-2]) == round((3.0 + 8.0 / 64 + 8.0 / 256) * grid * 64)
+    fin = [ln for ln in lines if "k_page_finish" in ln][0].split()
+    assert fin[-1] == "-"
